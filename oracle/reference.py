@@ -1,0 +1,414 @@
+"""Reference implementation of the EXL3 trellis tile encoder -- TEST INFRASTRUCTURE ONLY.
+
+This module is the oracle.  Only the test-suite, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import it.  It shares no code with the
+GPU library: it has its own codebook generator, its own Hadamard transform, its
+own packer and its own scale search.  It is plain and slow on purpose, so that
+each step can be checked by eye against the sources:
+
+  [P1] "EXL3 Intel Arc Quantizer" (project README), section "Core Implemented
+       Architecture" -- item 1 (SYCL XPU tile encoder: add-compare-select,
+       two-pass tail-biting closure), item 4 (CPU reference encoder: state
+       algebra), item 5 (format primitives: mul1 codebook, MSB-first container,
+       SWAP16), item 7 (Sylvester Hadamard, blockwise, decode order), item 8
+       (regularization, wrapped-diagonal tile sample for the scale search);
+       section "Test Suite & Verification" (ring invariant, shift-register
+       identity, round trips).
+  [P2] "JEV-9B EXL3 K=2 (mul1) Checkpoint for Intel Arc XPU" (model card),
+       section 2 "Quantization & Bitrate Breakdown" (golden-section scale
+       search) and section 3 "Verification & Metrics" (distortion band).
+
+Readings taken where the sources leave a step open (each is listed in the
+design notes with its reason):
+
+  * numerics: binary32, each subtract / multiply / add rounded on its own, no
+    fused multiply-add, lowest index on equal costs; host control in binary64;
+  * mul1 levels: the sources give only the name, the count of distinct levels
+    and their range.  This oracle uses a multiply-then-byte-sum construction:
+    h = (A * s) mod 2^32 for an odd constant A chosen here, beta = the sum of
+    the four bytes of h, level = fp16 round-to-nearest-even of
+    (beta - mean) / std over all 2^16 states (computed with exact integers and
+    two correctly rounded binary64 operations).  Compatibility with upstream
+    levels is NOT claimed (parity unpinned against upstream);
+  * search domain: the tile input is compared with v = rn(scale * level);
+  * regularization: signs, then blockwise left FWHT, x rn(1/sqrt(B)), then
+    blockwise right FWHT, x rn(1/sqrt(B)); natural Sylvester order;
+  * tile geometry: row-major tile grid, row-major 16x16 inside a tile (the
+    tensor-core permutation is not reproduced);
+  * statistics: sequential binary32 sum of squares per tile, binary64 sum over
+    tiles in ascending order;
+  * scale search: textbook golden section over [lo, hi] * rms with 2 initial
+    probes and `iters` reductions, strict "<" keeps the left part, result is the
+    midpoint of the final bracket rounded to binary32;
+  * scale-search tile set: the wrapped diagonal plus the tiles with the largest
+    and the smallest sum of squares (lowest index on ties), ascending order.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+from . import build as _build
+
+# --------------------------------------------------------------------------
+# C core (forward dynamic program and two-pass closure)
+# --------------------------------------------------------------------------
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+        i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+        u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+        lib.oracle_forward.argtypes = [f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       f32p, f32p, f32p, u8p]
+        lib.oracle_forward.restype = ctypes.c_int
+        lib.oracle_encode_many.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, f32p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_encode_many.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    return max(1, os.cpu_count() or 1)
+
+
+# --------------------------------------------------------------------------
+# Codebook  [P1 item 5]
+# --------------------------------------------------------------------------
+MUL1_MULTIPLIER = 0x9E3779B1   # odd 32-bit constant chosen here (golden-ratio hash)
+STATE_BITS = 16
+
+
+def mul1_levels_fp16() -> np.ndarray:
+    """fp16 level of each of the 2^16 states (the reading described in the header)."""
+    n = 1 << STATE_BITS
+    s = np.arange(n, dtype=np.uint64)
+    h = (s * np.uint64(MUL1_MULTIPLIER)) & np.uint64(0xFFFFFFFF)
+    beta = np.zeros(n, dtype=np.int64)
+    for byte in range(4):
+        beta += ((h >> np.uint64(8 * byte)) & np.uint64(0xFF)).astype(np.int64)
+    s1 = int(beta.sum())
+    s2 = int((beta * beta).sum())
+    # (beta - s1/n) / (sqrt(n*s2 - s1^2)/n) == (n*beta - s1) / sqrt(n*s2 - s1^2)
+    numer = (n * beta - s1).astype(np.float64)          # exact integers
+    denom = math.sqrt(float(n * s2 - s1 * s1))          # exact integer, one rounding
+    z = numer / denom                                   # one rounding per state
+    return z.astype(np.float16)                         # round-to-nearest-even
+
+
+def scaled_levels(levels_fp16: np.ndarray, scale) -> np.ndarray:
+    """v[s] = rn(scale * level[s]) in binary32."""
+    return (np.float32(scale) * levels_fp16.astype(np.float32)).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Trellis search  [P1 items 1 and 4]
+# --------------------------------------------------------------------------
+def forward(x, Q, K, v, M0):
+    """One forward pass; returns (final-step costs C[2^Q], predecessors [L-1, 2^(Q-K)])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    M0 = np.ascontiguousarray(M0, dtype=np.float32)
+    L = x.shape[0]
+    C = np.empty(1 << Q, dtype=np.float32)
+    bp = np.empty(((L - 1), 1 << (Q - K)), dtype=np.uint8)
+    rc = _load().oracle_forward(x, L, Q, K, v, M0, C, bp)
+    if rc != 0:
+        raise ValueError("oracle_forward rejected its arguments (rc=%d)" % rc)
+    return C, bp
+
+
+def encode_sequences(x, K, v, Q=STATE_BITS, threads=None):
+    """Two-pass tail-biting encode of each row of x [n, L].
+
+    Returns (states int32 [n, L], X int32 [n], cost float32 [n]); cost is the
+    pass-2 cost of X at the last step.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    if x.ndim != 2:
+        raise ValueError("x must be [n, L]")
+    n, L = x.shape
+    states = np.empty((n, L), dtype=np.int32)
+    X = np.empty(n, dtype=np.int32)
+    cost = np.empty(n, dtype=np.float32)
+    if n == 0:
+        return states, X, cost
+    lib = _load()
+    threads = threads or default_threads()
+    chunks = np.array_split(np.arange(n), min(threads, n))
+
+    def run(idx):
+        if idx.size == 0:
+            return 0
+        i0 = int(idx[0])
+        m = int(idx.size)
+        return lib.oracle_encode_many(
+            x[i0:].ctypes.data, m, L, Q, K, v,
+            states[i0:].ctypes.data, X[i0:].ctypes.data, cost[i0:].ctypes.data)
+
+    if len(chunks) == 1:
+        rcs = [run(chunks[0])]
+    else:
+        with ThreadPoolExecutor(max_workers=len(chunks)) as ex:
+            rcs = list(ex.map(run, chunks))
+    if any(rc != 0 for rc in rcs):
+        raise ValueError("oracle_encode_many rejected its arguments (rc=%s)" % rcs)
+    return states, X, cost
+
+
+def tile_sse(x, states, v):
+    """Sequential binary32 sum over t of rn(rn(x_t - v[S_t])^2), from +0."""
+    x = np.asarray(x, dtype=np.float32)
+    what = v[states]
+    acc = np.zeros(x.shape[0], dtype=np.float32)
+    for t in range(x.shape[1]):
+        d = x[:, t] - what[:, t]
+        acc = acc + d * d
+    return acc
+
+
+# --------------------------------------------------------------------------
+# Container  [P1 item 5: MSB-first packing of the low K bits, SWAP16]
+# --------------------------------------------------------------------------
+def pack_states(states, K):
+    """[n, 256] states -> [n, 16*K] uint16 words (MSB-first stream, then SWAP16)."""
+    states = np.asarray(states, dtype=np.int64)
+    n, L = states.shape
+    b = states & ((1 << K) - 1)
+    # stream bit j = bit (K-1-(j mod K)) of b_(j div K)
+    shifts = np.arange(K - 1, -1, -1)
+    bits = (b[:, :, None] >> shifts[None, None, :]) & 1          # [n, L, K]
+    bits = bits.reshape(n, (L * K) // 16, 16)
+    weights = (1 << np.arange(15, -1, -1)).astype(np.int64)
+    words = (bits * weights).sum(axis=2)                          # stream bit 16w -> bit 15
+    swapped = words.reshape(n, -1, 2)[:, :, ::-1].reshape(n, -1)  # words 2i <-> 2i+1
+    return swapped.astype(np.uint16)
+
+
+def unpack_states(words, K, L=256):
+    """Inverse view: S_t = the 16-bit window of the circular stream ending at bit (t+1)K-1."""
+    words = np.asarray(words, dtype=np.int64)
+    n = words.shape[0]
+    w = words.reshape(n, -1, 2)[:, :, ::-1].reshape(n, -1)        # undo SWAP16
+    bits = (w[:, :, None] >> np.arange(15, -1, -1)[None, None, :]) & 1
+    stream = bits.reshape(n, -1)                                  # [n, L*K]
+    nbits = L * K
+    out = np.zeros((n, L), dtype=np.int64)
+    for t in range(L):
+        end = (t + 1) * K                                         # exclusive
+        idx = np.arange(end - 16, end) % nbits
+        val = np.zeros(n, dtype=np.int64)
+        for j in idx:
+            val = (val << 1) | stream[:, j]
+        out[:, t] = val
+    return out.astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# Regularization  [P1 items 7 and 8]
+# --------------------------------------------------------------------------
+def hadamard_norm(B: int) -> np.float32:
+    """Binary32 normalisation constant 1/sqrt(B) for the supported block sizes."""
+    if B == 64:
+        return np.float32(0.125)
+    if B == 128:
+        return np.frombuffer(np.uint32(0x3DB504F3).tobytes(), dtype=np.float32)[0]
+    raise ValueError("Hadamard block must be 64 or 128")
+
+
+def fwht_rows_blockwise(a, B):
+    """In-place-order fast Walsh-Hadamard transform along axis 0, in blocks of B rows.
+
+    Levels h = 1, 2, 4, ..., B/2; at each level every pair (p, p+h) with
+    p mod 2h < h becomes (a+b, a-b), each rounded to binary32.
+    """
+    a = np.asarray(a, dtype=np.float32)
+    R, C = a.shape
+    if R % B:
+        raise ValueError("rows not a multiple of the block")
+    y = a.reshape(R // B, B, C).copy()
+    h = 1
+    while h < B:
+        y = y.reshape(R // B, B // (2 * h), 2, h, C)
+        top = y[:, :, 0]
+        bot = y[:, :, 1]
+        s = top + bot
+        d = top - bot
+        y = np.stack([s, d], axis=2)
+        h *= 2
+    return y.reshape(R, C)
+
+
+def regularize(w, su, sv, B):
+    """W_reg = H_l diag(su) W diag(sv) H_r, evaluated in the fixed order of the header."""
+    w = np.asarray(w, dtype=np.float32)
+    su = np.asarray(su, dtype=np.float32)
+    sv = np.asarray(sv, dtype=np.float32)
+    c = hadamard_norm(B)
+    y = (w * su[:, None]) * sv[None, :]             # exact: sign flips
+    y = fwht_rows_blockwise(y, B) * c               # left side, then normalise
+    y = fwht_rows_blockwise(y.T, B).T * c           # right side, then normalise
+    return np.ascontiguousarray(y, dtype=np.float32)
+
+
+def unregularize(w_reg, su, sv, B):
+    """Inverse of regularize (H is its own inverse); validation only."""
+    c = hadamard_norm(B)
+    y = fwht_rows_blockwise(np.asarray(w_reg, np.float32), B) * c
+    y = fwht_rows_blockwise(y.T, B).T * c
+    return (y * np.asarray(su, np.float32)[:, None]) * np.asarray(sv, np.float32)[None, :]
+
+
+def to_tiles(m):
+    """[R, C] -> [R/16 * C/16, 256]; tile tr*TC + tc, element 16*r + c."""
+    R, C = m.shape
+    return np.ascontiguousarray(
+        m.reshape(R // 16, 16, C // 16, 16).transpose(0, 2, 1, 3).reshape(-1, 256))
+
+
+def from_tiles(tiles, R, C):
+    return np.ascontiguousarray(
+        np.asarray(tiles).reshape(R // 16, C // 16, 16, 16).transpose(0, 2, 1, 3).reshape(R, C))
+
+
+# --------------------------------------------------------------------------
+# Statistics, tile sample and scale search  [P1 item 8; P2 section 2]
+# --------------------------------------------------------------------------
+def tile_sumsq(tiles):
+    """Sequential binary32 sum over t of rn(w_t * w_t), per tile."""
+    tiles = np.asarray(tiles, dtype=np.float32)
+    acc = np.zeros(tiles.shape[0], dtype=np.float32)
+    for t in range(tiles.shape[1]):
+        acc = acc + tiles[:, t] * tiles[:, t]
+    return acc
+
+
+def matrix_rms(sumsq, n_elems):
+    total = 0.0
+    for q in sumsq.tolist():                # ascending tile index, binary64
+        total += float(q)
+    return math.sqrt(total / n_elems)
+
+
+def sample_tiles(TR, TC, sumsq):
+    """Wrapped diagonal plus the largest- and smallest-energy tiles, ascending."""
+    picked = set()
+    for i in range(max(TR, TC)):
+        picked.add((i % TR) * TC + (i % TC))
+    picked.add(int(np.argmax(sumsq)))       # first occurrence = lowest index
+    picked.add(int(np.argmin(sumsq)))
+    return sorted(picked)
+
+
+GOLDEN = (math.sqrt(5.0) - 1.0) / 2.0
+
+
+def golden_section(f, lo, hi, iters):
+    """Golden-section minimisation of f on [lo, hi]; returns (midpoint, trace).
+
+    Two probes p < q inside the bracket; if f(p) < f(q) the right end moves to
+    q, otherwise the left end moves to p; one new probe per reduction.
+    """
+    a, b = lo, hi
+    p = b - (b - a) * GOLDEN
+    q = a + (b - a) * GOLDEN
+    fp = f(p)
+    fq = f(q)
+    trace = [(p, fp), (q, fq)]
+    for _ in range(iters):
+        if fp < fq:
+            b = q
+            q = p
+            fq = fp
+            p = b - (b - a) * GOLDEN
+            fp = f(p)
+            trace.append((p, fp))
+        else:
+            a = p
+            p = q
+            fp = fq
+            q = a + (b - a) * GOLDEN
+            fq = f(q)
+            trace.append((q, fq))
+    return (a + b) / 2.0, trace
+
+
+def encode_tiles(tiles, K, scale, levels=None, threads=None):
+    """Encode tiles [n, 256] at a fixed binary32 scale.
+
+    Returns dict(states, X, sse, packed).  sse is the pass-2 path cost, which is
+    also the sequential sum of squared errors of the dequantised tile.
+    """
+    if levels is None:
+        levels = mul1_levels_fp16()
+    v = scaled_levels(levels, scale)
+    states, X, cost = encode_sequences(tiles, K, v, threads=threads)
+    return {"states": states, "X": X, "sse": cost, "packed": pack_states(states, K)}
+
+
+def quantize_matrix(w, su, sv, K, had_block=128, gss=(12, 0.5, 2.0), fixed_scale=1.0,
+                    levels=None, threads=None, tiles_subset=None):
+    """Whole-matrix path: regularize, statistics, scale search, final encode.
+
+    gss=None uses fixed_scale.  tiles_subset, if given, restricts the FINAL
+    encode to those tile indices (the scale search always uses its full sample),
+    which is how large matrices are checked one sampled tile at a time.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    R, C = w.shape
+    if levels is None:
+        levels = mul1_levels_fp16()
+    w_reg = regularize(w, su, sv, had_block)
+    tiles = to_tiles(w_reg)
+    TR, TC = R // 16, C // 16
+    sumsq = tile_sumsq(tiles)
+    rms = matrix_rms(sumsq, R * C)
+    out = {"tiles": tiles, "sumsq": sumsq, "rms": rms}
+    if gss is None:
+        scale = np.float32(fixed_scale)
+        out["sample"] = []
+        out["trace"] = []
+    else:
+        iters, lo, hi = gss
+        sample = sample_tiles(TR, TC, sumsq)
+        out["sample"] = sample
+        if rms == 0.0:
+            scale = np.float32(0.0)
+            out["trace"] = []
+        else:
+            xs = tiles[sample]
+
+            def objective(s):
+                r = encode_tiles(xs, K, np.float32(s), levels, threads)
+                total = 0.0
+                for e in r["sse"].tolist():
+                    total += float(e)
+                return total
+
+            mid, trace = golden_section(objective, lo * rms, hi * rms, iters)
+            scale = np.float32(mid)
+            out["trace"] = trace
+    out["scale"] = scale
+    idx = np.arange(TR * TC) if tiles_subset is None else np.asarray(tiles_subset)
+    r = encode_tiles(tiles[idx], K, scale, levels, threads)
+    out.update({"index": idx, "states": r["states"], "X": r["X"], "sse": r["sse"],
+                "packed": r["packed"]})
+    if tiles_subset is None:
+        total = 0.0
+        for e in r["sse"].tolist():
+            total += float(e)
+        out["mse"] = total / (R * C)
+    return out
