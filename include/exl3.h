@@ -1,0 +1,176 @@
+/*
+ * exl3.h -- C ABI of the MI355X (gfx950) EXL3 trellis tile encoder.
+ *
+ * Sources of the operations (cited by page title and section):
+ *   [P1] "EXL3 Intel Arc Quantizer" README, Core Implemented Architecture:
+ *        section 1 (tile encoder: add-compare-select dynamic program, two-pass
+ *        tail-biting closure), section 4 (16-bit state algebra), section 5
+ *        (mul1 codebook, MSB-first container with SWAP16), section 7 (blockwise
+ *        Sylvester Hadamard), section 8 (regularization and scale search over a
+ *        wrapped-diagonal tile sample), section 2 (bounded scratch, admission
+ *        before work, batch halving that keeps results identical).
+ *   [P2] "JEV-9B EXL3 K=2 (mul1) Checkpoint" model card, section 2
+ *        (golden-section scale search).
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer on the context's device unless
+ *     stated otherwise; the caller owns it.  The library never frees it and
+ *     never keeps it beyond the work it enqueued on the context's stream.
+ *   - Calls return EXL3_OK (0) or a negative EXL3_E* code and never throw.
+ *     exl3_last_error() gives the message.  Arguments are validated before
+ *     anything is enqueued: on an error return no output has been written.
+ *   - Arithmetic contract: binary32, each subtract / multiply / add rounded on
+ *     its own (no fused multiply-add), lowest index on equal costs.  Outputs
+ *     are bit-identical for any batch size and scratch limit.
+ *   - A context is not thread-safe; use one per host thread / stream.
+ *   - Tiles: a 16x16 tile is 256 consecutive floats, element t = 16*row + col;
+ *     tile tau = tr * (cols/16) + tc of a rows x cols matrix.
+ */
+#ifndef EXL3_H
+#define EXL3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    EXL3_OK = 0,
+    EXL3_EINVAL = -1,        /* bad argument (null pointer, shape, sign vector, ...) */
+    EXL3_ENOMEM = -2,        /* scratch limit below one tile, or device allocation failed */
+    EXL3_ENONFINITE = -3,    /* NaN or Inf in the weight matrix */
+    EXL3_EHIP = -4,          /* a HIP runtime call failed; the context stays usable */
+    EXL3_EUNSUPPORTED = -5   /* K or Hadamard block not supported */
+};
+
+enum { EXL3_F32 = 0, EXL3_BF16 = 1 };              /* weight storage type */
+enum { EXL3_ROW_MAJOR = 0, EXL3_TILE_MAJOR = 1 };  /* layout of regularized output */
+
+typedef struct exl3_ctx exl3_ctx;
+
+/* Golden-section scale search [P2 section 2; P1 section 8]: bracket
+ * [lo * rms, hi * rms], two initial probes, then `iters` reductions. */
+typedef struct {
+    int iters;
+    double lo;
+    double hi;
+} exl3_gss;
+
+/* Library version string (static storage). */
+const char *exl3_version(void);
+
+/*
+ * Create a context on HIP device `device`.  `hip_stream` is a hipStream_t the
+ * caller owns (NULL = the null stream); every call enqueues on it.
+ * `scratch_bytes` bounds the backpointer scratch the context may allocate
+ * (0 = a default of 8 GiB); batches are sized to fit it [P1 section 2].
+ * The context uploads the mul1 level table (65,536 fp16 values, 128 KiB).
+ * Errors: EXL3_EINVAL (out == NULL), EXL3_EHIP (device unusable).
+ */
+int exl3_ctx_create(exl3_ctx **out, int device, void *hip_stream, size_t scratch_bytes);
+
+/* Destroy a context: waits for its stream, frees what it allocated.  NULL is ignored. */
+void exl3_ctx_destroy(exl3_ctx *ctx);
+
+/* Last error message of this context ("" if none); never NULL.  ctx may be NULL. */
+const char *exl3_last_error(const exl3_ctx *ctx);
+
+/* Change the stream later calls enqueue on (the caller still owns it). */
+int exl3_ctx_set_stream(exl3_ctx *ctx, void *hip_stream);
+
+/*
+ * Replace the level table with caller-supplied fp16 values (HOST pointer,
+ * 65,536 uint16 bit patterns, copied before return).  NULL restores mul1.
+ * Used to run other procedural codebooks or synthetic tables through the
+ * same kernels.  Errors: EXL3_EINVAL (a value is NaN or Inf), EXL3_EHIP.
+ */
+int exl3_set_codebook(exl3_ctx *ctx, const uint16_t *levels_fp16_host);
+
+/* Copy the current level table to a HOST buffer of 65,536 uint16. */
+int exl3_get_codebook(exl3_ctx *ctx, uint16_t *levels_fp16_host);
+
+/*
+ * Regularize a weight matrix [P1 sections 7 and 8]:
+ *   W_reg = H_l diag(su) W diag(sv) H_r
+ * where H_l / H_r apply the natural-order Sylvester Hadamard of size had_block
+ * to each block of had_block rows / columns, each normalised by the binary32
+ * value of 1/sqrt(had_block).  Order of evaluation: sign flips, left
+ * transform, normalisation, right transform, normalisation.
+ *   w          [rows][cols] row-major, w_dtype EXL3_F32 or EXL3_BF16
+ *   su, sv     float [rows], float [cols]; every entry exactly +1 or -1
+ *   w_reg      float [rows*cols]; row-major or tile-major (out_layout)
+ *   tile_sumsq optional float [(rows/16)*(cols/16)]: per tile, the sequential
+ *              binary32 sum over t = 0..255 of rn(w_t * w_t)
+ *   nonfinite  optional int [1]: set to 1 if W holds NaN/Inf (left unchanged
+ *              otherwise; the caller clears it)
+ * rows and cols must be multiples of had_block (64 or 128).  Asynchronous.
+ * Errors: EXL3_EINVAL, EXL3_EUNSUPPORTED, EXL3_EHIP.
+ */
+int exl3_regularize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
+                    int had_block, const float *su, const float *sv, float *w_reg,
+                    int out_layout, float *tile_sumsq, int *nonfinite);
+
+/*
+ * Encode n tiles at a fixed binary32 scale [P1 sections 1, 4, 5]:
+ * a two-pass tail-biting Viterbi search over the 16-bit bitshift trellis that
+ * shifts in K bits per step, comparing each input with v[s] = rn(scale*c[s]).
+ *   x         float [n][256] tile-major inputs (finite; otherwise the output is
+ *             unspecified but the call stays memory-safe)
+ *   packed    uint16 [n][16*K]: the low K bits of each state, MSB-first, then
+ *             words 2i and 2i+1 swapped
+ *   states    optional uint16 [n][256]: the state sequence S_0..S_255
+ *   tile_sse  optional float [n]: sequential binary32 sum of squared errors of
+ *             the decoded tile, which equals the search's own path cost
+ * K in {2, 3, 4}.  n may be 0.  Asynchronous (uses the context's scratch).
+ * Errors: EXL3_EINVAL, EXL3_EUNSUPPORTED, EXL3_ENOMEM, EXL3_EHIP.
+ */
+int exl3_encode_tiles(exl3_ctx *ctx, const float *x, int64_t n, int K, float scale,
+                      uint16_t *packed, uint16_t *states, float *tile_sse);
+
+/*
+ * Decode n packed tiles [P1 section 5]: S_t = the 16-bit window of the
+ * circular bit stream that ends at bit (t+1)*K - 1; out[t] = rn(scale*c[S_t]).
+ *   packed uint16 [n][16*K] (as written by exl3_encode_tiles), out float [n][256].
+ * K in 1..8.  Asynchronous.  Errors: EXL3_EINVAL, EXL3_EUNSUPPORTED, EXL3_EHIP.
+ */
+int exl3_decode_tiles(exl3_ctx *ctx, const uint16_t *packed, int64_t n, int K, float scale,
+                      float *out);
+
+/*
+ * Whole-matrix quantization [P1 sections 1, 7, 8; P2 section 2]:
+ * regularize, per-tile energy, rms = sqrt(sum / (rows*cols)) in binary64,
+ * then either the fixed scale (gss == NULL) or a golden-section search for the
+ * scale on the tile sample (wrapped diagonal plus the highest- and
+ * lowest-energy tiles), whose objective is the binary64 sum, in ascending tile
+ * order, of the sample tiles' squared errors; the result is the midpoint of the
+ * final bracket rounded to binary32 (0 when rms is 0).  Then every tile is
+ * encoded at that scale.
+ *   w, w_dtype, rows, cols, had_block, su, sv : as exl3_regularize
+ *   packed    uint16 [rows/16][cols/16][16*K]
+ *   scale_out HOST float [1]: the scale used
+ *   mse_out   optional HOST double [1]: binary64 sum of tile errors / (rows*cols)
+ *   w_hat     optional float [rows*cols]: dequantized weights in the
+ *             regularized domain, tile-major
+ *   tile_sse  optional float [tiles]: per-tile squared error
+ * Synchronizes the stream (the scale search reads results back); returns after
+ * all work is complete.  Errors: EXL3_EINVAL, EXL3_EUNSUPPORTED, EXL3_ENOMEM,
+ * EXL3_ENONFINITE (before any encode), EXL3_EHIP.
+ */
+int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
+                         int K, int had_block, const float *su, const float *sv,
+                         const exl3_gss *gss, float fixed_scale, uint16_t *packed,
+                         float *scale_out, double *mse_out, float *w_hat, float *tile_sse);
+
+/*
+ * Scratch bytes one tile needs in flight at this K (backpointers of the
+ * longer pass plus per-tile bookkeeping).  0 for an unsupported K.
+ */
+size_t exl3_scratch_per_tile(int K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXL3_H */

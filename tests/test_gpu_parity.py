@@ -1,0 +1,239 @@
+"""GPU library against the oracle, element by element, through the C ABI.
+
+Bar: bit-exact for states, packed words, backpointer-derived end states,
+regularized weights, per-tile energies and squared errors, decoded values and
+the scale chosen by the golden-section search (the fixed binary64 summation
+order makes it exact, inside the 1e-5 relative bound).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    import trellis_coded_weight_amd as T
+    c = T.Context(0)
+    yield c
+    c.close()
+
+
+def _u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def _bits(a):
+    return np.asarray(a, np.float32).view(np.uint32)
+
+
+def test_level_table_matches_oracle(ctx):
+    lv = ctx.get_codebook().numpy().view(np.uint16)
+    assert np.array_equal(lv, oracle.mul1_levels_fp16().view(np.uint16))
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+def test_encode_tiles_bit_exact(ctx, K):
+    n = 37                                   # several workgroups, odd count
+    x = workloads.random_tiles(n, 100 + K)
+    want = oracle.encode_tiles(x, K, 1.0)
+    xd = torch.from_numpy(x).to(DEV)
+    packed, states, sse = ctx.encode_tiles(xd, K, 1.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(_u16(states), want["states"].astype(np.uint16))
+    assert np.array_equal(_u16(packed), want["packed"])
+    assert np.array_equal(_bits(sse.cpu().numpy()), _bits(want["sse"]))
+
+
+@pytest.mark.parametrize("K,scale", [(2, 0.0173), (3, 2.5), (4, 0.9)])
+def test_encode_tiles_scaled_inputs(ctx, K, scale):
+    x = workloads.random_tiles(9, 200 + K, std=scale)
+    want = oracle.encode_tiles(x, K, scale)
+    packed, states, sse = ctx.encode_tiles(torch.from_numpy(x).to(DEV), K, scale)
+    assert np.array_equal(_u16(states), want["states"].astype(np.uint16))
+    assert np.array_equal(_bits(sse.cpu().numpy()), _bits(want["sse"]))
+
+
+def test_edge_inputs(ctx):
+    """Zeros, a constant tile, huge outliers, tiny (subnormal-producing) values."""
+    K = 2
+    x = np.zeros((5, 256), np.float32)
+    x[1] = 0.37
+    x[2, ::17] = 1.0e4
+    x[3] = np.float32(1e-20) * np.arange(256, dtype=np.float32)
+    x[4] = workloads.random_tiles(1, 5)[0] * np.float32(1e-19)
+    for scale in (1.0, 1e-19):
+        want = oracle.encode_tiles(x, K, scale)
+        _, states, sse = ctx.encode_tiles(torch.from_numpy(x).to(DEV), K, scale)
+        assert np.array_equal(_u16(states), want["states"].astype(np.uint16))
+        assert np.array_equal(_bits(sse.cpu().numpy()), _bits(want["sse"]))
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+def test_ties_follow_lowest_index(ctx, K):
+    """A table with 5 distinct levels: exact ties everywhere; the tie rule decides."""
+    rng = np.random.default_rng(K)
+    lv = rng.choice(np.array([-1.5, -0.5, 0.0, 0.5, 1.5], np.float16), size=65536)
+    x = (np.round(workloads.random_tiles(6, 300 + K) * 2) / 2).astype(np.float32)
+    want = oracle.encode_tiles(x, K, 1.0, levels=lv)
+    ctx.set_codebook(torch.from_numpy(lv))
+    try:
+        _, states, sse = ctx.encode_tiles(torch.from_numpy(x).to(DEV), K, 1.0)
+        assert np.array_equal(_u16(states), want["states"].astype(np.uint16))
+        assert np.array_equal(_bits(sse.cpu().numpy()), _bits(want["sse"]))
+    finally:
+        ctx.set_codebook(None)
+
+
+def test_scalar_quantiser_case_on_gpu(ctx):
+    K = 2
+    lev = np.array([-1.25, -0.375, 0.5, 1.5], np.float16)
+    lv = lev[np.arange(65536) & 3]
+    x = workloads.random_tiles(4, 9)
+    ctx.set_codebook(torch.from_numpy(lv))
+    try:
+        _, states, _ = ctx.encode_tiles(torch.from_numpy(x).to(DEV), K, 1.0)
+    finally:
+        ctx.set_codebook(None)
+    err = (x[:, :, None] - lev.astype(np.float32)[None, None, :]) ** 2
+    assert np.array_equal(_u16(states) & 3, np.argmin(err, axis=2).astype(np.uint16))
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 5, 8])
+def test_decode_matches_oracle(ctx, K):
+    rng = np.random.default_rng(K)
+    n = 7
+    b = rng.integers(0, 1 << K, (n, 256))
+    states = np.zeros((n, 256), np.int64)
+    for t in range(256):
+        s = np.zeros(n, np.int64)
+        for j in range(-(16 // K) - 1, 1):
+            s = ((s << K) | b[:, (t + j) % 256]) & 0xFFFF
+        states[:, t] = s
+    packed = oracle.pack_states(states, K)
+    v = oracle.scaled_levels(oracle.mul1_levels_fp16(), 0.75)
+    out = ctx.decode_tiles(torch.from_numpy(packed.view(np.int16)).to(DEV), K, 0.75)
+    assert np.array_equal(_bits(out.cpu().numpy()), _bits(v[states]))
+
+
+@pytest.mark.parametrize("B,dtype", [(64, torch.float32), (128, torch.bfloat16),
+                                     (128, torch.float32)])
+def test_regularize_bit_exact(ctx, B, dtype):
+    R, C = 2 * B, 3 * B
+    rng = np.random.default_rng(B)
+    w = (rng.standard_normal((R, C)) * 0.02).astype(np.float32)
+    wt = torch.from_numpy(w).to(dtype)
+    w32 = wt.to(torch.float32).numpy()
+    su = (2 * rng.integers(0, 2, R) - 1).astype(np.float32)
+    sv = (2 * rng.integers(0, 2, C) - 1).astype(np.float32)
+    want = oracle.regularize(w32, su, sv, B)
+    out, sums, flag = ctx.regularize(wt.to(DEV), torch.from_numpy(su).to(DEV),
+                                     torch.from_numpy(sv).to(DEV), B)
+    tiles = oracle.to_tiles(want)
+    assert np.array_equal(_bits(out.cpu().numpy()), _bits(tiles))
+    assert np.array_equal(_bits(sums.cpu().numpy()), _bits(oracle.tile_sumsq(tiles)))
+    assert int(flag.item()) == 0
+    rm, _, _ = ctx.regularize(wt.to(DEV), torch.from_numpy(su).to(DEV),
+                              torch.from_numpy(sv).to(DEV), B, tile_major=False)
+    assert np.array_equal(_bits(rm.cpu().numpy()), _bits(want))
+
+
+def test_workload1_whole_path(ctx):
+    m = workloads.config(1)[0]
+    want = oracle.quantize_matrix(m.w, m.su, m.sv, m.K, had_block=m.had_block, gss=None,
+                                  fixed_scale=1.0)
+    got = ctx.quantize_matrix(torch.from_numpy(m.w).to(DEV), m.K,
+                              torch.from_numpy(m.su).to(DEV), torch.from_numpy(m.sv).to(DEV),
+                              had_block=m.had_block, gss=None, scale=1.0, want_w_hat=True,
+                              want_tile_sse=True)
+    assert got["scale"] == 1.0
+    assert np.array_equal(_u16(got["packed"]).reshape(-1, 32), want["packed"])
+    assert np.array_equal(_bits(got["tile_sse"].cpu().numpy()), _bits(want["sse"]))
+    assert got["mse"] == want["mse"]
+    v = oracle.scaled_levels(oracle.mul1_levels_fp16(), 1.0)
+    assert np.array_equal(_bits(got["w_hat"].cpu().numpy()), _bits(v[want["states"]]))
+
+
+@pytest.mark.parametrize("K", [2, 4])
+def test_small_matrix_with_scale_search(ctx, K):
+    m = workloads.gaussian(256, 384, 0.02, 31 + K, 41 + K, K=K)
+    want = oracle.quantize_matrix(m.w, m.su, m.sv, K, had_block=128, gss=m.gss)
+    got = ctx.quantize_matrix(torch.from_numpy(m.w).to(torch.bfloat16).to(DEV), K,
+                              torch.from_numpy(m.su).to(DEV), torch.from_numpy(m.sv).to(DEV),
+                              had_block=128, gss=m.gss, want_tile_sse=True)
+    assert abs(got["scale"] - float(want["scale"])) <= 1e-5 * abs(float(want["scale"]))
+    assert np.float32(got["scale"]) == want["scale"]
+    assert np.array_equal(_u16(got["packed"]).reshape(-1, 16 * K), want["packed"])
+    assert np.array_equal(_bits(got["tile_sse"].cpu().numpy()), _bits(want["sse"]))
+    assert got["mse"] == want["mse"]
+
+
+def test_batching_does_not_change_results():
+    import trellis_coded_weight_amd as T
+    x = workloads.random_tiles(11, 77)
+    xd = torch.from_numpy(x).to(DEV)
+    outs = []
+    for scratch in (0, T.scratch_per_tile(2) * 3, T.scratch_per_tile(2)):
+        with T.Context(0, scratch_bytes=scratch) as c:
+            p, s, e = c.encode_tiles(xd, 2, 1.0)
+            torch.cuda.synchronize()
+            outs.append((_u16(p), _u16(s), _bits(e.cpu().numpy())))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)
+
+
+def test_errors_leave_outputs_untouched(ctx):
+    import trellis_coded_weight_amd as T
+    x = torch.zeros(2, 256, device=DEV)
+    with pytest.raises(T.Exl3Error) as e:
+        ctx.encode_tiles(x, 5, 1.0)
+    assert e.value.code == T.EXL3_EUNSUPPORTED
+    with pytest.raises(T.Exl3Error) as e:
+        ctx.encode_tiles(x, 2, float("nan"))
+    assert e.value.code == T.EXL3_EINVAL
+    w = torch.zeros(128, 128, device=DEV)
+    su = torch.ones(128, device=DEV)
+    bad = su.clone()
+    bad[3] = 0.5
+    with pytest.raises(T.Exl3Error) as e:
+        ctx.quantize_matrix(w, 2, bad, su)
+    assert e.value.code == T.EXL3_EINVAL
+    with pytest.raises(T.Exl3Error) as e:
+        ctx.quantize_matrix(torch.zeros(96, 128, device=DEV), 2, torch.ones(96, device=DEV), su)
+    assert e.value.code == T.EXL3_EINVAL
+    w2 = w.clone()
+    w2[5, 7] = float("inf")
+    with pytest.raises(T.Exl3Error) as e:
+        ctx.quantize_matrix(w2, 2, su, su)
+    assert e.value.code == T.EXL3_ENONFINITE
+    with T.Context(0, scratch_bytes=1000) as small:
+        packed = torch.full((2, 32), 7, dtype=torch.int16, device=DEV)
+        rc = small.lib.exl3_encode_tiles(small.handle, x.data_ptr(), 2, 2, 1.0,
+                                         packed.data_ptr(), None, None)
+        assert rc == T.EXL3_ENOMEM
+        assert bool((packed == 7).all())
+    # the context still works after errors
+    p, s, e2 = ctx.encode_tiles(x, 2, 1.0)
+    want = oracle.encode_tiles(np.zeros((2, 256), np.float32), 2, 1.0)
+    assert np.array_equal(_u16(s), want["states"].astype(np.uint16))
+
+
+def test_zero_matrix_gives_zero_scale(ctx):
+    w = torch.zeros(128, 128, device=DEV, dtype=torch.bfloat16)
+    su = torch.ones(128, device=DEV)
+    got = ctx.quantize_matrix(w, 2, su, su)
+    assert got["scale"] == 0.0
+    assert bool((got["packed"] == 0).all())
+
+
+def test_empty_input(ctx):
+    x = torch.empty(0, 256, device=DEV)
+    p, s, e = ctx.encode_tiles(x, 3, 1.0)
+    assert p.shape == (0, 48)

@@ -1,0 +1,258 @@
+"""Thin ctypes binding of libexl3_gfx950.so (names follow include/exl3.h).
+
+Only argument marshalling happens here: torch tensors give device pointers and
+the current HIP stream; every step of the encoder runs in the library's
+kernels.  There is no CPU fallback -- if the library or a GPU is missing, the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+from . import build as _build
+
+EXL3_OK = 0
+EXL3_EINVAL = -1
+EXL3_ENOMEM = -2
+EXL3_ENONFINITE = -3
+EXL3_EHIP = -4
+EXL3_EUNSUPPORTED = -5
+EXL3_F32 = 0
+EXL3_BF16 = 1
+EXL3_ROW_MAJOR = 0
+EXL3_TILE_MAJOR = 1
+
+EXPORTED = [
+    "exl3_version", "exl3_ctx_create", "exl3_ctx_destroy", "exl3_last_error",
+    "exl3_ctx_set_stream", "exl3_set_codebook", "exl3_get_codebook", "exl3_regularize",
+    "exl3_encode_tiles", "exl3_decode_tiles", "exl3_quantize_matrix", "exl3_scratch_per_tile",
+]
+
+
+class Exl3Error(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("exl3 error %d: %s" % (code, msg))
+        self.code = code
+        self.msg = msg
+
+
+class GSS(ctypes.Structure):
+    _fields_ = [("iters", ctypes.c_int), ("lo", ctypes.c_double), ("hi", ctypes.c_double)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def load_library():
+    """Load the built library (never builds; raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        raise FileNotFoundError(
+            "libexl3_gfx950.so is not built; run __graft_entry__.build() or "
+            "python trellis_coded_weight_amd/build.py")
+    lib = ctypes.CDLL(_build.LIB)
+    vp, i32, i64, f32, f64, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                  ctypes.c_float, ctypes.c_double, ctypes.c_size_t)
+    lib.exl3_version.restype = ctypes.c_char_p
+    lib.exl3_version.argtypes = []
+    lib.exl3_ctx_create.restype = i32
+    lib.exl3_ctx_create.argtypes = [ctypes.POINTER(vp), i32, vp, sz]
+    lib.exl3_ctx_destroy.restype = None
+    lib.exl3_ctx_destroy.argtypes = [vp]
+    lib.exl3_last_error.restype = ctypes.c_char_p
+    lib.exl3_last_error.argtypes = [vp]
+    lib.exl3_ctx_set_stream.restype = i32
+    lib.exl3_ctx_set_stream.argtypes = [vp, vp]
+    lib.exl3_set_codebook.restype = i32
+    lib.exl3_set_codebook.argtypes = [vp, vp]
+    lib.exl3_get_codebook.restype = i32
+    lib.exl3_get_codebook.argtypes = [vp, vp]
+    lib.exl3_regularize.restype = i32
+    lib.exl3_regularize.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
+    lib.exl3_encode_tiles.restype = i32
+    lib.exl3_encode_tiles.argtypes = [vp, vp, i64, i32, f32, vp, vp, vp]
+    lib.exl3_decode_tiles.restype = i32
+    lib.exl3_decode_tiles.argtypes = [vp, vp, i64, i32, f32, vp]
+    lib.exl3_quantize_matrix.restype = i32
+    lib.exl3_quantize_matrix.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp,
+                                         ctypes.POINTER(GSS), f32, vp, ctypes.POINTER(f32),
+                                         ctypes.POINTER(f64), vp, vp]
+    lib.exl3_scratch_per_tile.restype = sz
+    lib.exl3_scratch_per_tile.argtypes = [i32]
+    _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, dtype, shape, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+class Context:
+    """One library context (scratch, level table) bound to a device."""
+
+    def __init__(self, device: int = 0, scratch_bytes: int = 0):
+        if not torch.cuda.is_available():
+            raise RuntimeError("the EXL3 encoder needs a GPU; none is visible")
+        self.lib = load_library()
+        self.device = torch.device("cuda", device)
+        h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            rc = self.lib.exl3_ctx_create(ctypes.byref(h), device,
+                                          ctypes.c_void_p(_stream_handle(self.device)),
+                                          scratch_bytes)
+        if rc != EXL3_OK:
+            raise Exl3Error(rc, "context creation failed")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.exl3_ctx_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.close()
+
+    # -- helpers --
+    def _sync_stream(self):
+        rc = self.lib.exl3_ctx_set_stream(self.handle,
+                                          ctypes.c_void_p(_stream_handle(self.device)))
+        self._check(rc)
+
+    def _check(self, rc):
+        if rc != EXL3_OK:
+            raise Exl3Error(rc, self.lib.exl3_last_error(self.handle).decode())
+
+    def last_error(self) -> str:
+        return self.lib.exl3_last_error(self.handle).decode()
+
+    # -- API --
+    def set_codebook(self, levels_fp16: Optional[torch.Tensor]):
+        """levels_fp16: host tensor of 65536 float16 values (None restores mul1)."""
+        self._sync_stream()
+        if levels_fp16 is None:
+            return self._check(self.lib.exl3_set_codebook(self.handle, None))
+        lv = levels_fp16.detach().cpu().contiguous().view(torch.int16)
+        if lv.numel() != 65536:
+            raise ValueError("need 65536 levels")
+        self._check(self.lib.exl3_set_codebook(self.handle, ctypes.c_void_p(lv.data_ptr())))
+
+    def get_codebook(self) -> torch.Tensor:
+        out = torch.empty(65536, dtype=torch.int16)
+        self._sync_stream()
+        self._check(self.lib.exl3_get_codebook(self.handle, ctypes.c_void_p(out.data_ptr())))
+        return out.view(torch.float16)
+
+    def regularize(self, w: torch.Tensor, su: torch.Tensor, sv: torch.Tensor,
+                   had_block: int = 128, tile_major: bool = True):
+        """Returns (w_reg float32, tile_sumsq float32 [tiles], nonfinite int32 [1])."""
+        rows, cols = w.shape
+        dt = {torch.float32: EXL3_F32, torch.bfloat16: EXL3_BF16}.get(w.dtype)
+        if dt is None:
+            raise ValueError("w must be float32 or bfloat16")
+        w = w.contiguous()
+        if tile_major:
+            out = torch.empty((rows // 16) * (cols // 16), 256, dtype=torch.float32,
+                              device=w.device)
+        else:
+            out = torch.empty(rows, cols, dtype=torch.float32, device=w.device)
+        sums = torch.empty((rows // 16) * (cols // 16), dtype=torch.float32, device=w.device)
+        flag = torch.zeros(1, dtype=torch.int32, device=w.device)
+        self._sync_stream()
+        self._check(self.lib.exl3_regularize(
+            self.handle, _ptr(w), dt, rows, cols, had_block, _ptr(su.contiguous()),
+            _ptr(sv.contiguous()), _ptr(out), EXL3_TILE_MAJOR if tile_major else EXL3_ROW_MAJOR,
+            _ptr(sums), _ptr(flag)))
+        return out, sums, flag
+
+    def encode_tiles(self, x: torch.Tensor, K: int, scale: float, want_states: bool = True,
+                     want_sse: bool = True):
+        """x float32 [n, 256] -> (packed int16 [n, 16K], states int16 [n, 256] | None,
+        sse float32 [n] | None)."""
+        n = x.shape[0]
+        _need(x, torch.float32, (n, 256), "x")
+        packed = torch.empty(n, 16 * K, dtype=torch.int16, device=x.device)
+        states = torch.empty(n, 256, dtype=torch.int16, device=x.device) if want_states else None
+        sse = torch.empty(n, dtype=torch.float32, device=x.device) if want_sse else None
+        self._sync_stream()
+        self._check(self.lib.exl3_encode_tiles(self.handle, _ptr(x), n, K, float(scale),
+                                               _ptr(packed), _ptr(states), _ptr(sse)))
+        return packed, states, sse
+
+    def decode_tiles(self, packed: torch.Tensor, K: int, scale: float) -> torch.Tensor:
+        n = packed.shape[0]
+        _need(packed, torch.int16, (n, 16 * K), "packed")
+        out = torch.empty(n, 256, dtype=torch.float32, device=packed.device)
+        self._sync_stream()
+        self._check(self.lib.exl3_decode_tiles(self.handle, _ptr(packed), n, K, float(scale),
+                                               _ptr(out)))
+        return out
+
+    def quantize_matrix(self, w: torch.Tensor, K: int, su: torch.Tensor, sv: torch.Tensor,
+                        had_block: int = 128,
+                        gss: Optional[Tuple[int, float, float]] = (12, 0.5, 2.0),
+                        scale: float = 1.0, want_w_hat: bool = False,
+                        want_tile_sse: bool = False):
+        """Returns dict(packed int16 [R/16, C/16, 16K], scale, mse, w_hat?, tile_sse?)."""
+        rows, cols = w.shape
+        dt = {torch.float32: EXL3_F32, torch.bfloat16: EXL3_BF16}.get(w.dtype)
+        if dt is None:
+            raise ValueError("w must be float32 or bfloat16")
+        w = w.contiguous()
+        dev = w.device
+        packed = torch.empty(rows // 16, cols // 16, 16 * K, dtype=torch.int16, device=dev)
+        w_hat = (torch.empty((rows // 16) * (cols // 16), 256, dtype=torch.float32, device=dev)
+                 if want_w_hat else None)
+        tsse = (torch.empty((rows // 16) * (cols // 16), dtype=torch.float32, device=dev)
+                if want_tile_sse else None)
+        g = None if gss is None else ctypes.byref(GSS(int(gss[0]), float(gss[1]), float(gss[2])))
+        s_out = ctypes.c_float(0.0)
+        mse = ctypes.c_double(0.0)
+        self._sync_stream()
+        self._check(self.lib.exl3_quantize_matrix(
+            self.handle, _ptr(w), dt, rows, cols, K, had_block, _ptr(su.contiguous()),
+            _ptr(sv.contiguous()), g, float(scale), _ptr(packed), ctypes.byref(s_out),
+            ctypes.byref(mse), _ptr(w_hat), _ptr(tsse)))
+        return {"packed": packed, "scale": s_out.value, "mse": mse.value, "w_hat": w_hat,
+                "tile_sse": tsse}
+
+
+def scratch_per_tile(K: int) -> int:
+    return int(load_library().exl3_scratch_per_tile(K))
+
+
+def version() -> str:
+    return load_library().exl3_version().decode()

@@ -1,0 +1,460 @@
+// C ABI of the gfx950 EXL3 trellis tile encoder: context, validation,
+// batching of the kernel chain within the scratch bound, and the host-side
+// golden-section scale search.
+//
+// Sources: "EXL3 Intel Arc Quantizer" README, Core Implemented Architecture
+// section 1 (the pass-1 / traceback / pass-2 / traceback chain per tile),
+// section 2 (scratch bounded up front, admission before any work, batches
+// that leave results unchanged), section 8 (rms and the wrapped-diagonal tile
+// sample with the highest- and lowest-energy tiles for the scale search);
+// "JEV-9B EXL3 K=2 (mul1) Checkpoint" model card, section 2 (golden-section
+// scale search).  Host control runs in binary64 with a fixed summation order
+// (ascending tile index), so the chosen scale does not depend on batching.
+#include "exl3.h"
+#include "exl3_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <set>
+#include <string>
+#include <vector>
+
+struct exl3_ctx {
+    int device = 0;
+    hipStream_t stream = nullptr;
+    size_t scratch_limit = 0;
+    uint16_t *d_levels = nullptr;
+    void *d_bp = nullptr;
+    size_t bp_cap = 0;
+    uint16_t *d_end = nullptr;
+    uint16_t *d_X = nullptr;
+    float *d_cost = nullptr;
+    size_t small_cap = 0;
+    int32_t *d_idx = nullptr;
+    size_t idx_cap = 0;
+    float *d_wreg = nullptr;
+    size_t wreg_cap = 0;
+    float *d_sumsq = nullptr;
+    size_t sumsq_cap = 0;
+    float *d_sse = nullptr;
+    size_t sse_cap = 0;
+    int *d_flag = nullptr;
+    std::string err;
+};
+
+namespace {
+
+constexpr size_t kDefaultScratch = (size_t)8 << 30;
+
+int fail(exl3_ctx *ctx, int code, const char *fmt, ...) {
+    if (ctx) {
+        char buf[512];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof buf, fmt, ap);
+        va_end(ap);
+        ctx->err = buf;
+    }
+    return code;
+}
+
+#define EXL3_HIP(ctx, call)                                                              \
+    do {                                                                                 \
+        hipError_t e_ = (call);                                                          \
+        if (e_ != hipSuccess)                                                            \
+            return fail((ctx), EXL3_EHIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+// Grow-only device buffer.  Waits for the stream before releasing the old one.
+template <typename T>
+int ensure(exl3_ctx *ctx, T *&ptr, size_t &cap, size_t count) {
+    if (count <= cap && ptr) return EXL3_OK;
+    if (ptr) {
+        EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+        EXL3_HIP(ctx, hipFree(ptr));
+        ptr = nullptr;
+        cap = 0;
+    }
+    void *p = nullptr;
+    hipError_t e = hipMalloc(&p, std::max<size_t>(count, 1) * sizeof(T));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, EXL3_ENOMEM, "device allocation of %zu bytes failed: %s",
+                    count * sizeof(T), hipGetErrorString(e));
+    }
+    ptr = static_cast<T *>(p);
+    cap = count;
+    return EXL3_OK;
+}
+
+int set_device(exl3_ctx *ctx) {
+    EXL3_HIP(ctx, hipSetDevice(ctx->device));
+    return EXL3_OK;
+}
+
+bool k_supported(int K) { return K >= 2 && K <= 4; }
+
+int ensure_small(exl3_ctx *ctx, size_t n) {
+    if (n <= ctx->small_cap && ctx->d_end && ctx->d_X && ctx->d_cost) return EXL3_OK;
+    if (ctx->d_end || ctx->d_X || ctx->d_cost) {
+        EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+        (void)hipFree(ctx->d_end);
+        (void)hipFree(ctx->d_X);
+        (void)hipFree(ctx->d_cost);
+        ctx->d_end = nullptr;
+        ctx->d_X = nullptr;
+        ctx->d_cost = nullptr;
+        ctx->small_cap = 0;
+    }
+    size_t m = std::max<size_t>(n, 1);
+    if (hipMalloc((void **)&ctx->d_end, m * sizeof(uint16_t)) != hipSuccess ||
+        hipMalloc((void **)&ctx->d_X, m * sizeof(uint16_t)) != hipSuccess ||
+        hipMalloc((void **)&ctx->d_cost, m * sizeof(float)) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, EXL3_ENOMEM, "device allocation of per-tile bookkeeping failed");
+    }
+    ctx->small_cap = m;
+    return EXL3_OK;
+}
+
+// The pass-1 / traceback / pass-2 (/ traceback) chain over n tiles, batched so
+// that the backpointers of one batch fit the scratch bound.  With cost_only,
+// only the pass-2 path costs are produced (scale-search probes).
+int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, int K,
+                 float scale, uint16_t *packed, uint16_t *states, float *sse, float *w_hat,
+                 float *cost_only) {
+    if (n == 0) return EXL3_OK;
+    const size_t per_tile = exl3::bp_bytes_per_tile(K);
+    const size_t max_batch = ctx->scratch_limit / per_tile;
+    if (max_batch == 0)
+        return fail(ctx, EXL3_ENOMEM, "scratch limit %zu B is below one tile's %zu B",
+                    ctx->scratch_limit, per_tile);
+    const int64_t batch = (int64_t)std::min<size_t>((size_t)n, max_batch);
+    int rc;
+    size_t bytes_cap = ctx->bp_cap;
+    char *bp = static_cast<char *>(ctx->d_bp);
+    if ((rc = ensure(ctx, bp, bytes_cap, (size_t)batch * per_tile)) != EXL3_OK) return rc;
+    ctx->d_bp = bp;
+    ctx->bp_cap = bytes_cap;
+    if ((rc = ensure_small(ctx, (size_t)batch)) != EXL3_OK) return rc;
+    for (int64_t i0 = 0; i0 < n; i0 += batch) {
+        const int64_t nb = std::min<int64_t>(batch, n - i0);
+        const int32_t *idx_b = idx ? idx + i0 : nullptr;
+        EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 1, x, idx_b, i0, nb, ctx->d_levels, scale,
+                                               nullptr, ctx->d_bp, ctx->d_end, nullptr,
+                                               ctx->stream));
+        EXL3_HIP(ctx, exl3::launch_traceback(K, 1, ctx->d_bp, nb, ctx->d_end, ctx->d_X, nullptr,
+                                             nullptr, 0, nullptr, 0.0f, nullptr, nullptr,
+                                             nullptr, nullptr, ctx->stream));
+        EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 2, x, idx_b, i0, nb, ctx->d_levels, scale,
+                                               ctx->d_X, ctx->d_bp, nullptr,
+                                               cost_only ? cost_only + i0 : ctx->d_cost,
+                                               ctx->stream));
+        if (!cost_only)
+            EXL3_HIP(ctx, exl3::launch_traceback(K, 2, ctx->d_bp, nb, ctx->d_X, nullptr, x,
+                                                 idx_b, i0, ctx->d_levels, scale, packed,
+                                                 states, sse, w_hat, ctx->stream));
+    }
+    return EXL3_OK;
+}
+
+// Sign vectors must hold exactly +1 or -1 (copied to the host to check).
+int check_signs(exl3_ctx *ctx, const float *d, int n, const char *name) {
+    std::vector<float> h((size_t)n);
+    EXL3_HIP(ctx, hipMemcpyAsync(h.data(), d, (size_t)n * sizeof(float), hipMemcpyDeviceToHost,
+                                 ctx->stream));
+    EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    for (int i = 0; i < n; ++i)
+        if (h[i] != 1.0f && h[i] != -1.0f)
+            return fail(ctx, EXL3_EINVAL, "%s[%d] = %g is not +1 or -1", name, i, (double)h[i]);
+    return EXL3_OK;
+}
+
+int check_matrix_args(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
+                      int had_block, const float *su, const float *sv) {
+    if (!w || !su || !sv) return fail(ctx, EXL3_EINVAL, "null weight or sign pointer");
+    if (w_dtype != EXL3_F32 && w_dtype != EXL3_BF16)
+        return fail(ctx, EXL3_EINVAL, "weight dtype %d is not EXL3_F32 or EXL3_BF16", w_dtype);
+    if (had_block != 64 && had_block != 128)
+        return fail(ctx, EXL3_EUNSUPPORTED, "Hadamard block %d (supported: 64, 128)", had_block);
+    if (rows <= 0 || cols <= 0 || rows % had_block || cols % had_block)
+        return fail(ctx, EXL3_EINVAL, "shape %d x %d is not a positive multiple of %d", rows,
+                    cols, had_block);
+    return EXL3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *exl3_version(void) { return "exl3-gfx950 0.1"; }
+
+size_t exl3_scratch_per_tile(int K) {
+    return k_supported(K) ? exl3::bp_bytes_per_tile(K) : 0;
+}
+
+int exl3_ctx_create(exl3_ctx **out, int device, void *hip_stream, size_t scratch_bytes) {
+    if (!out) return EXL3_EINVAL;
+    *out = nullptr;
+    exl3_ctx *ctx = new (std::nothrow) exl3_ctx();
+    if (!ctx) return EXL3_ENOMEM;
+    ctx->device = device;
+    ctx->stream = static_cast<hipStream_t>(hip_stream);
+    ctx->scratch_limit = scratch_bytes ? scratch_bytes : kDefaultScratch;
+    if (hipSetDevice(device) != hipSuccess) {
+        (void)hipGetLastError();
+        delete ctx;
+        return EXL3_EHIP;
+    }
+    std::vector<uint16_t> lv(65536);
+    exl3::build_mul1_levels(lv.data());
+    if (hipMalloc((void **)&ctx->d_levels, 65536 * sizeof(uint16_t)) != hipSuccess ||
+        hipMalloc((void **)&ctx->d_flag, sizeof(int)) != hipSuccess ||
+        hipMemcpy(ctx->d_levels, lv.data(), 65536 * sizeof(uint16_t), hipMemcpyHostToDevice) !=
+            hipSuccess) {
+        (void)hipGetLastError();
+        exl3_ctx_destroy(ctx);
+        return EXL3_EHIP;
+    }
+    *out = ctx;
+    return EXL3_OK;
+}
+
+void exl3_ctx_destroy(exl3_ctx *ctx) {
+    if (!ctx) return;
+    (void)hipSetDevice(ctx->device);
+    (void)hipStreamSynchronize(ctx->stream);
+    void *bufs[] = {ctx->d_levels, ctx->d_bp, ctx->d_end, ctx->d_X,   ctx->d_cost,
+                    ctx->d_idx,    ctx->d_wreg, ctx->d_sumsq, ctx->d_sse, ctx->d_flag};
+    for (void *p : bufs)
+        if (p) (void)hipFree(p);
+    delete ctx;
+}
+
+const char *exl3_last_error(const exl3_ctx *ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+int exl3_ctx_set_stream(exl3_ctx *ctx, void *hip_stream) {
+    if (!ctx) return EXL3_EINVAL;
+    ctx->stream = static_cast<hipStream_t>(hip_stream);
+    return EXL3_OK;
+}
+
+int exl3_set_codebook(exl3_ctx *ctx, const uint16_t *levels_fp16_host) {
+    if (!ctx) return EXL3_EINVAL;
+    int rc;
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    std::vector<uint16_t> lv(65536);
+    if (levels_fp16_host) {
+        for (int i = 0; i < 65536; ++i) {
+            if ((levels_fp16_host[i] & 0x7C00u) == 0x7C00u)
+                return fail(ctx, EXL3_EINVAL, "level %d is NaN or Inf", i);
+            lv[(size_t)i] = levels_fp16_host[i];
+        }
+    } else {
+        exl3::build_mul1_levels(lv.data());
+    }
+    EXL3_HIP(ctx, hipMemcpyAsync(ctx->d_levels, lv.data(), 65536 * sizeof(uint16_t),
+                                 hipMemcpyHostToDevice, ctx->stream));
+    EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    return EXL3_OK;
+}
+
+int exl3_get_codebook(exl3_ctx *ctx, uint16_t *levels_fp16_host) {
+    if (!ctx || !levels_fp16_host) return fail(ctx, EXL3_EINVAL, "null argument");
+    int rc;
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    EXL3_HIP(ctx, hipMemcpyAsync(levels_fp16_host, ctx->d_levels, 65536 * sizeof(uint16_t),
+                                 hipMemcpyDeviceToHost, ctx->stream));
+    EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    return EXL3_OK;
+}
+
+int exl3_regularize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
+                    int had_block, const float *su, const float *sv, float *w_reg,
+                    int out_layout, float *tile_sumsq, int *nonfinite) {
+    if (!ctx) return EXL3_EINVAL;
+    int rc;
+    if ((rc = check_matrix_args(ctx, w, w_dtype, rows, cols, had_block, su, sv)) != EXL3_OK)
+        return rc;
+    if (!w_reg) return fail(ctx, EXL3_EINVAL, "null output");
+    if (out_layout != EXL3_ROW_MAJOR && out_layout != EXL3_TILE_MAJOR)
+        return fail(ctx, EXL3_EINVAL, "layout %d", out_layout);
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    EXL3_HIP(ctx, exl3::launch_regularize(w, w_dtype, rows, cols, had_block, su, sv, w_reg,
+                                          out_layout, tile_sumsq, nonfinite, ctx->stream));
+    return EXL3_OK;
+}
+
+int exl3_encode_tiles(exl3_ctx *ctx, const float *x, int64_t n, int K, float scale,
+                      uint16_t *packed, uint16_t *states, float *tile_sse) {
+    if (!ctx) return EXL3_EINVAL;
+    if (!k_supported(K)) return fail(ctx, EXL3_EUNSUPPORTED, "K = %d (supported: 2, 3, 4)", K);
+    if (n < 0) return fail(ctx, EXL3_EINVAL, "n = %lld", (long long)n);
+    if (n > 0 && (!x || !packed)) return fail(ctx, EXL3_EINVAL, "null input or output");
+    if (!std::isfinite(scale)) return fail(ctx, EXL3_EINVAL, "scale is not finite");
+    if (n > (int64_t)INT32_MAX) return fail(ctx, EXL3_EINVAL, "too many tiles");
+    int rc;
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    return encode_chain(ctx, x, nullptr, n, K, scale, packed, states, tile_sse, nullptr, nullptr);
+}
+
+int exl3_decode_tiles(exl3_ctx *ctx, const uint16_t *packed, int64_t n, int K, float scale,
+                      float *out) {
+    if (!ctx) return EXL3_EINVAL;
+    if (K < 1 || K > 8) return fail(ctx, EXL3_EUNSUPPORTED, "K = %d (supported: 1..8)", K);
+    if (n < 0) return fail(ctx, EXL3_EINVAL, "n = %lld", (long long)n);
+    if (n > 0 && (!packed || !out)) return fail(ctx, EXL3_EINVAL, "null input or output");
+    if (!std::isfinite(scale)) return fail(ctx, EXL3_EINVAL, "scale is not finite");
+    if (n > (int64_t)INT32_MAX) return fail(ctx, EXL3_EINVAL, "too many tiles");
+    int rc;
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    EXL3_HIP(ctx, exl3::launch_decode(packed, n, K, scale, ctx->d_levels, out, ctx->stream));
+    return EXL3_OK;
+}
+
+int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols, int K,
+                         int had_block, const float *su, const float *sv, const exl3_gss *gss,
+                         float fixed_scale, uint16_t *packed, float *scale_out, double *mse_out,
+                         float *w_hat, float *tile_sse) {
+    if (!ctx) return EXL3_EINVAL;
+    int rc;
+    if ((rc = check_matrix_args(ctx, w, w_dtype, rows, cols, had_block, su, sv)) != EXL3_OK)
+        return rc;
+    if (!k_supported(K)) return fail(ctx, EXL3_EUNSUPPORTED, "K = %d (supported: 2, 3, 4)", K);
+    if (!packed || !scale_out) return fail(ctx, EXL3_EINVAL, "null output");
+    if (gss) {
+        if (gss->iters < 1 || gss->iters > 64 || !(gss->lo > 0.0) || !(gss->hi > gss->lo) ||
+            !std::isfinite(gss->hi))
+            return fail(ctx, EXL3_EINVAL, "scale search {iters %d, lo %g, hi %g}", gss->iters,
+                        gss->lo, gss->hi);
+    } else if (!std::isfinite(fixed_scale)) {
+        return fail(ctx, EXL3_EINVAL, "fixed scale is not finite");
+    }
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    if ((rc = check_signs(ctx, su, rows, "su")) != EXL3_OK) return rc;
+    if ((rc = check_signs(ctx, sv, cols, "sv")) != EXL3_OK) return rc;
+
+    const int TR = rows / 16, TC = cols / 16;
+    const int64_t ntiles = (int64_t)TR * TC;
+    const size_t nel = (size_t)rows * cols;
+    if ((rc = ensure(ctx, ctx->d_wreg, ctx->wreg_cap, nel)) != EXL3_OK) return rc;
+    if ((rc = ensure(ctx, ctx->d_sumsq, ctx->sumsq_cap, (size_t)ntiles)) != EXL3_OK) return rc;
+
+    // 1. regularize (tile-major) with per-tile energy and the non-finite flag
+    EXL3_HIP(ctx, hipMemsetAsync(ctx->d_flag, 0, sizeof(int), ctx->stream));
+    EXL3_HIP(ctx, exl3::launch_regularize(w, w_dtype, rows, cols, had_block, su, sv, ctx->d_wreg,
+                                          EXL3_TILE_MAJOR, ctx->d_sumsq, ctx->d_flag,
+                                          ctx->stream));
+    std::vector<float> sumsq((size_t)ntiles);
+    int flag = 0;
+    EXL3_HIP(ctx, hipMemcpyAsync(sumsq.data(), ctx->d_sumsq, (size_t)ntiles * sizeof(float),
+                                 hipMemcpyDeviceToHost, ctx->stream));
+    EXL3_HIP(ctx, hipMemcpyAsync(&flag, ctx->d_flag, sizeof(int), hipMemcpyDeviceToHost,
+                                 ctx->stream));
+    EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    if (flag) return fail(ctx, EXL3_ENONFINITE, "weight matrix holds NaN or Inf");
+
+    // 2. rms in binary64, ascending tile order
+    double total = 0.0;
+    for (int64_t i = 0; i < ntiles; ++i) total += (double)sumsq[(size_t)i];
+    const double rms = std::sqrt(total / (double)nel);
+
+    // 3. scale
+    float scale = fixed_scale;
+    if (gss) {
+        if (rms == 0.0) {
+            scale = 0.0f;
+        } else {
+            // sample: wrapped diagonal + highest / lowest energy (lowest index on ties)
+            std::set<int64_t> pick;
+            for (int i = 0; i < std::max(TR, TC); ++i)
+                pick.insert((int64_t)(i % TR) * TC + (i % TC));
+            int64_t imax = 0, imin = 0;
+            for (int64_t i = 1; i < ntiles; ++i) {
+                if (sumsq[(size_t)i] > sumsq[(size_t)imax]) imax = i;
+                if (sumsq[(size_t)i] < sumsq[(size_t)imin]) imin = i;
+            }
+            pick.insert(imax);
+            pick.insert(imin);
+            std::vector<int32_t> sample(pick.begin(), pick.end());
+            const int64_t ns = (int64_t)sample.size();
+            if ((rc = ensure(ctx, ctx->d_idx, ctx->idx_cap, (size_t)ns)) != EXL3_OK) return rc;
+            if ((rc = ensure(ctx, ctx->d_sse, ctx->sse_cap,
+                             std::max<size_t>((size_t)ns, (size_t)ntiles))) != EXL3_OK)
+                return rc;
+            EXL3_HIP(ctx, hipMemcpyAsync(ctx->d_idx, sample.data(), (size_t)ns * sizeof(int32_t),
+                                         hipMemcpyHostToDevice, ctx->stream));
+            std::vector<float> costs((size_t)ns);
+            int err = EXL3_OK;
+            auto objective = [&](double s) -> double {
+                if (err != EXL3_OK) return 0.0;
+                int r = encode_chain(ctx, ctx->d_wreg, ctx->d_idx, ns, K, (float)s, nullptr,
+                                     nullptr, nullptr, nullptr, ctx->d_sse);
+                if (r == EXL3_OK) {
+                    hipError_t e = hipMemcpyAsync(costs.data(), ctx->d_sse,
+                                                  (size_t)ns * sizeof(float),
+                                                  hipMemcpyDeviceToHost, ctx->stream);
+                    if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+                    if (e != hipSuccess)
+                        r = fail(ctx, EXL3_EHIP, "scale-search readback: %s",
+                                 hipGetErrorString(e));
+                }
+                if (r != EXL3_OK) {
+                    err = r;
+                    return 0.0;
+                }
+                double f = 0.0;
+                for (int64_t i = 0; i < ns; ++i) f += (double)costs[(size_t)i];
+                return f;
+            };
+            const double g = (std::sqrt(5.0) - 1.0) / 2.0;
+            double a = gss->lo * rms, b = gss->hi * rms;
+            double p = b - (b - a) * g, q = a + (b - a) * g;
+            double fp = objective(p), fq = objective(q);
+            for (int it = 0; it < gss->iters && err == EXL3_OK; ++it) {
+                if (fp < fq) {
+                    b = q;
+                    q = p;
+                    fq = fp;
+                    p = b - (b - a) * g;
+                    fp = objective(p);
+                } else {
+                    a = p;
+                    p = q;
+                    fp = fq;
+                    q = a + (b - a) * g;
+                    fq = objective(q);
+                }
+            }
+            if (err != EXL3_OK) return err;
+            scale = (float)((a + b) / 2.0);
+        }
+    }
+
+    // 4. final encode of every tile at the chosen scale
+    float *sse_dev = tile_sse;
+    if (!sse_dev) {
+        if ((rc = ensure(ctx, ctx->d_sse, ctx->sse_cap, (size_t)ntiles)) != EXL3_OK) return rc;
+        sse_dev = ctx->d_sse;
+    }
+    if ((rc = encode_chain(ctx, ctx->d_wreg, nullptr, ntiles, K, scale, packed, nullptr, sse_dev,
+                           w_hat, nullptr)) != EXL3_OK)
+        return rc;
+    if (mse_out) {
+        std::vector<float> sse((size_t)ntiles);
+        EXL3_HIP(ctx, hipMemcpyAsync(sse.data(), sse_dev, (size_t)ntiles * sizeof(float),
+                                     hipMemcpyDeviceToHost, ctx->stream));
+        EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+        double tot = 0.0;
+        for (int64_t i = 0; i < ntiles; ++i) tot += (double)sse[(size_t)i];
+        *mse_out = tot / (double)nel;
+    }
+    EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    *scale_out = scale;
+    return EXL3_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Host generator of the mul1 level table used by the gfx950 encoder.
+//
+// Source: "EXL3 Intel Arc Quantizer" README, Core Implemented Architecture
+// section 5 names the mul1 procedural codebook (a level for each 16-bit state;
+// the distinct values are fp16 numbers spread over roughly [-3.45, 3.35]) but
+// does not define it.  This library's definition (a documented reading, not a
+// reproduction of upstream's table):
+//   h(s)    = (A * s) mod 2^32 with A = 0x9E3779B1 (odd; golden-ratio hash),
+//   beta(s) = sum of the four bytes of h(s),
+//   level   = fp16 round-to-nearest-even of (beta - mean) / std,
+// where mean and std are over all 2^16 states.  The quotient is formed as
+// (2^16 * beta - S1) / sqrt(2^16 * S2 - S1^2) with exact integer sums
+// S1 = sum beta, S2 = sum beta^2, so only two correctly rounded binary64
+// operations are involved and the table is the same on every IEEE machine.
+#include "exl3_internal.h"
+
+#include <cmath>
+#include <cstdint>
+
+namespace exl3 {
+
+namespace {
+
+constexpr uint32_t kMul1A = 0x9E3779B1u;
+
+// binary64 -> fp16 bits, round to nearest, ties to even (finite inputs).
+uint16_t f64_to_f16_bits(double z) {
+    uint16_t sign = std::signbit(z) ? 0x8000u : 0u;
+    double a = std::fabs(z);
+    if (a == 0.0) return sign;
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);   // rounds to infinity
+    int e = 0;
+    std::frexp(a, &e);                 // a in [2^(e-1), 2^e)
+    int ulp_exp = e - 11;              // 11 significant bits in the normal range
+    if (ulp_exp < -24) ulp_exp = -24;  // subnormal spacing
+    double q = std::ldexp(a, -ulp_exp);          // exact
+    double r = std::nearbyint(q);                // ties to even (default mode)
+    long mant = (long)r;
+    if (mant >= 2048) {                          // carried into the next binade
+        mant >>= 1;
+        ulp_exp += 1;
+    }
+    if (mant < 1024) return (uint16_t)(sign | (uint16_t)mant);   // subnormal
+    int efield = ulp_exp + 25;
+    return (uint16_t)(sign | (uint16_t)(efield << 10) | (uint16_t)(mant - 1024));
+}
+
+}  // namespace
+
+void build_mul1_levels(uint16_t *out) {
+    static int beta[65536];
+    int64_t s1 = 0, s2 = 0;
+    for (uint32_t s = 0; s < 65536u; ++s) {
+        uint32_t h = kMul1A * s;       // mod 2^32
+        int bsum = (int)(h & 0xFFu) + (int)((h >> 8) & 0xFFu) + (int)((h >> 16) & 0xFFu) +
+                   (int)(h >> 24);
+        beta[s] = bsum;
+        s1 += bsum;
+        s2 += (int64_t)bsum * bsum;
+    }
+    const int64_t n = 65536;
+    const double denom = std::sqrt((double)(n * s2 - s1 * s1));
+    for (uint32_t s = 0; s < 65536u; ++s) {
+        double z = (double)(n * beta[s] - s1) / denom;
+        out[s] = f64_to_f16_bits(z);
+    }
+}
+
+}  // namespace exl3

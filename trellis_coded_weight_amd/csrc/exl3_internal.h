@@ -1,0 +1,97 @@
+// Internal declarations of the gfx950 EXL3 encoder library (not part of the ABI).
+//
+// Trellis algebra ("EXL3 Intel Arc Quantizer" README, Core Implemented
+// Architecture section 4): a 16-bit state shifts K new bits in at the bottom,
+// S_t = ((S_{t-1} << K) | b_t) & 0xFFFF.  Kr = 16 - K.  The search keeps one
+// running minimum per value e of the low Kr bits (2^Kr "tracked" minima); the
+// full states that can precede a state whose top Kr bits are e are
+// (k << Kr) | e, k = 0 .. 2^K - 1.
+//
+// Work split of the forward kernel.  The 2^16 states of a step fall into
+// radix-2^K butterflies: for m in [0, 2^(16-2K)) the states
+//   sigma(k, m, b) = (k << Kr) | (m << K) | b,   k, b in [0, 2^K)
+// read the tracked minima M[(k << (16-2K)) | m] and, after the minimum over k,
+// write the new minima M'[(m << K) | b].  A workgroup of 1024 lanes owns one
+// tile; every lane owns 64 states for the whole pass, so their levels
+// v = rn(scale * c) stay in registers:
+//   K=2: 4096 butterflies of 16 states; lane g owns m = g + 1024*i, i < 4
+//   K=3: 1024 butterflies of 64 states; lane g owns m = g
+//   K=4:  256 butterflies of 256 states; lane g owns m = g >> 2 and the four
+//         values b = 4*(g & 3) + 0..3
+// Backpointers (the winning k of every tracked state, K bits) are packed per
+// lane per step into one word: 32 bits at K=2 and 24 at K=3 (uint32), 16 at
+// K=4 (uint16).  The lane appends its tracked states in the order
+// n = i * BPL + bb, high bit first, so state n's k sits at bit
+// K * (GPL * BPL - 1 - n).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace exl3 {
+
+constexpr int kLanes = 1024;        // lanes per tile workgroup
+constexpr int kSteps = 256;         // trellis steps per tile (16 x 16 weights)
+constexpr int kSlots = kSteps - 1;  // steps that produce backpointers
+
+template <int K>
+struct Geo {
+    static constexpr int Kr = 16 - K;
+    static constexpr int T = 1 << Kr;             // tracked minima
+    static constexpr int NB = 1 << K;             // branches per tracked state
+    static constexpr int MBITS = 16 - 2 * K;      // butterfly index bits
+    static constexpr int GPL = (K == 2) ? 4 : 1;  // butterflies per lane
+    static constexpr int BPL = (K == 4) ? 4 : NB; // b values per lane per butterfly
+    static constexpr int SPL = GPL * NB * BPL;    // states per lane (64)
+    using bp_t = typename std::conditional<(K == 4), uint16_t, uint32_t>::type;
+    static_assert(SPL == 64, "every lane owns 64 states");
+};
+
+// Lane and bit of tracked state e's backpointer inside a step's row of words.
+template <int K>
+__host__ __device__ inline void bp_locate(uint32_t e, uint32_t &lane, uint32_t &bit) {
+    if (K == 2) {
+        uint32_t m = e >> 2, bb = e & 3u;
+        lane = m & 1023u;
+        bit = 2u * (15u - (4u * (m >> 10) + bb));
+    } else if (K == 3) {
+        lane = e >> 3;
+        bit = 3u * (7u - (e & 7u));
+    } else {
+        uint32_t m = e >> 4, b = e & 15u;
+        lane = (m << 2) | (b >> 2);
+        bit = 4u * (3u - (b & 3u));
+    }
+}
+
+// Bytes of backpointer scratch per tile in flight.
+inline size_t bp_bytes_per_tile(int K) {
+    return (size_t)kSlots * kLanes * (K == 4 ? 2 : 4);
+}
+
+// ---- kernel launchers (defined in the .hip files) ----
+hipError_t launch_viterbi_fwd(int K, int pass, const float *x, const int32_t *tile_idx,
+                              int64_t tile0, int64_t n, const uint16_t *levels, float scale,
+                              const uint16_t *X_in, void *bp, uint16_t *end_state,
+                              float *cost_out, hipStream_t stream);
+
+hipError_t launch_traceback(int K, int pass, const void *bp, int64_t n,
+                            const uint16_t *start_state, uint16_t *X_out, const float *x,
+                            const int32_t *tile_idx, int64_t tile0, const uint16_t *levels,
+                            float scale, uint16_t *packed, uint16_t *states, float *sse,
+                            float *w_hat, hipStream_t stream);
+
+hipError_t launch_regularize(const void *w, int w_dtype, int rows, int cols, int had_block,
+                             const float *su, const float *sv, float *out, int layout,
+                             float *tile_sumsq, int *nonfinite, hipStream_t stream);
+
+hipError_t launch_decode(const uint16_t *packed, int64_t n, int K, float scale,
+                         const uint16_t *levels, float *out, hipStream_t stream);
+
+hipError_t launch_gather_tiles(const float *src, const int32_t *idx, int64_t n, float *dst,
+                               hipStream_t stream);
+
+// Host-side generator of the mul1 level table (fp16 bit patterns).
+void build_mul1_levels(uint16_t *out65536);
+
+}  // namespace exl3

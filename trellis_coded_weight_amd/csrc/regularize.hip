@@ -1,0 +1,140 @@
+// Sign flips + blockwise Sylvester Hadamard regularization on gfx950.
+//
+// Source: "EXL3 Intel Arc Quantizer" README, Core Implemented Architecture
+// section 7 (natural-order Sylvester Hadamard normalised by 1/sqrt(B), applied
+// per block of B rows on the left and per block of B columns on the right, not
+// as one Kronecker transform; decode applies H_l, x su, H_r, x sv) and
+// section 8 (per-tile energy for the scale search).
+//
+//   W_reg = H_l diag(su) W diag(sv) H_r
+// evaluated as: sign flips (exact), left fast Walsh-Hadamard transform with
+// levels h = 1, 2, ..., B/2 (pairs (p, p+h), p mod 2h < h, become (a+b, a-b)),
+// x rn(1/sqrt(B)), the same transform along rows, x rn(1/sqrt(B)).
+//
+// One workgroup of B lanes per B x B block (the blocks are independent).  Lane
+// j first holds column j of the block in registers for the left transform,
+// the block is turned around in LDS, then lane j holds row j for the right
+// transform.  The output is written tile-major (or row-major) and each of the
+// block's (B/16)^2 tiles gets its sequential binary32 sum of squares.
+#include "exl3_internal.h"
+
+#include <math.h>
+
+namespace exl3 {
+namespace {
+
+__device__ __forceinline__ float load_w(const float *w, size_t i) { return w[i]; }
+__device__ __forceinline__ float load_w(const uint16_t *w, size_t i) {
+    return __uint_as_float((uint32_t)w[i] << 16);   // bf16 -> fp32 is exact
+}
+
+template <int B>
+__device__ __forceinline__ void fwht_regs(float (&a)[B]) {
+#pragma unroll
+    for (int h = 1; h < B; h <<= 1)
+#pragma unroll
+        for (int p = 0; p < B; ++p)
+            if ((p & h) == 0) {
+                float u = a[p], w = a[p + h];
+                a[p] = u + w;
+                a[p + h] = u - w;
+            }
+}
+
+template <int B>
+__device__ __forceinline__ float norm_const() {
+    return B == 64 ? 0.125f : __uint_as_float(0x3DB504F3u);   // rn(1/sqrt(128))
+}
+
+template <int B, typename Tin>
+__global__ void __launch_bounds__(B)
+regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__restrict__ su,
+                  const float *__restrict__ sv, float *__restrict__ out, int layout,
+                  float *__restrict__ tile_sumsq, int *__restrict__ nonfinite) {
+    __shared__ float blk[B][B + 1];
+    const int j = threadIdx.x;
+    const int br = blockIdx.y, bc = blockIdx.x;
+    const int r0 = br * B, c0 = bc * B;
+    const float c = norm_const<B>();
+
+    float a[B];
+    bool bad = false;
+    const float svj = sv[c0 + j];
+#pragma unroll
+    for (int r = 0; r < B; ++r) {
+        float val = load_w(w, (size_t)(r0 + r) * cols + c0 + j);
+        bad |= !isfinite(val);
+        a[r] = (val * su[r0 + r]) * svj;
+    }
+    if (bad && nonfinite) *nonfinite = 1;
+
+    fwht_regs<B>(a);
+#pragma unroll
+    for (int r = 0; r < B; ++r) blk[r][j] = a[r] * c;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < B; ++q) a[q] = blk[j][q];
+    fwht_regs<B>(a);
+#pragma unroll
+    for (int q = 0; q < B; ++q) blk[j][q] = a[q] * c;
+    __syncthreads();
+
+    const int TC = cols / 16;
+    constexpr int TB = B / 16;        // tiles per block side
+    if (layout == 1) {
+        for (int idx = j; idx < B * B; idx += B) {
+            int lt = idx >> 8, t = idx & 255;
+            int tr = lt / TB, tc = lt % TB;
+            int rr = tr * 16 + (t >> 4), cc = tc * 16 + (t & 15);
+            size_t tau = (size_t)(r0 / 16 + tr) * TC + (c0 / 16 + tc);
+            out[tau * 256 + t] = blk[rr][cc];
+        }
+    } else {
+        for (int idx = j; idx < B * B; idx += B) {
+            int rr = idx / B, cc = idx % B;
+            out[(size_t)(r0 + rr) * cols + c0 + cc] = blk[rr][cc];
+        }
+    }
+    if (tile_sumsq && j < TB * TB) {
+        int tr = j / TB, tc = j % TB;
+        float acc = 0.0f;
+        for (int t = 0; t < 256; ++t) {
+            float val = blk[tr * 16 + (t >> 4)][tc * 16 + (t & 15)];
+            float sq = val * val;
+            acc = acc + sq;
+        }
+        tile_sumsq[(size_t)(r0 / 16 + tr) * TC + (c0 / 16 + tc)] = acc;
+    }
+}
+
+template <int B, typename Tin>
+hipError_t launch_reg_t(const void *w, int rows, int cols, const float *su, const float *sv,
+                        float *out, int layout, float *tile_sumsq, int *nonfinite,
+                        hipStream_t stream) {
+    dim3 grid(cols / B, rows / B);
+    hipLaunchKernelGGL((regularize_kernel<B, Tin>), grid, dim3(B), 0, stream,
+                       reinterpret_cast<const Tin *>(w), rows, cols, su, sv, out, layout,
+                       tile_sumsq, nonfinite);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_regularize(const void *w, int w_dtype, int rows, int cols, int had_block,
+                             const float *su, const float *sv, float *out, int layout,
+                             float *tile_sumsq, int *nonfinite, hipStream_t stream) {
+    if (rows <= 0 || cols <= 0) return hipSuccess;
+    if (had_block == 64)
+        return w_dtype == 1 ? launch_reg_t<64, uint16_t>(w, rows, cols, su, sv, out, layout,
+                                                         tile_sumsq, nonfinite, stream)
+                            : launch_reg_t<64, float>(w, rows, cols, su, sv, out, layout,
+                                                      tile_sumsq, nonfinite, stream);
+    if (had_block == 128)
+        return w_dtype == 1 ? launch_reg_t<128, uint16_t>(w, rows, cols, su, sv, out, layout,
+                                                          tile_sumsq, nonfinite, stream)
+                            : launch_reg_t<128, float>(w, rows, cols, su, sv, out, layout,
+                                                       tile_sumsq, nonfinite, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace exl3

@@ -1,0 +1,193 @@
+// Traceback, packing and dequantisation of the EXL3 tile encoder on gfx950.
+//
+// Source: "EXL3 Intel Arc Quantizer" README, Core Implemented Architecture
+// section 1 (device-resident circular traceback of the two-pass closure) and
+// section 5 (container: the low K bits of each state, MSB-first, 16-bit words,
+// then a swap of the two halves of every 32-bit pair; decode by reading the
+// 16-bit window that ends at each state's last bit).
+//
+// Traceback is a chain of dependent reads, one per step, so one lane walks one
+// tile; many tiles in flight hide the latency.  The walk uses the predecessor
+// rule S_{t-1} = (bp[t-1][S_t >> K] << Kr) | (S_t >> K).
+#include "exl3_internal.h"
+
+namespace exl3 {
+namespace {
+
+constexpr int kTbThreads = 64;   // tiles per traceback workgroup (one wave)
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+template <int K>
+__device__ __forceinline__ uint32_t bp_read(const typename Geo<K>::bp_t *__restrict__ bp_tile,
+                                            int slot, uint32_t e) {
+    uint32_t lane, bit;
+    bp_locate<K>(e, lane, bit);
+    uint32_t w = bp_tile[(size_t)slot * kLanes + lane];
+    return (w >> bit) & ((1u << K) - 1u);
+}
+
+// Pass 1: from the best final state of the rotated pass back to rotated step
+// 127 (original position 255); that state is X.
+template <int K>
+__global__ void __launch_bounds__(kTbThreads)
+traceback1_kernel(const typename Geo<K>::bp_t *__restrict__ bp, int64_t n,
+                  const uint16_t *__restrict__ end_state, uint16_t *__restrict__ X_out) {
+    using G = Geo<K>;
+    const int64_t b = (int64_t)blockIdx.x * kTbThreads + threadIdx.x;
+    if (b >= n) return;
+    const typename G::bp_t *bp_tile = bp + (size_t)b * kSlots * kLanes;
+    uint32_t s = end_state[b];
+    for (int j = kSteps - 1; j >= kSteps / 2; --j) {
+        uint32_t e = s >> K;
+        uint32_t k = bp_read<K>(bp_tile, (j - 1) - 127, e);
+        s = (k << G::Kr) | e;
+    }
+    X_out[b] = (uint16_t)s;
+}
+
+// Pass 2: from X at step 255 back to step 0, then pack, dequantise and sum the
+// squared error of the tile in step order.
+template <int K>
+__global__ void __launch_bounds__(kTbThreads)
+traceback2_kernel(const typename Geo<K>::bp_t *__restrict__ bp, int64_t n,
+                  const uint16_t *__restrict__ X_in, const float *__restrict__ x,
+                  const int32_t *__restrict__ tile_idx, int64_t tile0,
+                  const uint16_t *__restrict__ levels, float scale, uint16_t *__restrict__ packed,
+                  uint16_t *__restrict__ states_out, float *__restrict__ sse_out,
+                  float *__restrict__ w_hat) {
+    using G = Geo<K>;
+    __shared__ uint16_t S[kTbThreads][kSteps];
+    const int lt = threadIdx.x;
+    const int64_t b = (int64_t)blockIdx.x * kTbThreads + lt;
+    if (b >= n) return;
+    const int64_t tile = tile_idx ? (int64_t)tile_idx[b] : tile0 + b;
+    const typename G::bp_t *bp_tile = bp + (size_t)b * kSlots * kLanes;
+
+    uint32_t s = X_in[b];
+    S[lt][kSteps - 1] = (uint16_t)s;
+    for (int t = kSteps - 1; t >= 1; --t) {
+        uint32_t e = s >> K;
+        uint32_t k = bp_read<K>(bp_tile, t - 1, e);
+        s = (k << G::Kr) | e;
+        S[lt][t - 1] = (uint16_t)s;
+    }
+
+    // container: MSB-first stream of the low K bits, 16-bit words, pair swap
+    uint16_t *pk = packed + (size_t)tile * (16 * K);
+    uint32_t acc = 0;
+    int nbits = 0, word = 0;
+    for (int t = 0; t < kSteps; ++t) {
+        acc = (acc << K) | ((uint32_t)S[lt][t] & ((1u << K) - 1u));
+        nbits += K;
+        if (nbits >= 16) {
+            nbits -= 16;
+            pk[word ^ 1] = (uint16_t)(acc >> nbits);
+            acc &= (1u << nbits) - 1u;
+            ++word;
+        }
+    }
+
+    // dequantise and sequential squared error (equals the search's path cost)
+    const float *xt = x + (size_t)tile * kSteps;
+    float sse = 0.0f;
+    for (int t = 0; t < kSteps; ++t) {
+        uint32_t st = S[lt][t];
+        float v = scale * half_bits_to_float(levels[st]);
+        float d = xt[t] - v;
+        float q = d * d;
+        sse = sse + q;
+        if (w_hat) w_hat[(size_t)tile * kSteps + t] = v;
+        if (states_out) states_out[(size_t)tile * kSteps + t] = (uint16_t)st;
+    }
+    if (sse_out) sse_out[tile] = sse;
+}
+
+__global__ void __launch_bounds__(256)
+decode_kernel(const uint16_t *__restrict__ packed, int K, float scale,
+              const uint16_t *__restrict__ levels, float *__restrict__ out) {
+    __shared__ uint16_t words[16 * 8];
+    const int64_t tile = blockIdx.x;
+    const int t = threadIdx.x;
+    const int nw = 16 * K;
+    if (t < nw) words[t] = packed[(size_t)tile * nw + (t ^ 1)];   // undo the pair swap
+    __syncthreads();
+    const int nbits = kSteps * K;
+    uint32_t s = 0;
+    const int end = (t + 1) * K;                  // exclusive end of S_t's window
+    for (int j = end - 16; j < end; ++j) {
+        int jj = j < 0 ? j + nbits : j;
+        uint32_t bit = (words[jj >> 4] >> (15 - (jj & 15))) & 1u;
+        s = (s << 1) | bit;
+    }
+    out[(size_t)tile * kSteps + t] = scale * half_bits_to_float(levels[s]);
+}
+
+__global__ void __launch_bounds__(256)
+gather_tiles_kernel(const float *__restrict__ src, const int32_t *__restrict__ idx,
+                    float *__restrict__ dst) {
+    const int64_t b = blockIdx.x;
+    const int t = threadIdx.x;
+    dst[(size_t)b * kSteps + t] = src[(size_t)idx[b] * kSteps + t];
+}
+
+template <int K>
+hipError_t launch_tb_t(int pass, const void *bp, int64_t n, const uint16_t *start_state,
+                       uint16_t *X_out, const float *x, const int32_t *tile_idx, int64_t tile0,
+                       const uint16_t *levels, float scale, uint16_t *packed, uint16_t *states,
+                       float *sse, float *w_hat, hipStream_t stream) {
+    using bp_t = typename Geo<K>::bp_t;
+    const unsigned blocks = (unsigned)((n + kTbThreads - 1) / kTbThreads);
+    if (pass == 1)
+        hipLaunchKernelGGL(traceback1_kernel<K>, dim3(blocks), dim3(kTbThreads), 0, stream,
+                           reinterpret_cast<const bp_t *>(bp), n, start_state, X_out);
+    else
+        hipLaunchKernelGGL(traceback2_kernel<K>, dim3(blocks), dim3(kTbThreads), 0, stream,
+                           reinterpret_cast<const bp_t *>(bp), n, start_state, x, tile_idx,
+                           tile0, levels, scale, packed, states, sse, w_hat);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_traceback(int K, int pass, const void *bp, int64_t n,
+                            const uint16_t *start_state, uint16_t *X_out, const float *x,
+                            const int32_t *tile_idx, int64_t tile0, const uint16_t *levels,
+                            float scale, uint16_t *packed, uint16_t *states, float *sse,
+                            float *w_hat, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    switch (K) {
+        case 2:
+            return launch_tb_t<2>(pass, bp, n, start_state, X_out, x, tile_idx, tile0, levels,
+                                  scale, packed, states, sse, w_hat, stream);
+        case 3:
+            return launch_tb_t<3>(pass, bp, n, start_state, X_out, x, tile_idx, tile0, levels,
+                                  scale, packed, states, sse, w_hat, stream);
+        case 4:
+            return launch_tb_t<4>(pass, bp, n, start_state, X_out, x, tile_idx, tile0, levels,
+                                  scale, packed, states, sse, w_hat, stream);
+        default:
+            return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode(const uint16_t *packed, int64_t n, int K, float scale,
+                         const uint16_t *levels, float *out, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    if (K < 1 || K > 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(decode_kernel, dim3((unsigned)n), dim3(kSteps), 0, stream, packed, K, scale,
+                       levels, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_tiles(const float *src, const int32_t *idx, int64_t n, float *dst,
+                               hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_tiles_kernel, dim3((unsigned)n), dim3(kSteps), 0, stream, src, idx,
+                       dst);
+    return hipGetLastError();
+}
+
+}  // namespace exl3
