@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Throughput of the EXL3 trellis tile encoder on one MI355X.
+
+One step = the whole hot path on one 4096x4096 bf16 weight matrix (entries
+N(0, 0.02^2), 128-block Hadamard with random signs, K=2, golden-section scale
+search with 12 reductions over [0.5, 2.0] x rms): regularization, per-tile
+energy, 14 probe encodes of the 258-tile sample, and the final encode of all
+65,536 tiles.  The input is resident in HBM before the timed region.
+
+Prints one JSON line.  `value` is matrix tiles encoded per second.
+`roofline` rates the forward (add-compare-select) kernel, which holds almost
+all of the time, against the FP32 vector peak; `cpu_baseline` is the oracle on
+a bounded sample of the same matrix on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_TFLOPS = 157.3      # 256 CU x 2.4 GHz x 256 FP32 flop/clk (packed FMA)
+PEAK_ISSUE_TOPS = 39.3        # 256 CU x 2.4 GHz x 64 unpacked single-op lanes/clk
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "viterbi_fwd_traffic.json")
+FWD_SOURCE = os.path.join(ROOT, "trellis_coded_weight_amd", "csrc", "viterbi_fwd.hip")
+METRIC = "encoded 16x16 tiles/sec at K=2/3/4 on 1 MI355X; % of FP32 VALU peak"
+
+
+def ops_per_pass(K: int, first: bool) -> int:
+    """Algorithmic FP32 operations of one forward pass over one tile:
+    subtract, multiply and add for each of the 2^16 states at each of the 256
+    steps, plus the 2^16 - 2^(16-K) compare-selects that eliminate non-survivors
+    at each of the 255 transitions (+ the 2^16 - 1 comparisons of the final
+    argmin in the first pass)."""
+    n = 1 << 16
+    ops = 256 * 3 * n + 255 * (n - (n >> K))
+    return ops + (n - 1 if first else 0)
+
+
+def ops_per_tile_encode(K: int) -> int:
+    return ops_per_pass(K, True) + ops_per_pass(K, False)
+
+
+def sample_size(TR: int, TC: int) -> int:
+    # wrapped diagonal + two extremes (at most; the extremes may fall on it)
+    return max(TR, TC) + 2
+
+
+def file_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(K: int):
+    """HBM bytes per forward launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256") != file_sha(FWD_SOURCE):
+        return None
+    per = d.get("per_launch", {}).get("K%d" % K)
+    if not per:
+        return None
+    return per
+
+
+def cpu_baseline(m, K, scale, n_tiles, threads, sample_tiles):
+    """Oracle on this host: full regularization and statistics, plus the final
+    encode of `sample_tiles` tiles; extrapolated to the whole step."""
+    import numpy as np
+    import oracle
+    levels = oracle.mul1_levels_fp16()
+    t0 = time.perf_counter()
+    w_reg = oracle.regularize(m.w, m.su, m.sv, m.had_block)
+    tiles = oracle.to_tiles(w_reg)
+    oracle.tile_sumsq(tiles)
+    t_reg = time.perf_counter() - t0
+    idx = np.linspace(0, n_tiles - 1, sample_tiles).astype(np.int64)
+    t1 = time.perf_counter()
+    oracle.encode_tiles(tiles[idx], K, np.float32(scale), levels, threads=threads)
+    t_enc = time.perf_counter() - t1
+    per_tile = t_enc / sample_tiles
+    TR, TC = m.w.shape[0] // 16, m.w.shape[1] // 16
+    encodes = n_tiles + (m.gss[0] + 2) * sample_size(TR, TC)
+    total = t_reg + per_tile * encodes
+    return {
+        "value": n_tiles / total,
+        "unit": "tiles/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": ("full regularization + energy of the %dx%d matrix, then the final encode "
+                   "of %d evenly spaced tiles at the chosen scale; extrapolated to %d "
+                   "tile encodes (all tiles + %d scale-search probes)"
+                   % (m.w.shape[0], m.w.shape[1], sample_tiles, encodes, encodes - n_tiles)),
+        "measured_s": round(t_reg + t_enc, 2),
+        "tile_encodes_per_s": 1.0 / per_tile,
+    }
+
+
+def run_steps(ctx, w, su, sv, K, gss, steps):
+    import torch
+    out = None
+    for _ in range(steps):
+        out = ctx.quantize_matrix(w, K, su, sv, had_block=128, gss=gss)
+    torch.cuda.synchronize()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tiles", type=int, default=2048)
+    ap.add_argument("--no-other-k", action="store_true",
+                    help="skip the K=3 and K=4 runs on the same matrix")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "kernel to scale HBM byte counters against)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the encoder's tiles are independent and "
+              "this build runs on a single MI355X; --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+
+    import numpy as np
+    import torch
+    import trellis_coded_weight_amd as T
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    m = workloads.config(2)[0]
+    K = m.K
+    R, C = m.w.shape
+    n_tiles = (R // 16) * (C // 16)
+    w = torch.from_numpy(m.w).to(torch.bfloat16).to(dev)
+    su = torch.from_numpy(m.su).to(dev)
+    sv = torch.from_numpy(m.sv).to(dev)
+    ctx = T.Context(0)
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    out = run_steps(ctx, w, su, sv, K, m.gss, max(args.warmup, 0))
+    ctx.set_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    out = run_steps(ctx, w, su, sv, K, m.gss, args.steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+
+    kern = {k: ctx.read_timing(k) for k in ("fwd1", "fwd2", "tb1", "tb2", "regularize")}
+    ctx.set_timing(False)
+    value = n_tiles * args.steps / dt
+    ms_step = 1000.0 * dt / args.steps
+    TR, TC = R // 16, C // 16
+    gss_encodes = (m.gss[0] + 2) * sample_size(TR, TC)
+    encodes_per_s = (n_tiles + gss_encodes) * args.steps / dt
+
+    # roofline of the forward kernel (both passes), from its own launch times
+    f1_ms, f1_n, f1_tiles = kern["fwd1"]
+    f2_ms, f2_n, f2_tiles = kern["fwd2"]
+    fwd_ops = f1_tiles * ops_per_pass(K, True) + f2_tiles * ops_per_pass(K, False)
+    fwd_s = (f1_ms + f2_ms) / 1000.0
+    achieved = fwd_ops / fwd_s / 1e12
+    traffic = load_traffic(K)
+    roofline = {
+        "bound": "alu",
+        "achieved": round(achieved, 3),
+        "peak": PEAK_FP32_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+        "traffic": traffic,
+        "kernel": "viterbi_fwd_kernel<K=2> (passes 1 and 2)",
+        "launches": f1_n + f2_n,
+        "avg_launch_ms": round((f1_ms + f2_ms) / max(f1_n + f2_n, 1), 4),
+        "avg_tiles_per_launch": round((f1_tiles + f2_tiles) / max(f1_n + f2_n, 1), 1),
+        "peak_issue": PEAK_ISSUE_TOPS,
+        "frac_issue": round(achieved / PEAK_ISSUE_TOPS, 4),
+        "whole_path_frac": round(encodes_per_s * ops_per_tile_encode(K) / 1e12
+                                 / PEAK_FP32_TFLOPS, 4),
+    }
+    stages = {k: {"ms": round(v[0] / args.steps, 3), "launches": v[1] // max(args.steps, 1)}
+              for k, v in kern.items()}
+
+    by_k = {"2": round(value, 1)}
+    if not args.no_other_k:
+        for k2 in (3, 4):
+            run_steps(ctx, w, su, sv, k2, m.gss, 1)
+            t2 = time.perf_counter()
+            run_steps(ctx, w, su, sv, k2, m.gss, max(1, args.steps // 2))
+            by_k[str(k2)] = round(n_tiles * max(1, args.steps // 2)
+                                  / (time.perf_counter() - t2), 1)
+
+    cpu = None
+    if not args.no_cpu_baseline and rank == 0:
+        threads = max(1, min(os.cpu_count() or 1, 16))
+        cpu = cpu_baseline(m, K, out["scale"], n_tiles, threads, args.cpu_tiles)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tiles/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0, 0.02^2) bf16 matrix; no model weights)",
+        "config": {
+            "workload": "4096x4096 bf16 projection, N(0,0.02^2), 128-block Hadamard + random "
+                        "signs, K=2 trellis encode + 12-iteration golden-section scale search",
+            "rows": R, "cols": C, "K": K, "tiles": n_tiles, "had_block": 128,
+            "gss": list(m.gss), "scale_search_tile_encodes": gss_encodes,
+        },
+        "tile_encodes_per_s": round(encodes_per_s, 1),
+        "tiles_per_s_by_K": by_k,
+        "scale": out["scale"],
+        "mse": out["mse"],
+        "stages_ms_per_step": stages,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if rank == 0:
+        print(json.dumps(line), flush=True)
+    ctx.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -163,6 +163,29 @@ int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, in
                          const exl3_gss *gss, float fixed_scale, uint16_t *packed,
                          float *scale_out, double *mse_out, float *w_hat, float *tile_sse);
 
+/* Kernel kinds for exl3_ctx_read_timing. */
+enum {
+    EXL3_KERNEL_FWD1 = 0,        /* forward pass 1 (rotated input, free start) */
+    EXL3_KERNEL_FWD2 = 1,        /* forward pass 2 (start pinned to X) */
+    EXL3_KERNEL_TB1 = 2,         /* traceback to X */
+    EXL3_KERNEL_TB2 = 3,         /* traceback, packing, squared error */
+    EXL3_KERNEL_REGULARIZE = 4
+};
+
+/*
+ * Per-launch timing for measurement.  With timing on, every launch of the
+ * kinds above is bracketed by two HIP events on the context's stream
+ * (a small overhead per launch).  Turning it on or off clears the records.
+ */
+int exl3_ctx_set_timing(exl3_ctx *ctx, int enable);
+
+/*
+ * Sum of the durations (ms) of the recorded launches of one kind, their count
+ * and the number of tiles they processed.  Synchronizes the stream.
+ */
+int exl3_ctx_read_timing(exl3_ctx *ctx, int kind, double *total_ms, int64_t *launches,
+                         int64_t *tiles);
+
 /*
  * Scratch bytes one tile needs in flight at this K (backpointers of the
  * longer pass plus per-tile bookkeeping).  0 for an unsupported K.

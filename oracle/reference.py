@@ -81,7 +81,8 @@ def _load():
 
 
 def default_threads() -> int:
-    return max(1, os.cpu_count() or 1)
+    # at most 16 worker threads (the host share of one GPU on the target boxes)
+    return max(1, min(os.cpu_count() or 1, 16))
 
 
 # --------------------------------------------------------------------------

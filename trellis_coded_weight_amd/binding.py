@@ -30,7 +30,9 @@ EXPORTED = [
     "exl3_version", "exl3_ctx_create", "exl3_ctx_destroy", "exl3_last_error",
     "exl3_ctx_set_stream", "exl3_set_codebook", "exl3_get_codebook", "exl3_regularize",
     "exl3_encode_tiles", "exl3_decode_tiles", "exl3_quantize_matrix", "exl3_scratch_per_tile",
+    "exl3_ctx_set_timing", "exl3_ctx_read_timing",
 ]
+KERNEL_KINDS = {"fwd1": 0, "fwd2": 1, "tb1": 2, "tb2": 3, "regularize": 4}
 
 
 class Exl3Error(RuntimeError):
@@ -89,6 +91,11 @@ def load_library():
                                          ctypes.POINTER(f64), vp, vp]
     lib.exl3_scratch_per_tile.restype = sz
     lib.exl3_scratch_per_tile.argtypes = [i32]
+    lib.exl3_ctx_set_timing.restype = i32
+    lib.exl3_ctx_set_timing.argtypes = [vp, i32]
+    lib.exl3_ctx_read_timing.restype = i32
+    lib.exl3_ctx_read_timing.argtypes = [vp, i32, ctypes.POINTER(f64), ctypes.POINTER(i64),
+                                         ctypes.POINTER(i64)]
     _lib = lib
     return lib
 
@@ -158,6 +165,20 @@ class Context:
 
     def last_error(self) -> str:
         return self.lib.exl3_last_error(self.handle).decode()
+
+    def set_timing(self, enable: bool):
+        self._sync_stream()
+        self._check(self.lib.exl3_ctx_set_timing(self.handle, 1 if enable else 0))
+
+    def read_timing(self, kind: str):
+        """(total_ms, launches, tiles) of the recorded launches of one kernel kind."""
+        ms = ctypes.c_double()
+        nl = ctypes.c_int64()
+        nt = ctypes.c_int64()
+        self._check(self.lib.exl3_ctx_read_timing(self.handle, KERNEL_KINDS[kind],
+                                                  ctypes.byref(ms), ctypes.byref(nl),
+                                                  ctypes.byref(nt)))
+        return ms.value, nl.value, nt.value
 
     # -- API --
     def set_codebook(self, levels_fp16: Optional[torch.Tensor]):

@@ -24,6 +24,7 @@
 
 struct exl3_ctx {
     int device = 0;
+    int n_cu = 256;
     hipStream_t stream = nullptr;
     size_t scratch_limit = 0;
     uint16_t *d_levels = nullptr;
@@ -43,6 +44,14 @@ struct exl3_ctx {
     size_t sse_cap = 0;
     int *d_flag = nullptr;
     std::string err;
+    // optional per-launch timing (HIP events on the context's stream)
+    struct Timed {
+        int kind;
+        int64_t tiles;
+        hipEvent_t start, stop;
+    };
+    bool timing = false;
+    std::vector<Timed> timed;
 };
 
 namespace {
@@ -97,6 +106,32 @@ int set_device(exl3_ctx *ctx) {
 
 bool k_supported(int K) { return K >= 2 && K <= 4; }
 
+void clear_timing(exl3_ctx *ctx) {
+    for (auto &r : ctx->timed) {
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    ctx->timed.clear();
+}
+
+// Bracket one launch with events when timing is on.  Returns the record index
+// (or -1); close_timed() records the stop event.
+int open_timed(exl3_ctx *ctx, int kind, int64_t tiles) {
+    if (!ctx->timing) return -1;
+    exl3_ctx::Timed r{kind, tiles, nullptr, nullptr};
+    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    (void)hipEventRecord(r.start, ctx->stream);
+    ctx->timed.push_back(r);
+    return (int)ctx->timed.size() - 1;
+}
+
+void close_timed(exl3_ctx *ctx, int id) {
+    if (id >= 0) (void)hipEventRecord(ctx->timed[(size_t)id].stop, ctx->stream);
+}
+
 int ensure_small(exl3_ctx *ctx, size_t n) {
     if (n <= ctx->small_cap && ctx->d_end && ctx->d_X && ctx->d_cost) return EXL3_OK;
     if (ctx->d_end || ctx->d_X || ctx->d_cost) {
@@ -132,7 +167,10 @@ int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, i
     if (max_batch == 0)
         return fail(ctx, EXL3_ENOMEM, "scratch limit %zu B is below one tile's %zu B",
                     ctx->scratch_limit, per_tile);
-    const int64_t batch = (int64_t)std::min<size_t>((size_t)n, max_batch);
+    int64_t batch = (int64_t)std::min<size_t>((size_t)n, max_batch);
+    // when several batches are needed, keep each a whole number of rounds of
+    // one tile per compute unit so no batch ends in a mostly idle round
+    if (batch < n && batch > ctx->n_cu) batch -= batch % ctx->n_cu;
     int rc;
     size_t bytes_cap = ctx->bp_cap;
     char *bp = static_cast<char *>(ctx->d_bp);
@@ -143,20 +181,29 @@ int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, i
     for (int64_t i0 = 0; i0 < n; i0 += batch) {
         const int64_t nb = std::min<int64_t>(batch, n - i0);
         const int32_t *idx_b = idx ? idx + i0 : nullptr;
+        int id = open_timed(ctx, EXL3_KERNEL_FWD1, nb);
         EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 1, x, idx_b, i0, nb, ctx->d_levels, scale,
                                                nullptr, ctx->d_bp, ctx->d_end, nullptr,
                                                ctx->stream));
+        close_timed(ctx, id);
+        id = open_timed(ctx, EXL3_KERNEL_TB1, nb);
         EXL3_HIP(ctx, exl3::launch_traceback(K, 1, ctx->d_bp, nb, ctx->d_end, ctx->d_X, nullptr,
                                              nullptr, 0, nullptr, 0.0f, nullptr, nullptr,
                                              nullptr, nullptr, ctx->stream));
+        close_timed(ctx, id);
+        id = open_timed(ctx, EXL3_KERNEL_FWD2, nb);
         EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 2, x, idx_b, i0, nb, ctx->d_levels, scale,
                                                ctx->d_X, ctx->d_bp, nullptr,
                                                cost_only ? cost_only + i0 : ctx->d_cost,
                                                ctx->stream));
-        if (!cost_only)
+        close_timed(ctx, id);
+        if (!cost_only) {
+            id = open_timed(ctx, EXL3_KERNEL_TB2, nb);
             EXL3_HIP(ctx, exl3::launch_traceback(K, 2, ctx->d_bp, nb, ctx->d_X, nullptr, x,
                                                  idx_b, i0, ctx->d_levels, scale, packed,
                                                  states, sse, w_hat, ctx->stream));
+            close_timed(ctx, id);
+        }
     }
     return EXL3_OK;
 }
@@ -209,6 +256,10 @@ int exl3_ctx_create(exl3_ctx **out, int device, void *hip_stream, size_t scratch
         delete ctx;
         return EXL3_EHIP;
     }
+    int n_cu = 0;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess &&
+        n_cu > 0)
+        ctx->n_cu = n_cu;
     std::vector<uint16_t> lv(65536);
     exl3::build_mul1_levels(lv.data());
     if (hipMalloc((void **)&ctx->d_levels, 65536 * sizeof(uint16_t)) != hipSuccess ||
@@ -227,6 +278,7 @@ void exl3_ctx_destroy(exl3_ctx *ctx) {
     if (!ctx) return;
     (void)hipSetDevice(ctx->device);
     (void)hipStreamSynchronize(ctx->stream);
+    clear_timing(ctx);
     void *bufs[] = {ctx->d_levels, ctx->d_bp, ctx->d_end, ctx->d_X,   ctx->d_cost,
                     ctx->d_idx,    ctx->d_wreg, ctx->d_sumsq, ctx->d_sse, ctx->d_flag};
     for (void *p : bufs)
@@ -239,6 +291,38 @@ const char *exl3_last_error(const exl3_ctx *ctx) { return ctx ? ctx->err.c_str()
 int exl3_ctx_set_stream(exl3_ctx *ctx, void *hip_stream) {
     if (!ctx) return EXL3_EINVAL;
     ctx->stream = static_cast<hipStream_t>(hip_stream);
+    return EXL3_OK;
+}
+
+int exl3_ctx_set_timing(exl3_ctx *ctx, int enable) {
+    if (!ctx) return EXL3_EINVAL;
+    int rc;
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    clear_timing(ctx);
+    ctx->timing = enable != 0;
+    return EXL3_OK;
+}
+
+int exl3_ctx_read_timing(exl3_ctx *ctx, int kind, double *total_ms, int64_t *launches,
+                         int64_t *tiles) {
+    if (!ctx || !total_ms || !launches || !tiles) return fail(ctx, EXL3_EINVAL, "null argument");
+    int rc;
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    double ms = 0.0;
+    int64_t nl = 0, nt = 0;
+    for (auto &r : ctx->timed) {
+        if (r.kind != kind) continue;
+        float e = 0.0f;
+        EXL3_HIP(ctx, hipEventElapsedTime(&e, r.start, r.stop));
+        ms += e;
+        nl += 1;
+        nt += r.tiles;
+    }
+    *total_ms = ms;
+    *launches = nl;
+    *tiles = nt;
     return EXL3_OK;
 }
 
@@ -345,9 +429,11 @@ int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, in
 
     // 1. regularize (tile-major) with per-tile energy and the non-finite flag
     EXL3_HIP(ctx, hipMemsetAsync(ctx->d_flag, 0, sizeof(int), ctx->stream));
+    int reg_id = open_timed(ctx, EXL3_KERNEL_REGULARIZE, ntiles);
     EXL3_HIP(ctx, exl3::launch_regularize(w, w_dtype, rows, cols, had_block, su, sv, ctx->d_wreg,
                                           EXL3_TILE_MAJOR, ctx->d_sumsq, ctx->d_flag,
                                           ctx->stream));
+    close_timed(ctx, reg_id);
     std::vector<float> sumsq((size_t)ntiles);
     int flag = 0;
     EXL3_HIP(ctx, hipMemcpyAsync(sumsq.data(), ctx->d_sumsq, (size_t)ntiles * sizeof(float),

@@ -60,71 +60,129 @@ __device__ __forceinline__ void lane_butterflies(int g, int (&m)[Geo<K>::GPL], i
 
 // Append one bit per lane to acc: acc = 2 * acc + mask[lane] in one VALU op
 // (add with carry-in taken from the 64-bit lane mask).
-__device__ __forceinline__ uint32_t push_bit(uint32_t acc, uint64_t mask) {
-    uint32_t out;
-    uint64_t carry_out;
-    asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3"
-        : "=v"(out), "=s"(carry_out)
-        : "v"(acc), "s"(mask));
-    return out;
-}
-
-// Bits of the lowest index whose match mask is set, most significant first,
-// as lane masks.  c[j] = lanes where candidate j equals the minimum; the last
-// candidate wins where no earlier one matches, so c[N-1] is never read.
-template <int N>
-struct FirstMatch {
-    static __device__ __forceinline__ void bits(const uint64_t *c, uint64_t *out) {
-        uint64_t any_lo = 0;
-#pragma unroll
-        for (int j = 0; j < N / 2; ++j) any_lo |= c[j];
-        const uint64_t hi_half = ~any_lo;
-        uint64_t lo_bits[32], hi_bits[32];
-        FirstMatch<N / 2>::bits(c, lo_bits);
-        FirstMatch<N / 2>::bits(c + N / 2, hi_bits);
-        out[0] = hi_half;
-#pragma unroll
-        for (int j = 0; j + 1 < Log2<N>::v; ++j)
-            out[j + 1] = (hi_half & hi_bits[j]) | (~hi_half & lo_bits[j]);
-    }
-};
-template <>
-struct FirstMatch<2> {
-    static __device__ __forceinline__ void bits(const uint64_t *c, uint64_t *out) {
-        out[0] = ~c[0];
-    }
-};
-
-template <int NB>
-__device__ __forceinline__ float tree_min(const float (&a)[NB]) {
-    // pairwise then three-way minima (v_min3_f32); exact for non-NaN inputs
-    float r[(NB + 2) / 3];
-    int n = 0;
-#pragma unroll
-    for (int j = 0; j + 2 < NB; j += 3) r[n++] = __builtin_fminf(__builtin_fminf(a[j], a[j + 1]), a[j + 2]);
-    if (NB % 3 == 2) r[n++] = __builtin_fminf(a[NB - 2], a[NB - 1]);
-    if (NB % 3 == 1) r[n++] = a[NB - 1];
-    float m = r[0];
-#pragma unroll
-    for (int j = 1; j < n; ++j) m = __builtin_fminf(m, r[j]);
-    return m;
-}
-
-// One tracked-state update: minimum over the 2^K candidates and the lowest
-// index reaching it; the K index bits are appended to acc, high bit first.
+// The carry-outs go to scratch scalar pairs that nothing reads (writing VCC
+// here instead was measured to slow the whole loop down markedly); the K
+// insertions of one update form a single asm block.
 template <int K>
-__device__ __forceinline__ float acs(const float (&a)[1 << K], uint32_t &acc) {
-    constexpr int NB = 1 << K;
-    const float mn = tree_min<NB>(a);
-    uint64_t c[NB];
+__device__ __forceinline__ void push_bits(uint32_t &acc, const uint64_t (&kb)[K]);
+template <>
+__device__ __forceinline__ void push_bits<2>(uint32_t &acc, const uint64_t (&kb)[2]) {
+    uint64_t c0, c1;
+    asm("v_addc_co_u32_e64 %0, %1, %0, %0, %3\n\t"
+        "v_addc_co_u32_e64 %0, %2, %0, %0, %4"
+        : "+v"(acc), "=&s"(c0), "=&s"(c1) : "s"(kb[0]), "s"(kb[1]));
+}
+template <>
+__device__ __forceinline__ void push_bits<3>(uint32_t &acc, const uint64_t (&kb)[3]) {
+    uint64_t c0, c1, c2;
+    asm("v_addc_co_u32_e64 %0, %1, %0, %0, %4\n\t"
+        "v_addc_co_u32_e64 %0, %2, %0, %0, %5\n\t"
+        "v_addc_co_u32_e64 %0, %3, %0, %0, %6"
+        : "+v"(acc), "=&s"(c0), "=&s"(c1), "=&s"(c2) : "s"(kb[0]), "s"(kb[1]), "s"(kb[2]));
+}
+template <>
+__device__ __forceinline__ void push_bits<4>(uint32_t &acc, const uint64_t (&kb)[4]) {
+    uint64_t c0, c1, c2, c3;
+    asm("v_addc_co_u32_e64 %0, %1, %0, %0, %5\n\t"
+        "v_addc_co_u32_e64 %0, %2, %0, %0, %6\n\t"
+        "v_addc_co_u32_e64 %0, %3, %0, %0, %7\n\t"
+        "v_addc_co_u32_e64 %0, %4, %0, %0, %8"
+        : "+v"(acc), "=&s"(c0), "=&s"(c1), "=&s"(c2), "=&s"(c3)
+        : "s"(kb[0]), "s"(kb[1]), "s"(kb[2]), "s"(kb[3]));
+}
+
+// Minimum of the 2^K candidates and the lowest index reaching it, with the K
+// index bits appended to acc (high bit first).
+//
+// A tournament tree is built bottom-up but only the left child of every node
+// on a root-to-leaf path is ever needed: walking down from the root, the
+// minimum lies in the right subtree exactly when the left child's minimum is
+// larger than the overall minimum (equal values keep the left, i.e. lower,
+// index).  Each step of the walk is one compare, whose lane mask is both the
+// next index bit (inserted with add-with-carry) and the selector that picks
+// the next left child.  No scalar instructions are involved.
+template <int K>
+struct Acs;
+
+template <>
+struct Acs<2> {
+    static __device__ __forceinline__ float run(const float (&a)[4], uint32_t &acc) {
+        const float m01 = __builtin_fminf(a[0], a[1]);
+        const float m = __builtin_fminf(__builtin_fminf(m01, a[2]), a[3]);
+        const bool r1 = m01 > m;                      // index in {2, 3}
+        const float l0 = r1 ? a[2] : a[0];            // left leaf of the chosen pair
+        const bool r0 = l0 > m;
+        const uint64_t kb[2] = {__builtin_amdgcn_ballot_w64(r1), __builtin_amdgcn_ballot_w64(r0)};
+        push_bits<2>(acc, kb);
+        return m;
+    }
+};
+
+template <>
+struct Acs<3> {
+    static __device__ __forceinline__ float run(const float (&a)[8], uint32_t &acc) {
+        const float m01 = __builtin_fminf(a[0], a[1]);
+        const float m45 = __builtin_fminf(a[4], a[5]);
+        const float m67 = __builtin_fminf(a[6], a[7]);
+        const float m0123 = __builtin_fminf(__builtin_fminf(m01, a[2]), a[3]);
+        const float m = __builtin_fminf(__builtin_fminf(m0123, m45), m67);
+        const bool r2 = m0123 > m;                    // index in 4..7
+        const float l1 = r2 ? m45 : m01;              // left pair of the chosen half
+        const bool r1 = l1 > m;
+        const float lo = r1 ? a[2] : a[0];
+        const float hi = r1 ? a[6] : a[4];
+        const float l0 = r2 ? hi : lo;                // left leaf of the chosen pair
+        const bool r0 = l0 > m;
+        const uint64_t kb[3] = {__builtin_amdgcn_ballot_w64(r2), __builtin_amdgcn_ballot_w64(r1),
+                                __builtin_amdgcn_ballot_w64(r0)};
+        push_bits<3>(acc, kb);
+        return m;
+    }
+};
+
+template <>
+struct Acs<4> {
+    static __device__ __forceinline__ float run(const float (&a)[16], uint32_t &acc) {
+        const float m01 = __builtin_fminf(a[0], a[1]);
+        const float m45 = __builtin_fminf(a[4], a[5]);
+        const float m89 = __builtin_fminf(a[8], a[9]);
+        const float mCD = __builtin_fminf(a[12], a[13]);
+        const float m67 = __builtin_fminf(a[6], a[7]);
+        const float m0_3 = __builtin_fminf(__builtin_fminf(m01, a[2]), a[3]);
+        const float m8_11 = __builtin_fminf(__builtin_fminf(m89, a[10]), a[11]);
+        const float m0_7 = __builtin_fminf(__builtin_fminf(m0_3, m45), m67);
+        const float m12_15 = __builtin_fminf(__builtin_fminf(mCD, a[14]), a[15]);
+        const float m = __builtin_fminf(__builtin_fminf(m0_7, m8_11), m12_15);
+        const bool r3 = m0_7 > m;                     // index in 8..15
+        const float l2 = r3 ? m8_11 : m0_3;           // left quad of the chosen half
+        const bool r2 = l2 > m;
+        const float q_lo = r2 ? m45 : m01;            // left pair of the chosen quad
+        const float q_hi = r2 ? mCD : m89;
+        const float l1 = r3 ? q_hi : q_lo;
+        const bool r1 = l1 > m;
+        const float p0 = r1 ? a[2] : a[0];            // left leaf of the chosen pair
+        const float p1 = r1 ? a[6] : a[4];
+        const float p2 = r1 ? a[10] : a[8];
+        const float p3 = r1 ? a[14] : a[12];
+        const float h0 = r2 ? p1 : p0;
+        const float h1 = r2 ? p3 : p2;
+        const float l0 = r3 ? h1 : h0;
+        const bool r0 = l0 > m;
+        const uint64_t kb[4] = {__builtin_amdgcn_ballot_w64(r3), __builtin_amdgcn_ballot_w64(r2),
+                                __builtin_amdgcn_ballot_w64(r1), __builtin_amdgcn_ballot_w64(r0)};
+        push_bits<4>(acc, kb);
+        return m;
+    }
+};
+
+// Minimum of the 2^K candidates only (steps whose backpointers are not kept).
+template <int NB>
+__device__ __forceinline__ float min_only(const float (&a)[NB]) {
+    float r = __builtin_fminf(__builtin_fminf(a[0], a[1]), a[2]);
 #pragma unroll
-    for (int j = 0; j + 1 < NB; ++j) c[j] = __builtin_amdgcn_ballot_w64(a[j] == mn);
-    c[NB - 1] = 0;
-    uint64_t kb[K];
-    FirstMatch<NB>::bits(c, kb);
-#pragma unroll
-    for (int j = 0; j < K; ++j) acc = push_bit(acc, kb[j]);
-    return mn;
+    for (int j = 3; j + 1 < NB; j += 2) r = __builtin_fminf(__builtin_fminf(r, a[j]), a[j + 1]);
+    if (NB % 2 == 0) r = __builtin_fminf(r, a[NB - 1]);
+    return r;
 }
 
 template <int K, int PASS>
@@ -169,11 +227,13 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
 
     bp_t *bp_tile = bp + (size_t)b * kSlots * kLanes;
 
-    for (int t = 0; t < kSteps - 1; ++t) {
-        const float xt = xs[(PASS == 1) ? ((t + 128) & 255) : t];
+    // Pass 1 keeps backpointers only from step 127 on: the steps before need
+    // the minima alone.
+    constexpr int t_first = (PASS == 1) ? 127 : 0;
+    if constexpr (PASS == 1) for (int t = 0; t < t_first; ++t) {
+        const float xt = xs[(t + 128) & 255];
         const float *Mc = Mbuf[t & 1];
         float *Mn = Mbuf[(t + 1) & 1];
-        uint32_t bits = 0;
 #pragma unroll
         for (int i = 0; i < G::GPL; ++i) {
             float Mk[G::NB];
@@ -189,7 +249,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
                     float q = d * d;
                     a[k] = Mk[k] + q;
                 }
-                outv[bb] = acs<K>(a, bits);
+                outv[bb] = min_only<G::NB>(a);
             }
             float *dst = Mn + ((m[i] << K) | b0);
 #pragma unroll
@@ -197,11 +257,101 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
                 *reinterpret_cast<float4 *>(dst + q4) =
                     make_float4(outv[q4], outv[q4 + 1], outv[q4 + 2], outv[q4 + 3]);
         }
-        if (PASS == 1) {
-            if (t >= 127) bp_tile[(size_t)(t - 127) * kLanes + g] = (bp_t)bits;
-        } else {
-            bp_tile[(size_t)t * kLanes + g] = (bp_t)bits;
+        __syncthreads();
+    }
+
+    // K = 2: the lane's 16 updates per step are software-pipelined so that no
+    // compare result is consumed right after it is produced: iteration e issues
+    // the branch metrics of update e, the walk of update e-1 (select the left
+    // leaf of the chosen pair, compare), the tree of update e (minima and the
+    // top compare) and the bit insertion of update e-2.
+    if constexpr (K == 2) for (int t = t_first; t < kSteps - 1; ++t) {
+        const float xt = xs[(PASS == 1) ? ((t + 128) & 255) : t];
+        const float *Mc = Mbuf[t & 1];
+        float *Mn = Mbuf[(t + 1) & 1];
+        constexpr int NE = G::GPL * G::BPL;
+        float Mk[G::GPL][G::NB];
+#pragma unroll
+        for (int i = 0; i < G::GPL; ++i)
+#pragma unroll
+            for (int k = 0; k < G::NB; ++k) Mk[i][k] = Mc[(k << G::MBITS) | m[i]];
+        uint32_t bits = 0;
+        float mn[NE], a0[NE], a2[NE];
+        bool r1[NE], r0[NE];
+#pragma unroll
+        for (int e = 0; e < NE + 2; ++e) {
+            float a[4];
+            if (e < NE) {
+                const int i = e / G::BPL, bb = e % G::BPL;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    float d = xt - v[i][k][bb];
+                    float q = d * d;
+                    a[k] = Mk[i][k] + q;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (e >= 1 && e - 1 < NE) {
+                const float l0 = r1[e - 1] ? a2[e - 1] : a0[e - 1];
+                r0[e - 1] = l0 > mn[e - 1];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (e < NE) {
+                const float m01 = __builtin_fminf(a[0], a[1]);
+                mn[e] = __builtin_fminf(__builtin_fminf(m01, a[2]), a[3]);
+                r1[e] = m01 > mn[e];
+                a0[e] = a[0];
+                a2[e] = a[2];
+                const int i = e / G::BPL, bb = e % G::BPL;
+                if (bb == G::BPL - 1) {
+                    float *dst = Mn + ((m[i] << K) | b0);
+                    *reinterpret_cast<float4 *>(dst) =
+                        make_float4(mn[e - 3], mn[e - 2], mn[e - 1], mn[e]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (e >= 2) {
+                const uint64_t kb[2] = {__builtin_amdgcn_ballot_w64(r1[e - 2]),
+                                        __builtin_amdgcn_ballot_w64(r0[e - 2])};
+                push_bits<2>(bits, kb);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
+        bp_tile[(size_t)(t - t_first) * kLanes + g] = (bp_t)bits;
+        __syncthreads();
+    }
+
+    if constexpr (K != 2) for (int t = t_first; t < kSteps - 1; ++t) {
+        const float xt = xs[(PASS == 1) ? ((t + 128) & 255) : t];
+        const float *Mc = Mbuf[t & 1];
+        float *Mn = Mbuf[(t + 1) & 1];
+        float Mk[G::GPL][G::NB];
+#pragma unroll
+        for (int i = 0; i < G::GPL; ++i)
+#pragma unroll
+            for (int k = 0; k < G::NB; ++k) Mk[i][k] = Mc[(k << G::MBITS) | m[i]];
+        uint32_t bits = 0;
+#pragma unroll
+        for (int i = 0; i < G::GPL; ++i) {
+            float outv[G::BPL];
+#pragma unroll
+            for (int bb = 0; bb < G::BPL; ++bb) {
+                float a[G::NB];
+#pragma unroll
+                for (int k = 0; k < G::NB; ++k) {
+                    float d = xt - v[i][k][bb];
+                    float q = d * d;
+                    a[k] = Mk[i][k] + q;
+                }
+                outv[bb] = Acs<K>::run(a, bits);
+            }
+            float *dst = Mn + ((m[i] << K) | b0);
+#pragma unroll
+            for (int q4 = 0; q4 < G::BPL; q4 += 4)
+                *reinterpret_cast<float4 *>(dst + q4) =
+                    make_float4(outv[q4], outv[q4 + 1], outv[q4 + 2], outv[q4 + 3]);
+        }
+        bp_tile[(size_t)(t - t_first) * kLanes + g] = (bp_t)bits;
         __syncthreads();
     }
 
