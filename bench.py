@@ -24,8 +24,12 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_FP32_TFLOPS = 157.3      # 256 CU x 2.4 GHz x 256 FP32 flop/clk (packed FMA)
-PEAK_ISSUE_TOPS = 39.3        # 256 CU x 2.4 GHz x 64 unpacked single-op lanes/clk
+PEAK_FP32_TFLOPS = 157.3      # 256 CU x 2.4 GHz x 256 FP32 flop/clk (FMA = 2 flops)
+# One-operation (non-FMA) FP32 issue ceiling: each SIMD can issue two VALU
+# instructions per 4-cycle wave64 slot (measured on gfx950 with the
+# SQ_ACTIVE_INST_VALU2 counter and issue probes), i.e. 2 x 64 lanes / 4 cycles
+# per SIMD: 256 CU x 4 SIMD x 32 lane-ops/clk x 2.4 GHz.
+PEAK_ISSUE_TOPS = 78.6
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "viterbi_fwd_traffic.json")
 FWD_SOURCE = os.path.join(ROOT, "trellis_coded_weight_amd", "csrc", "viterbi_fwd.hip")
 METRIC = "encoded 16x16 tiles/sec at K=2/3/4 on 1 MI355X; % of FP32 VALU peak"
@@ -66,10 +70,57 @@ def load_traffic(K: int):
         return None
     if d.get("source_sha256") != file_sha(FWD_SOURCE):
         return None
-    per = d.get("per_launch", {}).get("K%d" % K)
-    if not per:
-        return None
-    return per
+    return d.get("per_launch", {}).get("K%d" % K)
+
+
+def summarize_traffic(fetch_csv, write_csv, copy_mib, out_path=TRAFFIC_FILE):
+    """Per-tile HBM bytes of the forward kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the
+    same counter reads for the plain device copy of known size that
+    --copy-probe-mib runs first (the largest copy dispatch in the file)."""
+    import collections
+    import csv
+
+    def per_dispatch(path, counter):
+        vals = collections.defaultdict(float)
+        meta = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            d = r["Dispatch_Id"]
+            vals[d] += float(r["Counter_Value"])
+            meta[d] = (r["Kernel_Name"], int(r["Grid_Size"]))
+        return vals, meta
+
+    out = {"source_sha256": file_sha(FWD_SOURCE), "per_launch": {}, "calibration": {}}
+    per = collections.defaultdict(dict)
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals, meta = per_dispatch(path, counter)
+        copies = [(meta[d][1], d) for d in vals if "copyBuffer" in meta[d][0]]
+        grid, dcopy = max(copies)                # the probe: the largest copy
+        copy_bytes = copy_mib * (1 << 20)          # it reads and writes this much
+        scale = copy_bytes / (vals[dcopy] * 1024.0)
+        out["calibration"][counter] = {"copy_bytes": copy_bytes,
+                                       "counter_kib": vals[dcopy], "scale": scale}
+        for d, v in vals.items():
+            name, grid = meta[d]
+            if "viterbi_fwd_kernel" not in name:
+                continue
+            k = name.split("viterbi_fwd_kernel<")[1].split(">")[0].replace(" ", "")
+            tiles = grid // 1024
+            acc = per[k].setdefault(counter, [0.0, 0])
+            acc[0] += v * 1024.0 * scale
+            acc[1] += tiles
+    for k, d in per.items():
+        K, pas = k.split(",")
+        ent = out["per_launch"].setdefault("K%s" % K, {})
+        ent["pass%s" % pas] = {
+            "fetch_bytes_per_tile": d["FETCH_SIZE"][0] / d["FETCH_SIZE"][1],
+            "write_bytes_per_tile": d["WRITE_SIZE"][0] / d["WRITE_SIZE"][1],
+        }
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
 
 
 def cpu_baseline(m, K, scale, n_tiles, threads, sample_tiles):
@@ -120,14 +171,23 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tiles", type=int, default=2048)
+    ap.add_argument("--cpu-tiles", type=int, default=8192)
     ap.add_argument("--no-other-k", action="store_true",
                     help="skip the K=3 and K=4 runs on the same matrix")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the forward kernel's HBM bytes per tile from two "
+                         "rocprofv3 --pmc counter_collection.csv files and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "kernel to scale HBM byte counters against)")
     args = ap.parse_args()
 
+    if args.summarize_traffic:
+        if args.copy_probe_mib <= 0:
+            sys.exit("--summarize-traffic needs --copy-probe-mib (the probe size used)")
+        print(json.dumps(summarize_traffic(*args.summarize_traffic, args.copy_probe_mib),
+                         indent=1))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the encoder's tiles are independent and "
               "this build runs on a single MI355X; --gpus %d is not supported" % args.gpus,
@@ -183,7 +243,12 @@ def main():
     fwd_ops = f1_tiles * ops_per_pass(K, True) + f2_tiles * ops_per_pass(K, False)
     fwd_s = (f1_ms + f2_ms) / 1000.0
     achieved = fwd_ops / fwd_s / 1e12
-    traffic = load_traffic(K)
+    traffic = None
+    per = load_traffic(K)
+    if per and "pass1" in per and "pass2" in per:
+        t1 = per["pass1"]["fetch_bytes_per_tile"] + per["pass1"]["write_bytes_per_tile"]
+        t2 = per["pass2"]["fetch_bytes_per_tile"] + per["pass2"]["write_bytes_per_tile"]
+        traffic = (t1 * f1_tiles + t2 * f2_tiles) / max(f1_n + f2_n, 1)
     roofline = {
         "bound": "alu",
         "achieved": round(achieved, 3),
