@@ -185,97 +185,27 @@ __device__ __forceinline__ float min_only(const float (&a)[NB]) {
     return r;
 }
 
-template <int K, int PASS>
-__global__ void __launch_bounds__(kLanes, 1)
-viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile_idx,
-                   int64_t tile0, const uint16_t *__restrict__ levels, float scale,
-                   const uint16_t *__restrict__ X_in, typename Geo<K>::bp_t *__restrict__ bp,
-                   uint16_t *__restrict__ end_state, float *__restrict__ cost_out) {
+// One trellis step for the lane's 64 states: read the tracked minima of its
+// butterflies from Mc, write the new minima to Mn and return the backpointer
+// word (BITS) -- or only the minima (!BITS, steps whose backpointers are never
+// read).  At K = 2 with bits the lane's 16 updates are software-pipelined so
+// that no compare result is consumed right after it is produced: iteration e
+// issues the branch metrics of update e, the walk of update e-1 (select the
+// left leaf of the chosen pair, compare), the tree of update e (minima and the
+// top compare) and the bit insertion of update e-2.
+template <int K, bool BITS>
+__device__ __forceinline__ uint32_t trellis_step(
+    float xt, const float *__restrict__ Mc, float *__restrict__ Mn,
+    const float (&v)[Geo<K>::GPL][Geo<K>::NB][Geo<K>::BPL], const int (&m)[Geo<K>::GPL], int b0) {
     using G = Geo<K>;
-    using bp_t = typename G::bp_t;
-    __shared__ float Mbuf[2][G::T];
-    __shared__ float xs[kSteps];
-    __shared__ float red_cost[kLanes / 64];
-    __shared__ uint32_t red_state[kLanes / 64];
-
-    const int g = threadIdx.x;
-    const int64_t b = blockIdx.x;
-    const int64_t tile = tile_idx ? (int64_t)tile_idx[b] : tile0 + b;
-
-    if (g < kSteps) xs[g] = x[tile * kSteps + g];
-
-    int m[G::GPL];
-    int b0;
-    lane_butterflies<K>(g, m, b0);
-
-    // levels of the lane's 64 states, scaled once per pass
-    float v[G::GPL][G::NB][G::BPL];
+    float Mk[G::GPL][G::NB];
 #pragma unroll
     for (int i = 0; i < G::GPL; ++i)
 #pragma unroll
-        for (int k = 0; k < G::NB; ++k)
-#pragma unroll
-            for (int bb = 0; bb < G::BPL; ++bb) {
-                uint32_t s = ((uint32_t)k << G::Kr) | ((uint32_t)m[i] << K) | (uint32_t)(b0 + bb);
-                v[i][k][bb] = scale * half_bits_to_float(levels[s]);
-            }
-
-    const uint32_t xm = (PASS == 1) ? 0u : ((uint32_t)X_in[b] & (uint32_t)(G::T - 1));
-    for (int e = g; e < G::T; e += kLanes)
-        Mbuf[0][e] = (PASS == 1 || (uint32_t)e == xm) ? 0.0f : INFINITY;
-    __syncthreads();
-
-    bp_t *bp_tile = bp + (size_t)b * kSlots * kLanes;
-
-    // Pass 1 keeps backpointers only from step 127 on: the steps before need
-    // the minima alone.
-    constexpr int t_first = (PASS == 1) ? 127 : 0;
-    if constexpr (PASS == 1) for (int t = 0; t < t_first; ++t) {
-        const float xt = xs[(t + 128) & 255];
-        const float *Mc = Mbuf[t & 1];
-        float *Mn = Mbuf[(t + 1) & 1];
-#pragma unroll
-        for (int i = 0; i < G::GPL; ++i) {
-            float Mk[G::NB];
-#pragma unroll
-            for (int k = 0; k < G::NB; ++k) Mk[k] = Mc[(k << G::MBITS) | m[i]];
-            float outv[G::BPL];
-#pragma unroll
-            for (int bb = 0; bb < G::BPL; ++bb) {
-                float a[G::NB];
-#pragma unroll
-                for (int k = 0; k < G::NB; ++k) {
-                    float d = xt - v[i][k][bb];
-                    float q = d * d;
-                    a[k] = Mk[k] + q;
-                }
-                outv[bb] = min_only<G::NB>(a);
-            }
-            float *dst = Mn + ((m[i] << K) | b0);
-#pragma unroll
-            for (int q4 = 0; q4 < G::BPL; q4 += 4)
-                *reinterpret_cast<float4 *>(dst + q4) =
-                    make_float4(outv[q4], outv[q4 + 1], outv[q4 + 2], outv[q4 + 3]);
-        }
-        __syncthreads();
-    }
-
-    // K = 2: the lane's 16 updates per step are software-pipelined so that no
-    // compare result is consumed right after it is produced: iteration e issues
-    // the branch metrics of update e, the walk of update e-1 (select the left
-    // leaf of the chosen pair, compare), the tree of update e (minima and the
-    // top compare) and the bit insertion of update e-2.
-    if constexpr (K == 2) for (int t = t_first; t < kSteps - 1; ++t) {
-        const float xt = xs[(PASS == 1) ? ((t + 128) & 255) : t];
-        const float *Mc = Mbuf[t & 1];
-        float *Mn = Mbuf[(t + 1) & 1];
+        for (int k = 0; k < G::NB; ++k) Mk[i][k] = Mc[(k << G::MBITS) | m[i]];
+    uint32_t bits = 0;
+    if constexpr (BITS && K == 2) {
         constexpr int NE = G::GPL * G::BPL;
-        float Mk[G::GPL][G::NB];
-#pragma unroll
-        for (int i = 0; i < G::GPL; ++i)
-#pragma unroll
-            for (int k = 0; k < G::NB; ++k) Mk[i][k] = Mc[(k << G::MBITS) | m[i]];
-        uint32_t bits = 0;
         float mn[NE], a0[NE], a2[NE];
         bool r1[NE], r0[NE];
 #pragma unroll
@@ -317,20 +247,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        bp_tile[(size_t)(t - t_first) * kLanes + g] = (bp_t)bits;
-        __syncthreads();
-    }
-
-    if constexpr (K != 2) for (int t = t_first; t < kSteps - 1; ++t) {
-        const float xt = xs[(PASS == 1) ? ((t + 128) & 255) : t];
-        const float *Mc = Mbuf[t & 1];
-        float *Mn = Mbuf[(t + 1) & 1];
-        float Mk[G::GPL][G::NB];
-#pragma unroll
-        for (int i = 0; i < G::GPL; ++i)
-#pragma unroll
-            for (int k = 0; k < G::NB; ++k) Mk[i][k] = Mc[(k << G::MBITS) | m[i]];
-        uint32_t bits = 0;
+    } else {
 #pragma unroll
         for (int i = 0; i < G::GPL; ++i) {
             float outv[G::BPL];
@@ -343,7 +260,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
                     float q = d * d;
                     a[k] = Mk[i][k] + q;
                 }
-                outv[bb] = Acs<K>::run(a, bits);
+                outv[bb] = BITS ? Acs<K>::run(a, bits) : min_only<G::NB>(a);
             }
             float *dst = Mn + ((m[i] << K) | b0);
 #pragma unroll
@@ -351,12 +268,108 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
                 *reinterpret_cast<float4 *>(dst + q4) =
                     make_float4(outv[q4], outv[q4 + 1], outv[q4 + 2], outv[q4 + 3]);
         }
-        bp_tile[(size_t)(t - t_first) * kLanes + g] = (bp_t)bits;
-        __syncthreads();
+    }
+    return bits;
+}
+
+template <int K, int PASS>
+__global__ void __launch_bounds__(kLanes, 1)
+viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile_idx,
+                   int64_t tile0, const uint16_t *__restrict__ levels, float scale,
+                   const uint16_t *__restrict__ X_in, typename Geo<K>::bp_t *__restrict__ bp,
+                   uint16_t *__restrict__ end_state, float *__restrict__ cost_out) {
+    using G = Geo<K>;
+    using bp_t = typename G::bp_t;
+    __shared__ float Mbuf[2][G::T];
+    __shared__ float xs[kSteps];
+    __shared__ float red_cost[kLanes / 64];
+    __shared__ uint32_t red_state[kLanes / 64];
+
+    const int g = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const int64_t tile = tile_idx ? (int64_t)tile_idx[b] : tile0 + b;
+
+    // step t reads the input at position (t + 128) mod 256 in pass 1 (rotated)
+    if (g < kSteps) xs[g] = x[tile * kSteps + ((PASS == 1) ? ((g + 128) & 255) : g)];
+
+    int m[G::GPL];
+    int b0;
+    lane_butterflies<K>(g, m, b0);
+
+    // levels of the lane's 64 states, scaled once per pass
+    float v[G::GPL][G::NB][G::BPL];
+#pragma unroll
+    for (int i = 0; i < G::GPL; ++i)
+#pragma unroll
+        for (int k = 0; k < G::NB; ++k)
+#pragma unroll
+            for (int bb = 0; bb < G::BPL; ++bb) {
+                uint32_t s = ((uint32_t)k << G::Kr) | ((uint32_t)m[i] << K) | (uint32_t)(b0 + bb);
+                v[i][k][bb] = scale * half_bits_to_float(levels[s]);
+            }
+
+    const uint32_t xm = (PASS == 1) ? 0u : ((uint32_t)X_in[b] & (uint32_t)(G::T - 1));
+    for (int e = g; e < G::T; e += kLanes)
+        Mbuf[0][e] = (PASS == 1 || (uint32_t)e == xm) ? 0.0f : INFINITY;
+    __syncthreads();
+
+    bp_t *bp_tile = bp + (size_t)b * kSlots * kLanes;
+
+    // Steps alternate between the two LDS buffers; the loops advance two steps
+    // at a time so both buffer addresses are constants.  Pass 1 keeps
+    // backpointers only from step 127 on (odd), pass 2 from step 0.
+    constexpr int t_first = (PASS == 1) ? 127 : 0;
+    float *const B0 = Mbuf[0];
+    float *const B1 = Mbuf[1];
+    float xt = xs[0];
+    int t = 0;
+    if constexpr (PASS == 1) {
+        for (; t + 1 < t_first; t += 2) {           // steps 0..125 in pairs
+            const float xn = xs[t + 1];
+            trellis_step<K, false>(xt, B0, B1, v, m, b0);
+            __syncthreads();
+            xt = xs[t + 2];
+            trellis_step<K, false>(xn, B1, B0, v, m, b0);
+            __syncthreads();
+        }
+        {                                           // step 126: B0 -> B1
+            const float xn = xs[t + 1];
+            trellis_step<K, false>(xt, B0, B1, v, m, b0);
+            __syncthreads();
+            xt = xn;
+            ++t;
+        }
+        for (; t < kSteps - 1; t += 2) {            // steps 127..254: B1 -> B0 -> B1
+            const float xn = xs[t + 1];
+            uint32_t w = trellis_step<K, true>(xt, B1, B0, v, m, b0);
+            bp_tile[(size_t)(t - t_first) * kLanes + g] = (bp_t)w;
+            __syncthreads();
+            xt = xn;
+            if (t + 1 < kSteps - 1) {
+                xt = xs[t + 2];
+                w = trellis_step<K, true>(xn, B0, B1, v, m, b0);
+                bp_tile[(size_t)(t + 1 - t_first) * kLanes + g] = (bp_t)w;
+                __syncthreads();
+            }
+        }
+    } else {
+        for (; t < kSteps - 1; t += 2) {            // steps 0..254: B0 -> B1 -> B0
+            const float xn = xs[t + 1];
+            uint32_t w = trellis_step<K, true>(xt, B0, B1, v, m, b0);
+            bp_tile[(size_t)t * kLanes + g] = (bp_t)w;
+            __syncthreads();
+            xt = xn;
+            if (t + 1 < kSteps - 1) {
+                xt = xs[t + 2];
+                w = trellis_step<K, true>(xn, B1, B0, v, m, b0);
+                bp_tile[(size_t)(t + 1) * kLanes + g] = (bp_t)w;
+                __syncthreads();
+            }
+        }
     }
 
     // last step: costs of all states, no minimum over predecessors
-    const float xt = xs[(PASS == 1) ? 127 : 255];
+    xt = xs[kSteps - 1];
     const float *Mc = Mbuf[(kSteps - 1) & 1];
     if (PASS == 1) {
         float best = 0.0f;
