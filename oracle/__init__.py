@@ -15,5 +15,5 @@ from .reference import (  # noqa: F401
     from_tiles, fwht_rows_blockwise, golden_section, hadamard_norm, matrix_rms,
     mul1_levels_fp16, pack_states, quantize_matrix, regularize, sample_tiles,
     scaled_levels, tile_sse, tile_sumsq, to_tiles, unpack_states, unregularize,
-    default_threads,
+    default_threads, encode_sequences_f16, encode_tiles_f16, f16_sqadd, f16_sub, forward_f16,
 )

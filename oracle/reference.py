@@ -76,6 +76,19 @@ def _load():
                                            ctypes.c_int, ctypes.c_int, f32p,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_encode_many.restype = ctypes.c_int
+        u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+        lib.oracle_f16_sub.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
+        lib.oracle_f16_sub.restype = ctypes.c_uint16
+        lib.oracle_f16_sqadd.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
+        lib.oracle_f16_sqadd.restype = ctypes.c_uint16
+        lib.oracle_forward_f16.argtypes = [u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           u16p, u16p, u16p, u8p]
+        lib.oracle_forward_f16.restype = ctypes.c_int
+        lib.oracle_encode_many_f16.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, u16p,
+                                               ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        lib.oracle_encode_many_f16.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -413,3 +426,74 @@ def quantize_matrix(w, su, sv, K, had_block=128, gss=(12, 0.5, 2.0), fixed_scale
             total += float(e)
         out["mse"] = total / (R * C)
     return out
+
+
+# --------------------------------------------------------------------------
+# fp16 mode  [P1 items 1 and 4: binary16 difference, single-rounded fused
+# multiply-add into binary16 path costs, first-branch strict "<" ties]
+# --------------------------------------------------------------------------
+def f16_sub(a: int, b: int) -> int:
+    """Bits of fp16(a - b) for binary16 bit patterns a, b (one rounding)."""
+    return int(_load().oracle_f16_sub(a, b))
+
+
+def f16_sqadd(d: int, m: int) -> int:
+    """Bits of fp16(d*d + m), rounded once (fused), for binary16 bit patterns."""
+    return int(_load().oracle_f16_sqadd(d, m))
+
+
+def forward_f16(x_bits, Q, K, c_bits, M0_bits):
+    """fp16 forward pass; returns (final-step costs as uint16 bits, predecessors)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    c = np.ascontiguousarray(c_bits, dtype=np.uint16)
+    M0 = np.ascontiguousarray(M0_bits, dtype=np.uint16)
+    L = x.shape[0]
+    C = np.empty(1 << Q, dtype=np.uint16)
+    bp = np.empty(((L - 1), 1 << (Q - K)), dtype=np.uint8)
+    rc = _load().oracle_forward_f16(x, L, Q, K, c, M0, C, bp)
+    if rc != 0:
+        raise ValueError("oracle_forward_f16 rejected its arguments (rc=%d)" % rc)
+    return C, bp
+
+
+def encode_sequences_f16(x_bits, K, c_bits, Q=STATE_BITS, threads=None):
+    """fp16 two-pass encode of each row of x_bits [n, L] (binary16 bit patterns).
+
+    Returns (states int32 [n, L], X int32 [n], cost uint16 bits [n]).
+    """
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    c = np.ascontiguousarray(c_bits, dtype=np.uint16)
+    n, L = x.shape
+    states = np.empty((n, L), dtype=np.int32)
+    X = np.empty(n, dtype=np.int32)
+    cost = np.empty(n, dtype=np.uint16)
+    if n == 0:
+        return states, X, cost
+    lib = _load()
+    threads = threads or default_threads()
+    chunks = np.array_split(np.arange(n), min(threads, n))
+
+    def run(idx):
+        if idx.size == 0:
+            return 0
+        i0 = int(idx[0])
+        return lib.oracle_encode_many_f16(
+            x[i0:].ctypes.data, int(idx.size), L, Q, K, c,
+            states[i0:].ctypes.data, X[i0:].ctypes.data, cost[i0:].ctypes.data)
+
+    if len(chunks) == 1:
+        rcs = [run(chunks[0])]
+    else:
+        with ThreadPoolExecutor(max_workers=len(chunks)) as ex:
+            rcs = list(ex.map(run, chunks))
+    if any(rc != 0 for rc in rcs):
+        raise ValueError("oracle_encode_many_f16 rejected its arguments (rc=%s)" % rcs)
+    return states, X, cost
+
+
+def encode_tiles_f16(x_bits, K, levels=None, threads=None):
+    """fp16-mode encode of tiles [n, 256] given as binary16 bits, raw level table."""
+    if levels is None:
+        levels = mul1_levels_fp16()
+    states, X, cost = encode_sequences_f16(x_bits, K, levels.view(np.uint16), threads=threads)
+    return {"states": states, "X": X, "cost": cost, "packed": pack_states(states, K)}
