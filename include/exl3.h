@@ -130,6 +130,28 @@ int exl3_encode_tiles(exl3_ctx *ctx, const float *x, int64_t n, int K, float sca
                       uint16_t *packed, uint16_t *states, float *tile_sse);
 
 /*
+ * Encode n tiles in binary16 arithmetic [P1 sections 1 and 4: the half-precision
+ * add-compare-select]: the same two-pass tail-biting search, with inputs, code
+ * values and path costs in IEEE binary16.  Per state and step the difference
+ * x_t - c[s] is rounded once to binary16 and the cost d*d + M is one fused
+ * multiply-add rounded once to binary16 (nearest-even, subnormals kept,
+ * overflow to +inf); among equal costs the lowest branch index wins, and the
+ * pass-1 end state is the lowest-index state of least cost.  The code values
+ * are the context's codebook as binary16 bit patterns, unscaled.
+ *   x         uint16 [n][256]: binary16 bit patterns, tile-major (finite;
+ *             otherwise the output is unspecified but the call stays
+ *             memory-safe)
+ *   packed    uint16 [n][16*K]: container as for exl3_encode_tiles
+ *   states    optional uint16 [n][256]: the state sequence S_0..S_255
+ *   cost      optional uint16 [n]: the path cost as binary16 bits (the
+ *             binary16 sequential sum over the tile of fp16(fp16(x_t - c)^2 + acc))
+ * K in {2, 3, 4}.  n may be 0.  Asynchronous (uses the context's scratch).
+ * Errors: EXL3_EINVAL, EXL3_EUNSUPPORTED, EXL3_ENOMEM, EXL3_EHIP.
+ */
+int exl3_encode_tiles_f16(exl3_ctx *ctx, const uint16_t *x, int64_t n, int K, uint16_t *packed,
+                          uint16_t *states, uint16_t *cost);
+
+/*
  * Decode n packed tiles [P1 section 5]: S_t = the 16-bit window of the
  * circular bit stream that ends at bit (t+1)*K - 1; out[t] = rn(scale*c[S_t]).
  *   packed uint16 [n][16*K] (as written by exl3_encode_tiles), out float [n][256].

@@ -29,7 +29,8 @@ EXL3_TILE_MAJOR = 1
 EXPORTED = [
     "exl3_version", "exl3_ctx_create", "exl3_ctx_destroy", "exl3_last_error",
     "exl3_ctx_set_stream", "exl3_set_codebook", "exl3_get_codebook", "exl3_regularize",
-    "exl3_encode_tiles", "exl3_decode_tiles", "exl3_quantize_matrix", "exl3_scratch_per_tile",
+    "exl3_encode_tiles", "exl3_encode_tiles_f16", "exl3_decode_tiles", "exl3_quantize_matrix",
+    "exl3_scratch_per_tile",
     "exl3_ctx_set_timing", "exl3_ctx_read_timing",
 ]
 KERNEL_KINDS = {"fwd1": 0, "fwd2": 1, "tb1": 2, "tb2": 3, "regularize": 4}
@@ -83,6 +84,8 @@ def load_library():
     lib.exl3_regularize.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
     lib.exl3_encode_tiles.restype = i32
     lib.exl3_encode_tiles.argtypes = [vp, vp, i64, i32, f32, vp, vp, vp]
+    lib.exl3_encode_tiles_f16.restype = i32
+    lib.exl3_encode_tiles_f16.argtypes = [vp, vp, i64, i32, vp, vp, vp]
     lib.exl3_decode_tiles.restype = i32
     lib.exl3_decode_tiles.argtypes = [vp, vp, i64, i32, f32, vp]
     lib.exl3_quantize_matrix.restype = i32
@@ -232,6 +235,20 @@ class Context:
         self._check(self.lib.exl3_encode_tiles(self.handle, _ptr(x), n, K, float(scale),
                                                _ptr(packed), _ptr(states), _ptr(sse)))
         return packed, states, sse
+
+    def encode_tiles_f16(self, x: torch.Tensor, K: int, want_states: bool = True,
+                         want_cost: bool = True):
+        """x float16 [n, 256] -> (packed int16 [n, 16K], states int16 [n, 256] | None,
+        cost float16 [n] | None); binary16 arithmetic throughout."""
+        n = x.shape[0]
+        _need(x, torch.float16, (n, 256), "x")
+        packed = torch.empty(n, 16 * K, dtype=torch.int16, device=x.device)
+        states = torch.empty(n, 256, dtype=torch.int16, device=x.device) if want_states else None
+        cost = torch.empty(n, dtype=torch.float16, device=x.device) if want_cost else None
+        self._sync_stream()
+        self._check(self.lib.exl3_encode_tiles_f16(self.handle, _ptr(x), n, K, _ptr(packed),
+                                                   _ptr(states), _ptr(cost)))
+        return packed, states, cost
 
     def decode_tiles(self, packed: torch.Tensor, K: int, scale: float) -> torch.Tensor:
         n = packed.shape[0]

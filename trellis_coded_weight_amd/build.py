@@ -16,7 +16,8 @@ OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libexl3_gfx950.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.hip", "viterbi_fwd.hip", "traceback.hip", "regularize.hip", "codebook.cpp"]
+SOURCES = ["api.hip", "viterbi_fwd.hip", "viterbi_fwd_f16.hip", "traceback.hip", "regularize.hip",
+           "codebook.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [
@@ -34,7 +35,7 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
-def build(verbose: bool = False, save_temps_dir: str = None) -> str:
+def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
     os.makedirs(OBJ_DIR, exist_ok=True)
     objs = []
@@ -43,9 +44,6 @@ def build(verbose: bool = False, save_temps_dir: str = None) -> str:
         cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
-        if save_temps_dir:
-            os.makedirs(save_temps_dir, exist_ok=True)
-            cmd += ["-save-temps=obj"] if False else []
         _run(cmd, verbose)
         objs.append(obj)
     tmp = LIB + ".tmp%d" % os.getpid()

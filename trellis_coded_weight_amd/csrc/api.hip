@@ -187,7 +187,7 @@ int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, i
                                                ctx->stream));
         close_timed(ctx, id);
         id = open_timed(ctx, EXL3_KERNEL_TB1, nb);
-        EXL3_HIP(ctx, exl3::launch_traceback(K, 1, ctx->d_bp, nb, ctx->d_end, ctx->d_X, nullptr,
+        EXL3_HIP(ctx, exl3::launch_traceback(K, 1, false, ctx->d_bp, nb, ctx->d_end, ctx->d_X, nullptr,
                                              nullptr, 0, nullptr, 0.0f, nullptr, nullptr,
                                              nullptr, nullptr, ctx->stream));
         close_timed(ctx, id);
@@ -199,11 +199,55 @@ int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, i
         close_timed(ctx, id);
         if (!cost_only) {
             id = open_timed(ctx, EXL3_KERNEL_TB2, nb);
-            EXL3_HIP(ctx, exl3::launch_traceback(K, 2, ctx->d_bp, nb, ctx->d_X, nullptr, x,
+            EXL3_HIP(ctx, exl3::launch_traceback(K, 2, false, ctx->d_bp, nb, ctx->d_X, nullptr, x,
                                                  idx_b, i0, ctx->d_levels, scale, packed,
                                                  states, sse, w_hat, ctx->stream));
             close_timed(ctx, id);
         }
+    }
+    return EXL3_OK;
+}
+
+// The same chain in binary16 arithmetic: costs come out of pass 2 directly.
+int encode_chain_f16(exl3_ctx *ctx, const uint16_t *x, int64_t n, int K, uint16_t *packed,
+                     uint16_t *states, uint16_t *cost) {
+    if (n == 0) return EXL3_OK;
+    const size_t per_tile = exl3::bp_bytes_per_tile(K);
+    const size_t max_batch = ctx->scratch_limit / per_tile;
+    if (max_batch == 0)
+        return fail(ctx, EXL3_ENOMEM, "scratch limit %zu B is below one tile's %zu B",
+                    ctx->scratch_limit, per_tile);
+    int64_t batch = (int64_t)std::min<size_t>((size_t)n, max_batch);
+    if (batch < n && batch > ctx->n_cu) batch -= batch % ctx->n_cu;
+    int rc;
+    size_t bytes_cap = ctx->bp_cap;
+    char *bp = static_cast<char *>(ctx->d_bp);
+    if ((rc = ensure(ctx, bp, bytes_cap, (size_t)batch * per_tile)) != EXL3_OK) return rc;
+    ctx->d_bp = bp;
+    ctx->bp_cap = bytes_cap;
+    if ((rc = ensure_small(ctx, (size_t)batch)) != EXL3_OK) return rc;
+    uint16_t *cost_tmp = reinterpret_cast<uint16_t *>(ctx->d_cost);
+    for (int64_t i0 = 0; i0 < n; i0 += batch) {
+        const int64_t nb = std::min<int64_t>(batch, n - i0);
+        int id = open_timed(ctx, EXL3_KERNEL_FWD1, nb);
+        EXL3_HIP(ctx, exl3::launch_viterbi_fwd_f16(K, 1, x, i0, nb, ctx->d_levels, nullptr,
+                                                   ctx->d_bp, ctx->d_end, nullptr, ctx->stream));
+        close_timed(ctx, id);
+        id = open_timed(ctx, EXL3_KERNEL_TB1, nb);
+        EXL3_HIP(ctx, exl3::launch_traceback(K, 1, true, ctx->d_bp, nb, ctx->d_end, ctx->d_X,
+                                             nullptr, nullptr, 0, nullptr, 0.0f, nullptr,
+                                             nullptr, nullptr, nullptr, ctx->stream));
+        close_timed(ctx, id);
+        id = open_timed(ctx, EXL3_KERNEL_FWD2, nb);
+        EXL3_HIP(ctx, exl3::launch_viterbi_fwd_f16(K, 2, x, i0, nb, ctx->d_levels, ctx->d_X,
+                                                   ctx->d_bp, nullptr,
+                                                   cost ? cost + i0 : cost_tmp, ctx->stream));
+        close_timed(ctx, id);
+        id = open_timed(ctx, EXL3_KERNEL_TB2, nb);
+        EXL3_HIP(ctx, exl3::launch_traceback(K, 2, true, ctx->d_bp, nb, ctx->d_X, nullptr,
+                                             nullptr, nullptr, i0, ctx->d_levels, 0.0f, packed,
+                                             states, nullptr, nullptr, ctx->stream));
+        close_timed(ctx, id);
     }
     return EXL3_OK;
 }
@@ -383,6 +427,18 @@ int exl3_encode_tiles(exl3_ctx *ctx, const float *x, int64_t n, int K, float sca
     int rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
     return encode_chain(ctx, x, nullptr, n, K, scale, packed, states, tile_sse, nullptr, nullptr);
+}
+
+int exl3_encode_tiles_f16(exl3_ctx *ctx, const uint16_t *x, int64_t n, int K, uint16_t *packed,
+                          uint16_t *states, uint16_t *cost) {
+    if (!ctx) return EXL3_EINVAL;
+    if (!k_supported(K)) return fail(ctx, EXL3_EUNSUPPORTED, "K = %d (supported: 2, 3, 4)", K);
+    if (n < 0) return fail(ctx, EXL3_EINVAL, "n = %lld", (long long)n);
+    if (n > 0 && (!x || !packed)) return fail(ctx, EXL3_EINVAL, "null input or output");
+    if (n > (int64_t)INT32_MAX) return fail(ctx, EXL3_EINVAL, "too many tiles");
+    int rc;
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    return encode_chain_f16(ctx, x, n, K, packed, states, cost);
 }
 
 int exl3_decode_tiles(exl3_ctx *ctx, const uint16_t *packed, int64_t n, int K, float scale,

@@ -64,6 +64,49 @@ __host__ __device__ inline void bp_locate(uint32_t e, uint32_t &lane, uint32_t &
     }
 }
 
+// Binary16 mode of the forward kernel.  Costs, levels and inputs are IEEE
+// binary16; two tracked states share one 32-bit register (low and high half),
+// paired as outputs b and b + 1 of one butterfly, so a packed instruction
+// serves both.  Ownership (1024 lanes per tile, 64 states per lane):
+//   K=2: lane g owns the butterflies m = 2g + j + 2048 i (i, j < 2)
+//   K=3: m = g
+//   K=4: m = g >> 2 and the outputs b = 4 (g & 3) + 0..3
+// Index bits are built in both halves of a word by shift-and-insert at bit 15
+// (and 31), the low index bit first; a pair's K bits are contiguous with the
+// low bit lowest.  After a step each half holds PUSH bits in its top PUSH
+// positions; at K=4 the two used bytes are compacted into 16 bits.
+template <int K>
+struct GeoH {
+    static constexpr int Kr = 16 - K;
+    static constexpr int T = 1 << Kr;
+    static constexpr int NB = 1 << K;
+    static constexpr int MBITS = 16 - 2 * K;
+    static constexpr int NI = (K == 2) ? 2 : 1;       // butterfly groups per lane
+    static constexpr int NJ = (K == 2) ? 2 : 1;       // adjacent butterflies per group
+    static constexpr int NP = (K == 4) ? 2 : NB / 2;  // output pairs per butterfly and lane
+    static constexpr int PUSH = NI * NJ * NP * K;     // index bits per half-word and step
+    using bp_t = typename std::conditional<(K == 4), uint16_t, uint32_t>::type;
+    static_assert(NI * NJ * NP * 2 * NB == 64, "every lane owns 64 states");
+};
+
+template <int K>
+__host__ __device__ inline void bp_locate_h(uint32_t e, uint32_t &lane, uint32_t &bit) {
+    if (K == 2) {
+        uint32_t m = e >> 2, b = e & 3u;
+        uint32_t q = ((m >> 11) * 2u + (m & 1u)) * 2u + (b >> 1);
+        lane = (m & 2047u) >> 1;
+        bit = 16u * (b & 1u) + 2u * q;
+    } else if (K == 3) {
+        uint32_t b = e & 7u;
+        lane = e >> 3;
+        bit = 16u * (b & 1u) + 4u + 3u * (b >> 1);
+    } else {
+        uint32_t m = e >> 4, b = e & 15u, bl = b & 3u;
+        lane = (m << 2) | (b >> 2);
+        bit = 8u * (bl & 1u) + 4u * (bl >> 1);
+    }
+}
+
 // Bytes of backpointer scratch per tile in flight.
 inline size_t bp_bytes_per_tile(int K) {
     return (size_t)kSlots * kLanes * (K == 4 ? 2 : 4);
@@ -75,7 +118,13 @@ hipError_t launch_viterbi_fwd(int K, int pass, const float *x, const int32_t *ti
                               const uint16_t *X_in, void *bp, uint16_t *end_state,
                               float *cost_out, hipStream_t stream);
 
-hipError_t launch_traceback(int K, int pass, const void *bp, int64_t n,
+hipError_t launch_viterbi_fwd_f16(int K, int pass, const uint16_t *x, int64_t tile0, int64_t n,
+                                  const uint16_t *levels, const uint16_t *X_in, void *bp,
+                                  uint16_t *end_state, uint16_t *cost_out, hipStream_t stream);
+
+// f16 selects the binary16 kernel's backpointer layout; x, sse and w_hat are
+// then unused (the path cost comes from the forward pass).
+hipError_t launch_traceback(int K, int pass, bool f16, const void *bp, int64_t n,
                             const uint16_t *start_state, uint16_t *X_out, const float *x,
                             const int32_t *tile_idx, int64_t tile0, const uint16_t *levels,
                             float scale, uint16_t *packed, uint16_t *states, float *sse,

@@ -20,18 +20,23 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
-template <int K>
+// The binary32 and binary16 forward kernels lay their backpointer words out
+// differently (same word type and size); H selects the binary16 layout.
+template <int K, bool H>
 __device__ __forceinline__ uint32_t bp_read(const typename Geo<K>::bp_t *__restrict__ bp_tile,
                                             int slot, uint32_t e) {
     uint32_t lane, bit;
-    bp_locate<K>(e, lane, bit);
+    if (H)
+        bp_locate_h<K>(e, lane, bit);
+    else
+        bp_locate<K>(e, lane, bit);
     uint32_t w = bp_tile[(size_t)slot * kLanes + lane];
     return (w >> bit) & ((1u << K) - 1u);
 }
 
 // Pass 1: from the best final state of the rotated pass back to rotated step
 // 127 (original position 255); that state is X.
-template <int K>
+template <int K, bool H>
 __global__ void __launch_bounds__(kTbThreads)
 traceback1_kernel(const typename Geo<K>::bp_t *__restrict__ bp, int64_t n,
                   const uint16_t *__restrict__ end_state, uint16_t *__restrict__ X_out) {
@@ -42,15 +47,15 @@ traceback1_kernel(const typename Geo<K>::bp_t *__restrict__ bp, int64_t n,
     uint32_t s = end_state[b];
     for (int j = kSteps - 1; j >= kSteps / 2; --j) {
         uint32_t e = s >> K;
-        uint32_t k = bp_read<K>(bp_tile, (j - 1) - 127, e);
+        uint32_t k = bp_read<K, H>(bp_tile, (j - 1) - 127, e);
         s = (k << G::Kr) | e;
     }
     X_out[b] = (uint16_t)s;
 }
 
-// Pass 2: from X at step 255 back to step 0, then pack, dequantise and sum the
-// squared error of the tile in step order.
-template <int K>
+// Pass 2: from X at step 255 back to step 0, then pack, and (binary32 mode,
+// x given) dequantise and sum the squared error of the tile in step order.
+template <int K, bool H>
 __global__ void __launch_bounds__(kTbThreads)
 traceback2_kernel(const typename Geo<K>::bp_t *__restrict__ bp, int64_t n,
                   const uint16_t *__restrict__ X_in, const float *__restrict__ x,
@@ -70,7 +75,7 @@ traceback2_kernel(const typename Geo<K>::bp_t *__restrict__ bp, int64_t n,
     S[lt][kSteps - 1] = (uint16_t)s;
     for (int t = kSteps - 1; t >= 1; --t) {
         uint32_t e = s >> K;
-        uint32_t k = bp_read<K>(bp_tile, t - 1, e);
+        uint32_t k = bp_read<K, H>(bp_tile, t - 1, e);
         s = (k << G::Kr) | e;
         S[lt][t - 1] = (uint16_t)s;
     }
@@ -90,6 +95,10 @@ traceback2_kernel(const typename Geo<K>::bp_t *__restrict__ bp, int64_t n,
         }
     }
 
+    if (states_out)
+        for (int t = 0; t < kSteps; ++t) states_out[(size_t)tile * kSteps + t] = S[lt][t];
+    if (!x) return;
+
     // dequantise and sequential squared error (equals the search's path cost)
     const float *xt = x + (size_t)tile * kSteps;
     float sse = 0.0f;
@@ -100,7 +109,6 @@ traceback2_kernel(const typename Geo<K>::bp_t *__restrict__ bp, int64_t n,
         float q = d * d;
         sse = sse + q;
         if (w_hat) w_hat[(size_t)tile * kSteps + t] = v;
-        if (states_out) states_out[(size_t)tile * kSteps + t] = (uint16_t)st;
     }
     if (sse_out) sse_out[tile] = sse;
 }
@@ -133,7 +141,7 @@ gather_tiles_kernel(const float *__restrict__ src, const int32_t *__restrict__ i
     dst[(size_t)b * kSteps + t] = src[(size_t)idx[b] * kSteps + t];
 }
 
-template <int K>
+template <int K, bool H>
 hipError_t launch_tb_t(int pass, const void *bp, int64_t n, const uint16_t *start_state,
                        uint16_t *X_out, const float *x, const int32_t *tile_idx, int64_t tile0,
                        const uint16_t *levels, float scale, uint16_t *packed, uint16_t *states,
@@ -141,10 +149,10 @@ hipError_t launch_tb_t(int pass, const void *bp, int64_t n, const uint16_t *star
     using bp_t = typename Geo<K>::bp_t;
     const unsigned blocks = (unsigned)((n + kTbThreads - 1) / kTbThreads);
     if (pass == 1)
-        hipLaunchKernelGGL(traceback1_kernel<K>, dim3(blocks), dim3(kTbThreads), 0, stream,
+        hipLaunchKernelGGL((traceback1_kernel<K, H>), dim3(blocks), dim3(kTbThreads), 0, stream,
                            reinterpret_cast<const bp_t *>(bp), n, start_state, X_out);
     else
-        hipLaunchKernelGGL(traceback2_kernel<K>, dim3(blocks), dim3(kTbThreads), 0, stream,
+        hipLaunchKernelGGL((traceback2_kernel<K, H>), dim3(blocks), dim3(kTbThreads), 0, stream,
                            reinterpret_cast<const bp_t *>(bp), n, start_state, x, tile_idx,
                            tile0, levels, scale, packed, states, sse, w_hat);
     return hipGetLastError();
@@ -152,25 +160,33 @@ hipError_t launch_tb_t(int pass, const void *bp, int64_t n, const uint16_t *star
 
 }  // namespace
 
-hipError_t launch_traceback(int K, int pass, const void *bp, int64_t n,
+hipError_t launch_traceback(int K, int pass, bool f16, const void *bp, int64_t n,
                             const uint16_t *start_state, uint16_t *X_out, const float *x,
                             const int32_t *tile_idx, int64_t tile0, const uint16_t *levels,
                             float scale, uint16_t *packed, uint16_t *states, float *sse,
                             float *w_hat, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
+    if (f16) {
+        x = nullptr;
+        sse = nullptr;
+        w_hat = nullptr;
+    }
+#define EXL3_TB_CASE(KK)                                                                     \
+    case KK:                                                                                 \
+        return f16 ? launch_tb_t<KK, true>(pass, bp, n, start_state, X_out, x, tile_idx,     \
+                                           tile0, levels, scale, packed, states, sse, w_hat, \
+                                           stream)                                           \
+                   : launch_tb_t<KK, false>(pass, bp, n, start_state, X_out, x, tile_idx,    \
+                                            tile0, levels, scale, packed, states, sse,       \
+                                            w_hat, stream);
     switch (K) {
-        case 2:
-            return launch_tb_t<2>(pass, bp, n, start_state, X_out, x, tile_idx, tile0, levels,
-                                  scale, packed, states, sse, w_hat, stream);
-        case 3:
-            return launch_tb_t<3>(pass, bp, n, start_state, X_out, x, tile_idx, tile0, levels,
-                                  scale, packed, states, sse, w_hat, stream);
-        case 4:
-            return launch_tb_t<4>(pass, bp, n, start_state, X_out, x, tile_idx, tile0, levels,
-                                  scale, packed, states, sse, w_hat, stream);
+        EXL3_TB_CASE(2)
+        EXL3_TB_CASE(3)
+        EXL3_TB_CASE(4)
         default:
             return hipErrorInvalidValue;
     }
+#undef EXL3_TB_CASE
 }
 
 hipError_t launch_decode(const uint16_t *packed, int64_t n, int K, float scale,
