@@ -156,6 +156,39 @@ def cpu_baseline(m, K, scale, n_tiles, threads, sample_tiles):
     }
 
 
+def f16_mode(ctx, w, su, sv, scale, n_tiles, steps):
+    """Binary16-mode encode of every tile of the same matrix (regularized,
+    divided by the chosen scale, rounded to binary16; prepared outside the
+    timed region), for K = 2, 3, 4.  Rated like the binary32 path: the same
+    algorithmic operation count per tile over the forward kernel's own launch
+    time, against the same vector peak (a packed binary16 FMA does two lanes'
+    work per issue, as dual-issued binary32 does)."""
+    import torch
+    reg, _, _ = ctx.regularize(w, su, sv, 128)
+    xh = (reg / scale).to(torch.float16).contiguous()
+    del reg
+    res = {"workload": "the 4096x4096 matrix's 65,536 tiles as binary16 (regularized / scale)",
+           "tiles_per_s_by_K": {}, "fwd_frac_by_K": {}, "fwd_avg_launch_ms_by_K": {}}
+    for K in (2, 3, 4):
+        ctx.encode_tiles_f16(xh, K, want_states=False, want_cost=True)
+        torch.cuda.synchronize()
+        ctx.set_timing(True)
+        t0 = time.perf_counter()
+        for _ in range(max(1, steps // 2)):
+            ctx.encode_tiles_f16(xh, K, want_states=False, want_cost=True)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        f1 = ctx.read_timing("fwd1")
+        f2 = ctx.read_timing("fwd2")
+        ctx.set_timing(False)
+        ops = f1[2] * ops_per_pass(K, True) + f2[2] * ops_per_pass(K, False)
+        ach = ops / ((f1[0] + f2[0]) / 1000.0) / 1e12
+        res["tiles_per_s_by_K"][str(K)] = round(n_tiles * max(1, steps // 2) / dt, 1)
+        res["fwd_frac_by_K"][str(K)] = round(ach / PEAK_FP32_TFLOPS, 4)
+        res["fwd_avg_launch_ms_by_K"][str(K)] = round((f1[0] + f2[0]) / max(f1[1] + f2[1], 1), 4)
+    return res
+
+
 def run_steps(ctx, w, su, sv, K, gss, steps):
     import torch
     out = None
@@ -174,6 +207,8 @@ def main():
     ap.add_argument("--cpu-tiles", type=int, default=8192)
     ap.add_argument("--no-other-k", action="store_true",
                     help="skip the K=3 and K=4 runs on the same matrix")
+    ap.add_argument("--no-f16", action="store_true",
+                    help="skip the binary16-mode encode of the same matrix")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the forward kernel's HBM bytes per tile from two "
                          "rocprofv3 --pmc counter_collection.csv files and exit")
@@ -277,6 +312,8 @@ def main():
             by_k[str(k2)] = round(n_tiles * max(1, args.steps // 2)
                                   / (time.perf_counter() - t2), 1)
 
+    f16 = None if args.no_f16 else f16_mode(ctx, w, su, sv, out["scale"], n_tiles, args.steps)
+
     cpu = None
     if not args.no_cpu_baseline and rank == 0:
         threads = max(1, min(os.cpu_count() or 1, 16))
@@ -308,6 +345,7 @@ def main():
         "stages_ms_per_step": stages,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "f16_mode": f16,
     }
     if rank == 0:
         print(json.dumps(line), flush=True)

@@ -71,10 +71,13 @@ __host__ __device__ inline void bp_locate(uint32_t e, uint32_t &lane, uint32_t &
 //   K=2: lane g owns the butterflies m = 2g + j + 2048 i (i, j < 2)
 //   K=3: m = g
 //   K=4: m = g >> 2 and the outputs b = 4 (g & 3) + 0..3
-// Index bits are built in both halves of a word by shift-and-insert at bit 15
-// (and 31), the low index bit first; a pair's K bits are contiguous with the
-// low bit lowest.  After a step each half holds PUSH bits in its top PUSH
-// positions; at K=4 the two used bytes are compacted into 16 bits.
+// The lane's output pairs are numbered q in loop order (i, j, pair p).  Index
+// bit r of pair q, half h, comes out as a flag; the step word keeps flags in
+// byte-bit positions:
+//   K=2: bit 8h + q (r=0), 16 + 8h + q (r=1)
+//   K=3: bit 8h + q (r=0), 16 + 8h + q (r=1), 8h + 16 (q & 1) + 4 + (q >> 1) (r=2)
+//   K=4: (word compacted to 16 bits) 8h + 2q (r=0), 8h + 4 + 2q (r=1),
+//        8h + 2q + 1 (r=2), 8h + 4 + 2q + 1 (r=3)
 template <int K>
 struct GeoH {
     static constexpr int Kr = 16 - K;
@@ -84,26 +87,33 @@ struct GeoH {
     static constexpr int NI = (K == 2) ? 2 : 1;       // butterfly groups per lane
     static constexpr int NJ = (K == 2) ? 2 : 1;       // adjacent butterflies per group
     static constexpr int NP = (K == 4) ? 2 : NB / 2;  // output pairs per butterfly and lane
-    static constexpr int PUSH = NI * NJ * NP * K;     // index bits per half-word and step
     using bp_t = typename std::conditional<(K == 4), uint16_t, uint32_t>::type;
     static_assert(NI * NJ * NP * 2 * NB == 64, "every lane owns 64 states");
 };
 
+// Lane and bit positions (index bit 0 first) of tracked state e's
+// backpointer in a step's row of words of the binary16 kernel.
 template <int K>
-__host__ __device__ inline void bp_locate_h(uint32_t e, uint32_t &lane, uint32_t &bit) {
+__host__ __device__ inline void bp_locate_h(uint32_t e, uint32_t &lane, uint32_t (&bit)[K]) {
     if (K == 2) {
-        uint32_t m = e >> 2, b = e & 3u;
+        uint32_t m = e >> 2, b = e & 3u, h = b & 1u;
         uint32_t q = ((m >> 11) * 2u + (m & 1u)) * 2u + (b >> 1);
         lane = (m & 2047u) >> 1;
-        bit = 16u * (b & 1u) + 2u * q;
+        bit[0] = 8u * h + q;
+        bit[1] = 16u + 8u * h + q;
     } else if (K == 3) {
-        uint32_t b = e & 7u;
+        uint32_t b = e & 7u, h = b & 1u, q = b >> 1;
         lane = e >> 3;
-        bit = 16u * (b & 1u) + 4u + 3u * (b >> 1);
+        bit[0] = 8u * h + q;
+        bit[1] = 16u + 8u * h + q;
+        bit[K - 1] = 8u * h + 16u * (q & 1u) + 4u + (q >> 1);
     } else {
-        uint32_t m = e >> 4, b = e & 15u, bl = b & 3u;
+        uint32_t m = e >> 4, b = e & 15u, bl = b & 3u, h = bl & 1u, q = bl >> 1;
         lane = (m << 2) | (b >> 2);
-        bit = 8u * (bl & 1u) + 4u * (bl >> 1);
+        bit[0] = 8u * h + 2u * q;
+        bit[1] = 8u * h + 4u + 2u * q;
+        bit[2 % K] = 8u * h + 2u * q + 1u;
+        bit[3 % K] = 8u * h + 4u + 2u * q + 1u;
     }
 }
 

@@ -25,12 +25,19 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
 template <int K, bool H>
 __device__ __forceinline__ uint32_t bp_read(const typename Geo<K>::bp_t *__restrict__ bp_tile,
                                             int slot, uint32_t e) {
-    uint32_t lane, bit;
-    if (H)
+    uint32_t lane;
+    if (H) {
+        uint32_t bit[K];
         bp_locate_h<K>(e, lane, bit);
-    else
-        bp_locate<K>(e, lane, bit);
-    uint32_t w = bp_tile[(size_t)slot * kLanes + lane];
+        const uint32_t w = bp_tile[(size_t)slot * kLanes + lane];
+        uint32_t k = 0;
+#pragma unroll
+        for (int r = 0; r < K; ++r) k |= ((w >> bit[r]) & 1u) << r;
+        return k;
+    }
+    uint32_t bit;
+    bp_locate<K>(e, lane, bit);
+    const uint32_t w = bp_tile[(size_t)slot * kLanes + lane];
     return (w >> bit) & ((1u << K) - 1u);
 }
 

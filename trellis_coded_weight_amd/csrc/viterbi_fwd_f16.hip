@@ -24,11 +24,19 @@
 //                                       + (c_lo - m_lo + 0x7FFF)
 // with both digits in [0x7FFF, 0xFBFF] (no carry between the halves), so bit
 // 15 is [c_lo > m_lo] and bit 31 is [c_hi > m_hi].  A tournament walk over
-// these flag words picks the lowest index reaching the minimum: at each level
-// the minimum is in the right subtree exactly when the left subtree's minimum
-// exceeds it.  Walk selects and bit insertion are v_bitop3_b32 (and the flag
-// subtractions plain 32-bit integer ops), which gfx950 can dual-issue beside
-// the packed arithmetic.
+// these flag words (v_bitop3_b32 selects) picks the lowest index reaching the
+// minimum: at each level the minimum is in the right subtree exactly when the
+// left subtree's minimum exceeds it.  v_perm_b32 turns bits 15 and 31 of two
+// flag words into four 0x00 / 0xFF bytes, and one v_bitop3_b32 merges them
+// into one bit of each byte of the step's backpointer word: two instructions
+// per four index bits.
+//
+// On gfx950 the packed binary16 and min instructions issue at one per
+// 4-cycle slot per SIMD, and mixing them with dual-issue-capable 32-bit
+// operations was measured not to pair, so the kernel's cost is its
+// instruction count: per output pair at K = 2, 4 v_pk_add + 4 v_pk_fma + 2
+// minima, and in steps that keep backpointers 5 flag operations + 1 perm +
+// 1 merge.
 #include "exl3_internal.h"
 
 namespace exl3 {
@@ -39,9 +47,11 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
-// bitop3 truth tables (operands S0, S1, S2 <-> 0xF0, 0xCC, 0xAA)
-constexpr unsigned kSelS0ifS2elseS1 = 0xE4;  // S2 ? S0 : S1
-constexpr unsigned kInsert = 0xD8;           // S2 ? S1 : S0
+// bitop3 truth table (operands S0, S1, S2 <-> 0xF0, 0xCC, 0xAA): S2 ? S0 : S1
+constexpr unsigned kSel = 0xE4;
+// v_perm_b32 selectors 8..11 give a byte of copies of bit 15 / 31 of the low
+// source and bit 15 / 31 of the high source
+constexpr uint32_t kSignBytes = 0x0B0A0908u;
 
 // flag word of c against the pair minimum (see the header comment)
 __device__ __forceinline__ uint32_t flag(h2 c, uint32_t guard) { return u32(c) - guard; }
@@ -49,12 +59,14 @@ __device__ __forceinline__ uint32_t guard_of(h2 m) { return u32(m) + 0x80008001u
 
 // cond ? a : b, bitwise (only bits 15 and 31 matter)
 __device__ __forceinline__ uint32_t sel(uint32_t cond, uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_bitop3_b32(a, b, cond, kSelS0ifS2elseS1);
+    return __builtin_amdgcn_bitop3_b32(a, b, cond, kSel);
 }
 
-// acc = (acc >> 1) with bits 15 and 31 replaced by those of f
-__device__ __forceinline__ void push(uint32_t &acc, uint32_t f, uint32_t mask) {
-    acc = __builtin_amdgcn_bitop3_b32(acc >> 1, f, mask, kInsert);
+// Four flags -> bit `pos` of each byte of acc: byte 0 / 1 <- bit 15 / 31 of
+// lo, byte 2 / 3 <- bit 15 / 31 of hi.
+__device__ __forceinline__ void merge(uint32_t &acc, uint32_t hi, uint32_t lo, int pos) {
+    const uint32_t bytes = __builtin_amdgcn_perm(hi, lo, kSignBytes);
+    acc = __builtin_amdgcn_bitop3_b32(bytes, acc, 0x01010101u << pos, kSel);
 }
 
 __device__ __forceinline__ h2 hmin(h2 a, h2 b) { return __builtin_elementwise_min(a, b); }
@@ -62,22 +74,21 @@ __device__ __forceinline__ h2 hmin3(h2 a, h2 b, h2 c) {
     return __builtin_elementwise_minimum(__builtin_elementwise_minimum(a, b), c);
 }
 
-// Minimum over the 2^K candidate words of one output pair; with BITS, the K
-// index bits of both halves are inserted into acc (low bit first).
+// Minimum over the 2^K candidate words of one output pair; with BITS, the
+// flag words r[0..K-1] of the lowest index reaching it (r[j] carries index
+// bit j of both halves in bits 15 and 31).
 template <int K, bool BITS>
 struct AcsH;
 
 template <bool BITS>
 struct AcsH<2, BITS> {
-    static __device__ __forceinline__ h2 run(const h2 (&a)[4], uint32_t &acc, uint32_t mask) {
+    static __device__ __forceinline__ h2 run(const h2 (&a)[4], uint32_t (&r)[2]) {
         const h2 m01 = hmin(a[0], a[1]);
         const h2 m = hmin3(m01, a[2], a[3]);
         if (BITS) {
             const uint32_t gd = guard_of(m);
-            const uint32_t r1 = flag(m01, gd);                        // index in {2, 3}
-            const uint32_t r0 = sel(r1, flag(a[2], gd), flag(a[0], gd));
-            push(acc, r0, mask);
-            push(acc, r1, mask);
+            r[1] = flag(m01, gd);                                     // index in {2, 3}
+            r[0] = sel(r[1], flag(a[2], gd), flag(a[0], gd));
         }
         return m;
     }
@@ -85,7 +96,7 @@ struct AcsH<2, BITS> {
 
 template <bool BITS>
 struct AcsH<3, BITS> {
-    static __device__ __forceinline__ h2 run(const h2 (&a)[8], uint32_t &acc, uint32_t mask) {
+    static __device__ __forceinline__ h2 run(const h2 (&a)[8], uint32_t (&r)[3]) {
         const h2 m01 = hmin(a[0], a[1]);
         const h2 m45 = hmin(a[4], a[5]);
         const h2 m0123 = hmin3(m01, a[2], a[3]);
@@ -93,14 +104,11 @@ struct AcsH<3, BITS> {
         const h2 m = hmin(m0123, m4567);
         if (BITS) {
             const uint32_t gd = guard_of(m);
-            const uint32_t r2 = flag(m0123, gd);                      // index in 4..7
-            const uint32_t r1 = sel(r2, flag(m45, gd), flag(m01, gd));
-            const uint32_t lo = sel(r1, flag(a[2], gd), flag(a[0], gd));
-            const uint32_t hi = sel(r1, flag(a[6], gd), flag(a[4], gd));
-            const uint32_t r0 = sel(r2, hi, lo);
-            push(acc, r0, mask);
-            push(acc, r1, mask);
-            push(acc, r2, mask);
+            r[2] = flag(m0123, gd);                                   // index in 4..7
+            r[1] = sel(r[2], flag(m45, gd), flag(m01, gd));
+            const uint32_t lo = sel(r[1], flag(a[2], gd), flag(a[0], gd));
+            const uint32_t hi = sel(r[1], flag(a[6], gd), flag(a[4], gd));
+            r[0] = sel(r[2], hi, lo);
         }
         return m;
     }
@@ -108,7 +116,7 @@ struct AcsH<3, BITS> {
 
 template <bool BITS>
 struct AcsH<4, BITS> {
-    static __device__ __forceinline__ h2 run(const h2 (&a)[16], uint32_t &acc, uint32_t mask) {
+    static __device__ __forceinline__ h2 run(const h2 (&a)[16], uint32_t (&r)[4]) {
         const h2 m01 = hmin(a[0], a[1]);
         const h2 m45 = hmin(a[4], a[5]);
         const h2 m89 = hmin(a[8], a[9]);
@@ -121,22 +129,18 @@ struct AcsH<4, BITS> {
         const h2 m = hmin3(m0_7, m8_11, m12_15);
         if (BITS) {
             const uint32_t gd = guard_of(m);
-            const uint32_t r3 = flag(m0_7, gd);                       // index in 8..15
-            const uint32_t r2 = sel(r3, flag(m8_11, gd), flag(m0_3, gd));
-            const uint32_t qlo = sel(r2, flag(m45, gd), flag(m01, gd));
-            const uint32_t qhi = sel(r2, flag(mCD, gd), flag(m89, gd));
-            const uint32_t r1 = sel(r3, qhi, qlo);
-            const uint32_t p0 = sel(r1, flag(a[2], gd), flag(a[0], gd));
-            const uint32_t p1 = sel(r1, flag(a[6], gd), flag(a[4], gd));
-            const uint32_t p2 = sel(r1, flag(a[10], gd), flag(a[8], gd));
-            const uint32_t p3 = sel(r1, flag(a[14], gd), flag(a[12], gd));
-            const uint32_t h0 = sel(r2, p1, p0);
-            const uint32_t h1 = sel(r2, p3, p2);
-            const uint32_t r0 = sel(r3, h1, h0);
-            push(acc, r0, mask);
-            push(acc, r1, mask);
-            push(acc, r2, mask);
-            push(acc, r3, mask);
+            r[3] = flag(m0_7, gd);                                    // index in 8..15
+            r[2] = sel(r[3], flag(m8_11, gd), flag(m0_3, gd));
+            const uint32_t qlo = sel(r[2], flag(m45, gd), flag(m01, gd));
+            const uint32_t qhi = sel(r[2], flag(mCD, gd), flag(m89, gd));
+            r[1] = sel(r[3], qhi, qlo);
+            const uint32_t p0 = sel(r[1], flag(a[2], gd), flag(a[0], gd));
+            const uint32_t p1 = sel(r[1], flag(a[6], gd), flag(a[4], gd));
+            const uint32_t p2 = sel(r[1], flag(a[10], gd), flag(a[8], gd));
+            const uint32_t p3 = sel(r[1], flag(a[14], gd), flag(a[12], gd));
+            const uint32_t h0 = sel(r[2], p1, p0);
+            const uint32_t h1 = sel(r[2], p3, p2);
+            r[0] = sel(r[3], h1, h0);
         }
         return m;
     }
@@ -187,10 +191,12 @@ __device__ __forceinline__ h2 bcast(uint32_t w, int j) {
     return (K == 2 && j == 1) ? h2{v.y, v.y} : h2{v.x, v.x};
 }
 
+// Backpointer word of a step (layout documented with bp_read_h): the flags of
+// the lane's output pairs, merged a byte-bit at a time.
 template <int K, bool BITS>
 __device__ __forceinline__ uint32_t step_h(
     h2 xt, const uint16_t *__restrict__ Mc, uint16_t *__restrict__ Mn,
-    const h2 (&v)[GeoH<K>::NI][GeoH<K>::NJ][GeoH<K>::NB][GeoH<K>::NP], int g, uint32_t mask) {
+    const h2 (&v)[GeoH<K>::NI][GeoH<K>::NJ][GeoH<K>::NB][GeoH<K>::NP], int g) {
     using G = GeoH<K>;
     uint32_t Mw[G::NI][G::NB];
 #pragma unroll
@@ -198,6 +204,7 @@ __device__ __forceinline__ uint32_t step_h(
 #pragma unroll
         for (int k = 0; k < G::NB; ++k) Mw[i][k] = read_m<K>(Mc, g, i, k);
     uint32_t acc = 0;
+    uint32_t r2prev = 0;
 #pragma unroll
     for (int i = 0; i < G::NI; ++i) {
         uint32_t out[G::NJ * G::NP];
@@ -211,7 +218,23 @@ __device__ __forceinline__ uint32_t step_h(
                     const h2 d = xt - v[i][j][k][p];
                     a[k] = __builtin_elementwise_fma(d, d, bcast<K>(Mw[i][k], j));
                 }
-                out[j * G::NP + p] = u32(AcsH<K, BITS>::run(a, acc, mask));
+                uint32_t r[K];
+                out[j * G::NP + p] = u32(AcsH<K, BITS>::run(a, r));
+                if (BITS) {
+                    const int q = (i * G::NJ + j) * G::NP + p;     // pair index in the lane
+                    if (K == 2) {
+                        merge(acc, r[1], r[0], q);
+                    } else if (K == 3) {
+                        merge(acc, r[1], r[0], q);
+                        if (q & 1)
+                            merge(acc, r[2], r2prev, 4 + (q >> 1));
+                        else
+                            r2prev = r[2];
+                    } else {
+                        merge(acc, r[1], r[0], 2 * q);
+                        merge(acc, r[3], r[2], 2 * q + 1);
+                    }
+                }
             }
         uint16_t *dst = Mn + write_index<K>(g, i);
         if constexpr (G::NJ * G::NP == 4)
@@ -219,12 +242,20 @@ __device__ __forceinline__ uint32_t step_h(
         else
             *reinterpret_cast<uint2 *>(dst) = make_uint2(out[0], out[1]);
     }
-    if (K == 4) acc = ((acc >> 8) & 0xFFu) | ((acc >> 16) & 0xFF00u);
+    if (K == 4) acc = (acc & 0x0F0Fu) | ((acc >> 12) & 0xF0F0u);
     return acc;
 }
 
+// At K = 2 and 3 the kernel fits in 64 registers per lane (8 waves per SIMD),
+// so two tiles' workgroups share a compute unit and one computes while the
+// other waits at its step barrier; K = 4 needs more registers and runs one.
+template <int K>
+struct WavesPerSimd {
+    static constexpr int v = (K == 4) ? 1 : 8;
+};
+
 template <int K, int PASS>
-__global__ void __launch_bounds__(kLanes, 1)
+__global__ void __launch_bounds__(kLanes, WavesPerSimd<K>::v)
 viterbi_fwd_f16_kernel(const uint16_t *__restrict__ x, int64_t tile0,
                        const uint16_t *__restrict__ levels, const uint16_t *__restrict__ X_in,
                        typename GeoH<K>::bp_t *__restrict__ bp, uint16_t *__restrict__ end_state,
@@ -244,10 +275,6 @@ viterbi_fwd_f16_kernel(const uint16_t *__restrict__ x, int64_t tile0,
         const uint32_t h = x[tile * kSteps + ((PASS == 1) ? ((g + 128) & 255) : g)];
         xs[g] = h | (h << 16);
     }
-
-    // insertion mask, kept in a vector register so the bitop3 inserts can pair
-    uint32_t mask;
-    asm volatile("v_mov_b32 %0, 0x80008000" : "=v"(mask));
 
     // levels of the lane's 64 states: adjacent states, one word per pair
     h2 v[G::NI][G::NJ][G::NB][G::NP];
@@ -276,28 +303,28 @@ viterbi_fwd_f16_kernel(const uint16_t *__restrict__ x, int64_t tile0,
     if constexpr (PASS == 1) {
         for (; t + 1 < t_first; t += 2) {           // steps 0..125 in pairs
             const h2 xn = as_h2(xs[t + 1]);
-            step_h<K, false>(xt, B0, B1, v, g, mask);
+            step_h<K, false>(xt, B0, B1, v, g);
             __syncthreads();
             xt = as_h2(xs[t + 2]);
-            step_h<K, false>(xn, B1, B0, v, g, mask);
+            step_h<K, false>(xn, B1, B0, v, g);
             __syncthreads();
         }
         {                                           // step 126: B0 -> B1
             const h2 xn = as_h2(xs[t + 1]);
-            step_h<K, false>(xt, B0, B1, v, g, mask);
+            step_h<K, false>(xt, B0, B1, v, g);
             __syncthreads();
             xt = xn;
             ++t;
         }
         for (; t < kSteps - 1; t += 2) {            // steps 127..254: B1 -> B0 -> B1
             const h2 xn = as_h2(xs[t + 1]);
-            uint32_t w = step_h<K, true>(xt, B1, B0, v, g, mask);
+            uint32_t w = step_h<K, true>(xt, B1, B0, v, g);
             bp_tile[(size_t)(t - t_first) * kLanes + g] = (bp_t)w;
             __syncthreads();
             xt = xn;
             if (t + 1 < kSteps - 1) {
                 xt = as_h2(xs[t + 2]);
-                w = step_h<K, true>(xn, B0, B1, v, g, mask);
+                w = step_h<K, true>(xn, B0, B1, v, g);
                 bp_tile[(size_t)(t + 1 - t_first) * kLanes + g] = (bp_t)w;
                 __syncthreads();
             }
@@ -305,13 +332,13 @@ viterbi_fwd_f16_kernel(const uint16_t *__restrict__ x, int64_t tile0,
     } else {
         for (; t < kSteps - 1; t += 2) {            // steps 0..254: B0 -> B1 -> B0
             const h2 xn = as_h2(xs[t + 1]);
-            uint32_t w = step_h<K, true>(xt, B0, B1, v, g, mask);
+            uint32_t w = step_h<K, true>(xt, B0, B1, v, g);
             bp_tile[(size_t)t * kLanes + g] = (bp_t)w;
             __syncthreads();
             xt = xn;
             if (t + 1 < kSteps - 1) {
                 xt = as_h2(xs[t + 2]);
-                w = step_h<K, true>(xn, B1, B0, v, g, mask);
+                w = step_h<K, true>(xn, B1, B0, v, g);
                 bp_tile[(size_t)(t + 1) * kLanes + g] = (bp_t)w;
                 __syncthreads();
             }
