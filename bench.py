@@ -280,10 +280,13 @@ def main():
     achieved = fwd_ops / fwd_s / 1e12
     traffic = None
     per = load_traffic(K)
-    if per and "pass1" in per and "pass2" in per:
-        t1 = per["pass1"]["fetch_bytes_per_tile"] + per["pass1"]["write_bytes_per_tile"]
-        t2 = per["pass2"]["fetch_bytes_per_tile"] + per["pass2"]["write_bytes_per_tile"]
-        traffic = (t1 * f1_tiles + t2 * f2_tiles) / max(f1_n + f2_n, 1)
+    if per and all(p in per for p in ("pass1", "pass2", "pass3")):
+        def tb(p):
+            return per[p]["fetch_bytes_per_tile"] + per[p]["write_bytes_per_tile"]
+        # the pass-2 timing records include the scale-search probes' cost-only form
+        probe_tiles = gss_encodes * args.steps
+        traffic = (tb("pass1") * f1_tiles + tb("pass2") * (f2_tiles - probe_tiles)
+                   + tb("pass3") * probe_tiles) / max(f1_n + f2_n, 1)
     roofline = {
         "bound": "alu",
         "achieved": round(achieved, 3),
@@ -291,7 +294,8 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
         "traffic": traffic,
-        "kernel": "viterbi_fwd_kernel<K=2> (passes 1 and 2)",
+        "kernel": "viterbi_fwd_kernel<K=2> (pass 1, pass 2, and pass 2's cost-only form in the "
+                  "scale-search probes)",
         "launches": f1_n + f2_n,
         "avg_launch_ms": round((f1_ms + f2_ms) / max(f1_n + f2_n, 1), 4),
         "avg_tiles_per_launch": round((f1_tiles + f2_tiles) / max(f1_n + f2_n, 1), 1),

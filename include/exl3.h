@@ -188,7 +188,8 @@ int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, in
 /* Kernel kinds for exl3_ctx_read_timing. */
 enum {
     EXL3_KERNEL_FWD1 = 0,        /* forward pass 1 (rotated input, free start) */
-    EXL3_KERNEL_FWD2 = 1,        /* forward pass 2 (start pinned to X) */
+    EXL3_KERNEL_FWD2 = 1,        /* forward pass 2 (start pinned to X); in the
+                                    scale search, its cost-only form */
     EXL3_KERNEL_TB1 = 2,         /* traceback to X */
     EXL3_KERNEL_TB2 = 3,         /* traceback, packing, squared error */
     EXL3_KERNEL_REGULARIZE = 4

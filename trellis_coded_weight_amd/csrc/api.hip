@@ -192,7 +192,8 @@ int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, i
                                              nullptr, nullptr, ctx->stream));
         close_timed(ctx, id);
         id = open_timed(ctx, EXL3_KERNEL_FWD2, nb);
-        EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 2, x, idx_b, i0, nb, ctx->d_levels, scale,
+        EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, cost_only ? 3 : 2, x, idx_b, i0, nb,
+                                               ctx->d_levels, scale,
                                                ctx->d_X, ctx->d_bp, nullptr,
                                                cost_only ? cost_only + i0 : ctx->d_cost,
                                                ctx->stream));

@@ -22,6 +22,8 @@
 //   pass 2: input in order, only tracked index X & (2^Kr - 1) admitted at the
 //           start (cost 0, others +inf); backpointers for steps 0..254;
 //           result: C_255[X] -> cost_out (the path's squared error).
+//   pass 3: pass 2 without backpointers, for callers that need only the path
+//           cost (scale-search probes).
 #include "exl3_internal.h"
 
 #include <math.h>
@@ -352,6 +354,18 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
                 __syncthreads();
             }
         }
+    } else if constexpr (PASS == 3) {
+        for (; t < kSteps - 1; t += 2) {            // steps 0..254, no backpointers
+            const float xn = xs[t + 1];
+            trellis_step<K, false>(xt, B0, B1, v, m, b0);
+            __syncthreads();
+            xt = xn;
+            if (t + 1 < kSteps - 1) {
+                xt = xs[t + 2];
+                trellis_step<K, false>(xn, B1, B0, v, m, b0);
+                __syncthreads();
+            }
+        }
     } else {
         for (; t < kSteps - 1; t += 2) {            // steps 0..254: B0 -> B1 -> B0
             const float xn = xs[t + 1];
@@ -456,10 +470,12 @@ hipError_t launch_viterbi_fwd(int K, int pass, const float *x, const int32_t *ti
                               float *cost_out, hipStream_t stream) {
 #define EXL3_FWD_CASE(KK)                                                                    \
     case KK:                                                                                 \
-        return pass == 1 ? launch_fwd_t<KK, 1>(x, tile_idx, tile0, n, levels, scale, X_in, bp, \
-                                                end_state, cost_out, stream)                 \
-                         : launch_fwd_t<KK, 2>(x, tile_idx, tile0, n, levels, scale, X_in, bp, \
-                                                end_state, cost_out, stream);
+        return pass == 1   ? launch_fwd_t<KK, 1>(x, tile_idx, tile0, n, levels, scale, X_in, bp, \
+                                                  end_state, cost_out, stream)                 \
+               : pass == 2 ? launch_fwd_t<KK, 2>(x, tile_idx, tile0, n, levels, scale, X_in, bp, \
+                                                  end_state, cost_out, stream)                 \
+                           : launch_fwd_t<KK, 3>(x, tile_idx, tile0, n, levels, scale, X_in, bp, \
+                                                  end_state, cost_out, stream);
     switch (K) {
         EXL3_FWD_CASE(2)
         EXL3_FWD_CASE(3)
