@@ -47,7 +47,7 @@ def _check(ctx, xh, K, tag):
     assert np.array_equal(_u16(cost), want["cost"])
 
 
-@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
 def test_f16_encode_bit_exact(ctx, K):
     _check(ctx, _half_tiles(21, 300 + K), K, "gaussian")
 

@@ -150,21 +150,21 @@ def test_f16_forward_min_equals_bruteforce(Q, K, L):
         assert C[s] == sel.min()            # binary16 bits of non-negatives order as integers
 
 
-@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
 def test_f16_scalar_quantiser_case(K):
     """A codebook that depends only on the low K bits makes every step's choice free.
 
     Binary16 rounding is monotone in both operands of the fused update, so the path that
-    takes the nearest level at every step (exact arithmetic) reaches the minimum
-    accumulated cost; the encoder must report exactly that cost, and its own state
-    sequence must accumulate to it (it may differ from the greedy one where rounding
-    absorbs a difference and the lowest-index rule picks another branch)."""
+    takes the nearest level at every step (exact arithmetic) reaches the least accumulated
+    cost of all paths: the unconstrained forward pass must find exactly that minimum.  The
+    two-pass encode may do worse (its closure fixes the last steps from pass 1's path, and
+    where rounding absorbed a difference pass 1's tie rule can pick a level that pass 2 then
+    pays for), never better, and its reported cost is its own path's accumulated cost."""
     rng = np.random.default_rng(10 + K)
     lev = np.sort(rng.standard_normal(1 << K)).astype(np.float16)
     lbits = lev.view(np.uint16)
     c = lbits[np.arange(1 << 16) & ((1 << K) - 1)]
     x = np.float16(rng.standard_normal((1, 256))).view(np.uint16)
-    states, X, cost = oracle.encode_sequences_f16(x, K, c)
     xf = x.view(np.float16).astype(np.float64)[0]
     greedy = np.argmin((xf[:, None] - lev.astype(np.float64)[None, :]) ** 2, axis=1)
 
@@ -175,11 +175,14 @@ def test_f16_scalar_quantiser_case(K):
         return acc
 
     best = accumulate(greedy)
-    assert int(cost[0]) == best
-    assert accumulate(states[0] & ((1 << K) - 1)) == best
+    C, _ = oracle.forward_f16(x[0], 16, K, c, np.zeros(1 << (16 - K), np.uint16))
+    assert int(C.min()) == best
+    states, X, cost = oracle.encode_sequences_f16(x, K, c)
+    assert accumulate(states[0] & ((1 << K) - 1)) == int(cost[0])
+    assert int(cost[0]) >= best
 
 
-@pytest.mark.parametrize("K", [2, 4])
+@pytest.mark.parametrize("K", [1, 2, 4])
 def test_f16_ring_and_cost(K):
     x = np.float16(np.random.default_rng(K).standard_normal((2, 256))).view(np.uint16)
     r = oracle.encode_tiles_f16(x, K)

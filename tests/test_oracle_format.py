@@ -42,7 +42,7 @@ def test_pack_matches_string_packer(K):
     assert np.array_equal(oracle.unpack_states(got[None, :], K)[0], states)
 
 
-@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
 def test_pack_closed_forms(K):
     ones = np.full((1, 256), 0xFFFF, np.int64)
     assert np.all(oracle.pack_states(ones, K) == 0xFFFF)

@@ -149,7 +149,7 @@ def _ring_ok(states, K, Q=16):
     return bool(ok)
 
 
-@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
 def test_production_ring_and_cost_identity(K):
     x = np.random.default_rng(K).standard_normal((3, 256)).astype(np.float32)
     levels = oracle.mul1_levels_fp16()
@@ -166,7 +166,7 @@ def test_production_ring_and_cost_identity(K):
     assert np.array_equal(oracle.unpack_states(words, K), states)
 
 
-@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
 def test_scalar_quantiser_special_case(K):
     """Levels that depend only on the newest K bits: the trellis is a scalar quantiser."""
     rng = np.random.default_rng(50 + K)

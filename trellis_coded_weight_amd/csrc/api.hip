@@ -104,7 +104,7 @@ int set_device(exl3_ctx *ctx) {
     return EXL3_OK;
 }
 
-bool k_supported(int K) { return K >= 2 && K <= 4; }
+bool k_supported(int K) { return K >= 1 && K <= 4; }
 
 void clear_timing(exl3_ctx *ctx) {
     for (auto &r : ctx->timed) {
@@ -420,7 +420,7 @@ int exl3_regularize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int col
 int exl3_encode_tiles(exl3_ctx *ctx, const float *x, int64_t n, int K, float scale,
                       uint16_t *packed, uint16_t *states, float *tile_sse) {
     if (!ctx) return EXL3_EINVAL;
-    if (!k_supported(K)) return fail(ctx, EXL3_EUNSUPPORTED, "K = %d (supported: 2, 3, 4)", K);
+    if (!k_supported(K)) return fail(ctx, EXL3_EUNSUPPORTED, "K = %d (supported: 1, 2, 3, 4)", K);
     if (n < 0) return fail(ctx, EXL3_EINVAL, "n = %lld", (long long)n);
     if (n > 0 && (!x || !packed)) return fail(ctx, EXL3_EINVAL, "null input or output");
     if (!std::isfinite(scale)) return fail(ctx, EXL3_EINVAL, "scale is not finite");
@@ -433,7 +433,7 @@ int exl3_encode_tiles(exl3_ctx *ctx, const float *x, int64_t n, int K, float sca
 int exl3_encode_tiles_f16(exl3_ctx *ctx, const uint16_t *x, int64_t n, int K, uint16_t *packed,
                           uint16_t *states, uint16_t *cost) {
     if (!ctx) return EXL3_EINVAL;
-    if (!k_supported(K)) return fail(ctx, EXL3_EUNSUPPORTED, "K = %d (supported: 2, 3, 4)", K);
+    if (!k_supported(K)) return fail(ctx, EXL3_EUNSUPPORTED, "K = %d (supported: 1, 2, 3, 4)", K);
     if (n < 0) return fail(ctx, EXL3_EINVAL, "n = %lld", (long long)n);
     if (n > 0 && (!x || !packed)) return fail(ctx, EXL3_EINVAL, "null input or output");
     if (n > (int64_t)INT32_MAX) return fail(ctx, EXL3_EINVAL, "too many tiles");
@@ -464,7 +464,7 @@ int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, in
     int rc;
     if ((rc = check_matrix_args(ctx, w, w_dtype, rows, cols, had_block, su, sv)) != EXL3_OK)
         return rc;
-    if (!k_supported(K)) return fail(ctx, EXL3_EUNSUPPORTED, "K = %d (supported: 2, 3, 4)", K);
+    if (!k_supported(K)) return fail(ctx, EXL3_EUNSUPPORTED, "K = %d (supported: 1, 2, 3, 4)", K);
     if (!packed || !scale_out) return fail(ctx, EXL3_EINVAL, "null output");
     if (gss) {
         if (gss->iters < 1 || gss->iters > 64 || !(gss->lo > 0.0) || !(gss->hi > gss->lo) ||

@@ -14,13 +14,14 @@
 // write the new minima M'[(m << K) | b].  A workgroup of 1024 lanes owns one
 // tile; every lane owns 64 states for the whole pass, so their levels
 // v = rn(scale * c) stay in registers:
+//   K=1: 16384 butterflies of 4 states; lane g owns m = g + 1024*i, i < 16
 //   K=2: 4096 butterflies of 16 states; lane g owns m = g + 1024*i, i < 4
 //   K=3: 1024 butterflies of 64 states; lane g owns m = g
 //   K=4:  256 butterflies of 256 states; lane g owns m = g >> 2 and the four
 //         values b = 4*(g & 3) + 0..3
 // Backpointers (the winning k of every tracked state, K bits) are packed per
-// lane per step into one word: 32 bits at K=2 and 24 at K=3 (uint32), 16 at
-// K=4 (uint16).  The lane appends its tracked states in the order
+// lane per step into one word: 32 bits at K=1 and 2, 24 at K=3 (uint32), 16
+// at K=4 (uint16).  The lane appends its tracked states in the order
 // n = i * BPL + bb, high bit first, so state n's k sits at bit
 // K * (GPL * BPL - 1 - n).
 #pragma once
@@ -40,7 +41,7 @@ struct Geo {
     static constexpr int T = 1 << Kr;             // tracked minima
     static constexpr int NB = 1 << K;             // branches per tracked state
     static constexpr int MBITS = 16 - 2 * K;      // butterfly index bits
-    static constexpr int GPL = (K == 2) ? 4 : 1;  // butterflies per lane
+    static constexpr int GPL = (K == 1) ? 16 : (K == 2) ? 4 : 1;  // butterflies per lane
     static constexpr int BPL = (K == 4) ? 4 : NB; // b values per lane per butterfly
     static constexpr int SPL = GPL * NB * BPL;    // states per lane (64)
     using bp_t = typename std::conditional<(K == 4), uint16_t, uint32_t>::type;
@@ -50,10 +51,11 @@ struct Geo {
 // Lane and bit of tracked state e's backpointer inside a step's row of words.
 template <int K>
 __host__ __device__ inline void bp_locate(uint32_t e, uint32_t &lane, uint32_t &bit) {
-    if (K == 2) {
-        uint32_t m = e >> 2, bb = e & 3u;
+    if (K <= 2) {
+        constexpr uint32_t bpl = 1u << K, n_e = 32u / K;
+        uint32_t m = e >> K, bb = e & (bpl - 1u);
         lane = m & 1023u;
-        bit = 2u * (15u - (4u * (m >> 10) + bb));
+        bit = K * (n_e - 1u - (bpl * (m >> 10) + bb));
     } else if (K == 3) {
         lane = e >> 3;
         bit = 3u * (7u - (e & 7u));
@@ -68,12 +70,14 @@ __host__ __device__ inline void bp_locate(uint32_t e, uint32_t &lane, uint32_t &
 // binary16; two tracked states share one 32-bit register (low and high half),
 // paired as outputs b and b + 1 of one butterfly, so a packed instruction
 // serves both.  Ownership (1024 lanes per tile, 64 states per lane):
+//   K=1: lane g owns the butterflies m = 2g + j + 2048 i (i < 8, j < 2)
 //   K=2: lane g owns the butterflies m = 2g + j + 2048 i (i, j < 2)
 //   K=3: m = g
 //   K=4: m = g >> 2 and the outputs b = 4 (g & 3) + 0..3
 // The lane's output pairs are numbered q in loop order (i, j, pair p).  Index
 // bit r of pair q, half h, comes out as a flag; the step word keeps flags in
 // byte-bit positions:
+//   K=1: bit 16 (q & 1) + 8h + (q >> 1)
 //   K=2: bit 8h + q (r=0), 16 + 8h + q (r=1)
 //   K=3: bit 8h + q (r=0), 16 + 8h + q (r=1), 8h + 16 (q & 1) + 4 + (q >> 1) (r=2)
 //   K=4: (word compacted to 16 bits) 8h + 2q (r=0), 8h + 4 + 2q (r=1),
@@ -84,8 +88,8 @@ struct GeoH {
     static constexpr int T = 1 << Kr;
     static constexpr int NB = 1 << K;
     static constexpr int MBITS = 16 - 2 * K;
-    static constexpr int NI = (K == 2) ? 2 : 1;       // butterfly groups per lane
-    static constexpr int NJ = (K == 2) ? 2 : 1;       // adjacent butterflies per group
+    static constexpr int NI = (K == 1) ? 8 : (K == 2) ? 2 : 1;  // butterfly groups per lane
+    static constexpr int NJ = (K <= 2) ? 2 : 1;       // adjacent butterflies per group
     static constexpr int NP = (K == 4) ? 2 : NB / 2;  // output pairs per butterfly and lane
     using bp_t = typename std::conditional<(K == 4), uint16_t, uint32_t>::type;
     static_assert(NI * NJ * NP * 2 * NB == 64, "every lane owns 64 states");
@@ -95,23 +99,28 @@ struct GeoH {
 // backpointer in a step's row of words of the binary16 kernel.
 template <int K>
 __host__ __device__ inline void bp_locate_h(uint32_t e, uint32_t &lane, uint32_t (&bit)[K]) {
-    if (K == 2) {
+    if (K == 1) {
+        uint32_t m = e >> 1, h = e & 1u;
+        uint32_t q = (m >> 11) * 2u + (m & 1u);
+        lane = (m & 2047u) >> 1;
+        bit[0] = 16u * (q & 1u) + 8u * h + (q >> 1);
+    } else if (K == 2) {
         uint32_t m = e >> 2, b = e & 3u, h = b & 1u;
         uint32_t q = ((m >> 11) * 2u + (m & 1u)) * 2u + (b >> 1);
         lane = (m & 2047u) >> 1;
         bit[0] = 8u * h + q;
-        bit[1] = 16u + 8u * h + q;
+        bit[1 % K] = 16u + 8u * h + q;
     } else if (K == 3) {
         uint32_t b = e & 7u, h = b & 1u, q = b >> 1;
         lane = e >> 3;
         bit[0] = 8u * h + q;
-        bit[1] = 16u + 8u * h + q;
-        bit[K - 1] = 8u * h + 16u * (q & 1u) + 4u + (q >> 1);
+        bit[1 % K] = 16u + 8u * h + q;
+        bit[2 % K] = 8u * h + 16u * (q & 1u) + 4u + (q >> 1);
     } else {
         uint32_t m = e >> 4, b = e & 15u, bl = b & 3u, h = bl & 1u, q = bl >> 1;
         lane = (m << 2) | (b >> 2);
         bit[0] = 8u * h + 2u * q;
-        bit[1] = 8u * h + 4u + 2u * q;
+        bit[1 % K] = 8u * h + 4u + 2u * q;
         bit[2 % K] = 8u * h + 2u * q + 1u;
         bit[3 % K] = 8u * h + 4u + 2u * q + 1u;
     }

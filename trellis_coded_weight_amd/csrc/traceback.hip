@@ -187,6 +187,7 @@ hipError_t launch_traceback(int K, int pass, bool f16, const void *bp, int64_t n
                                             tile0, levels, scale, packed, states, sse,       \
                                             w_hat, stream);
     switch (K) {
+        EXL3_TB_CASE(1)
         EXL3_TB_CASE(2)
         EXL3_TB_CASE(3)
         EXL3_TB_CASE(4)

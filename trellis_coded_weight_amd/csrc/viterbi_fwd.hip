@@ -47,7 +47,7 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
 template <int K>
 __device__ __forceinline__ void lane_butterflies(int g, int (&m)[Geo<K>::GPL], int &b0) {
     using G = Geo<K>;
-    if (K == 2) {
+    if (K <= 2) {
 #pragma unroll
         for (int i = 0; i < G::GPL; ++i) m[i] = g + kLanes * i;
         b0 = 0;
@@ -67,6 +67,11 @@ __device__ __forceinline__ void lane_butterflies(int g, int (&m)[Geo<K>::GPL], i
 // insertions of one update form a single asm block.
 template <int K>
 __device__ __forceinline__ void push_bits(uint32_t &acc, const uint64_t (&kb)[K]);
+template <>
+__device__ __forceinline__ void push_bits<1>(uint32_t &acc, const uint64_t (&kb)[1]) {
+    uint64_t c0;
+    asm("v_addc_co_u32_e64 %0, %1, %0, %0, %2" : "+v"(acc), "=&s"(c0) : "s"(kb[0]));
+}
 template <>
 __device__ __forceinline__ void push_bits<2>(uint32_t &acc, const uint64_t (&kb)[2]) {
     uint64_t c0, c1;
@@ -105,6 +110,16 @@ __device__ __forceinline__ void push_bits<4>(uint32_t &acc, const uint64_t (&kb)
 // the next left child.  No scalar instructions are involved.
 template <int K>
 struct Acs;
+
+template <>
+struct Acs<1> {
+    static __device__ __forceinline__ float run(const float (&a)[2], uint32_t &acc) {
+        const float m = __builtin_fminf(a[0], a[1]);
+        const uint64_t kb[1] = {__builtin_amdgcn_ballot_w64(a[0] > m)};
+        push_bits<1>(acc, kb);
+        return m;
+    }
+};
 
 template <>
 struct Acs<2> {
@@ -180,6 +195,7 @@ struct Acs<4> {
 // Minimum of the 2^K candidates only (steps whose backpointers are not kept).
 template <int NB>
 __device__ __forceinline__ float min_only(const float (&a)[NB]) {
+    if constexpr (NB == 2) return __builtin_fminf(a[0], a[1]);
     float r = __builtin_fminf(__builtin_fminf(a[0], a[1]), a[2]);
 #pragma unroll
     for (int j = 3; j + 1 < NB; j += 2) r = __builtin_fminf(__builtin_fminf(r, a[j]), a[j + 1]);
@@ -205,6 +221,9 @@ __device__ __forceinline__ uint32_t trellis_step(
     for (int i = 0; i < G::GPL; ++i)
 #pragma unroll
         for (int k = 0; k < G::NB; ++k) Mk[i][k] = Mc[(k << G::MBITS) | m[i]];
+    // K = 1 keeps a single buffer of tracked minima (128 KiB): every lane has
+    // read its predecessors before any lane overwrites them
+    if constexpr (K == 1) __syncthreads();
     uint32_t bits = 0;
     if constexpr (BITS && K == 2) {
         constexpr int NE = G::GPL * G::BPL;
@@ -265,10 +284,14 @@ __device__ __forceinline__ uint32_t trellis_step(
                 outv[bb] = BITS ? Acs<K>::run(a, bits) : min_only<G::NB>(a);
             }
             float *dst = Mn + ((m[i] << K) | b0);
+            if constexpr (G::BPL == 2) {
+                *reinterpret_cast<float2 *>(dst) = make_float2(outv[0], outv[1]);
+            } else {
 #pragma unroll
-            for (int q4 = 0; q4 < G::BPL; q4 += 4)
-                *reinterpret_cast<float4 *>(dst + q4) =
-                    make_float4(outv[q4], outv[q4 + 1], outv[q4 + 2], outv[q4 + 3]);
+                for (int q4 = 0; q4 < G::BPL; q4 += 4)
+                    *reinterpret_cast<float4 *>(dst + q4) =
+                        make_float4(outv[q4], outv[q4 + 1], outv[q4 + 2], outv[q4 + 3]);
+            }
         }
     }
     return bits;
@@ -282,7 +305,8 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
                    uint16_t *__restrict__ end_state, float *__restrict__ cost_out) {
     using G = Geo<K>;
     using bp_t = typename G::bp_t;
-    __shared__ float Mbuf[2][G::T];
+    constexpr int NBUF = (K == 1) ? 1 : 2;          // K = 1: one 128 KiB buffer
+    __shared__ float Mbuf[NBUF][G::T];
     __shared__ float xs[kSteps];
     __shared__ float red_cost[kLanes / 64];
     __shared__ uint32_t red_state[kLanes / 64];
@@ -322,7 +346,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
     // backpointers only from step 127 on (odd), pass 2 from step 0.
     constexpr int t_first = (PASS == 1) ? 127 : 0;
     float *const B0 = Mbuf[0];
-    float *const B1 = Mbuf[1];
+    float *const B1 = Mbuf[NBUF - 1];
     float xt = xs[0];
     int t = 0;
     if constexpr (PASS == 1) {
@@ -384,7 +408,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
 
     // last step: costs of all states, no minimum over predecessors
     xt = xs[kSteps - 1];
-    const float *Mc = Mbuf[(kSteps - 1) & 1];
+    const float *Mc = Mbuf[((kSteps - 1) & 1) % NBUF];
     if (PASS == 1) {
         float best = 0.0f;
         uint32_t best_s = 0xFFFFFFFFu;
@@ -477,6 +501,7 @@ hipError_t launch_viterbi_fwd(int K, int pass, const float *x, const int32_t *ti
                            : launch_fwd_t<KK, 3>(x, tile_idx, tile0, n, levels, scale, X_in, bp, \
                                                   end_state, cost_out, stream);
     switch (K) {
+        EXL3_FWD_CASE(1)
         EXL3_FWD_CASE(2)
         EXL3_FWD_CASE(3)
         EXL3_FWD_CASE(4)

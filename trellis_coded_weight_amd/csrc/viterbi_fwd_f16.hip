@@ -81,6 +81,15 @@ template <int K, bool BITS>
 struct AcsH;
 
 template <bool BITS>
+struct AcsH<1, BITS> {
+    static __device__ __forceinline__ h2 run(const h2 (&a)[2], uint32_t (&r)[1]) {
+        const h2 m = hmin(a[0], a[1]);
+        if (BITS) r[0] = flag(a[0], guard_of(m));                  // index 1
+        return m;
+    }
+};
+
+template <bool BITS>
 struct AcsH<2, BITS> {
     static __device__ __forceinline__ h2 run(const h2 (&a)[4], uint32_t (&r)[2]) {
         const h2 m01 = hmin(a[0], a[1]);
@@ -150,13 +159,14 @@ struct AcsH<4, BITS> {
 // for branch k, and of the outputs it writes.
 template <int K>
 __device__ __forceinline__ int read_index(int g, int i, int k) {
+    if (K == 1) return (k << 14) | (2 * g + 2048 * i);
     if (K == 2) return (k << 12) | (2 * g + 2048 * i);
     if (K == 3) return (k << 10) | g;
     return (k << 8) | (g >> 2);
 }
 template <int K>
 __device__ __forceinline__ int write_index(int g, int i) {
-    if (K == 2) return (2 * g + 2048 * i) << 2;
+    if (K <= 2) return (2 * g + 2048 * i) << K;
     if (K == 3) return g << 3;
     return 4 * g;
 }
@@ -165,7 +175,7 @@ template <int K>
 __device__ __forceinline__ uint32_t state_of(int g, int i, int j, int k, int p) {
     using G = GeoH<K>;
     uint32_t m, b;
-    if (K == 2) {
+    if (K <= 2) {
         m = 2 * g + j + 2048 * i;
         b = 2 * p;
     } else if (K == 3) {
@@ -182,13 +192,13 @@ __device__ __forceinline__ uint32_t state_of(int g, int i, int j, int k, int p) 
 // group's two adjacent butterflies; K=3, 4: the value sits in the low half).
 template <int K>
 __device__ __forceinline__ uint32_t read_m(const uint16_t *Mc, int g, int i, int k) {
-    if (K == 2) return *reinterpret_cast<const uint32_t *>(Mc + read_index<K>(g, i, k));
+    if (K <= 2) return *reinterpret_cast<const uint32_t *>(Mc + read_index<K>(g, i, k));
     return Mc[read_index<K>(g, i, k)];
 }
 template <int K>
 __device__ __forceinline__ h2 bcast(uint32_t w, int j) {
     const h2 v = as_h2(w);
-    return (K == 2 && j == 1) ? h2{v.y, v.y} : h2{v.x, v.x};
+    return (K <= 2 && j == 1) ? h2{v.y, v.y} : h2{v.x, v.x};
 }
 
 // Backpointer word of a step (layout documented with bp_read_h): the flags of
@@ -222,17 +232,22 @@ __device__ __forceinline__ uint32_t step_h(
                 out[j * G::NP + p] = u32(AcsH<K, BITS>::run(a, r));
                 if (BITS) {
                     const int q = (i * G::NJ + j) * G::NP + p;     // pair index in the lane
-                    if (K == 2) {
-                        merge(acc, r[1], r[0], q);
-                    } else if (K == 3) {
-                        merge(acc, r[1], r[0], q);
+                    if (K == 1) {
                         if (q & 1)
-                            merge(acc, r[2], r2prev, 4 + (q >> 1));
+                            merge(acc, r[0], r2prev, q >> 1);
                         else
-                            r2prev = r[2];
+                            r2prev = r[0];
+                    } else if (K == 2) {
+                        merge(acc, r[1 % K], r[0], q);
+                    } else if (K == 3) {
+                        merge(acc, r[1 % K], r[0], q);
+                        if (q & 1)
+                            merge(acc, r[2 % K], r2prev, 4 + (q >> 1));
+                        else
+                            r2prev = r[2 % K];
                     } else {
-                        merge(acc, r[1], r[0], 2 * q);
-                        merge(acc, r[3], r[2], 2 * q + 1);
+                        merge(acc, r[1 % K], r[0], 2 * q);
+                        merge(acc, r[3 % K], r[2 % K], 2 * q + 1);
                     }
                 }
             }
@@ -248,10 +263,11 @@ __device__ __forceinline__ uint32_t step_h(
 
 // At K = 2 and 3 the kernel fits in 64 registers per lane (8 waves per SIMD),
 // so two tiles' workgroups share a compute unit and one computes while the
-// other waits at its step barrier; K = 4 needs more registers and runs one.
+// other waits at its step barrier; K = 4 needs more registers, and K = 1's
+// tracked minima (2 x 64 KiB) leave LDS for one workgroup.
 template <int K>
 struct WavesPerSimd {
-    static constexpr int v = (K == 4) ? 1 : 8;
+    static constexpr int v = (K == 2 || K == 3) ? 8 : 1;
 };
 
 template <int K, int PASS>
@@ -421,6 +437,7 @@ hipError_t launch_viterbi_fwd_f16(int K, int pass, const uint16_t *x, int64_t ti
                          : launch_t<KK, 2>(x, tile0, n, levels, X_in, bp, end_state,        \
                                            cost_out, stream);
     switch (K) {
+        EXL3_FWDH_CASE(1)
         EXL3_FWDH_CASE(2)
         EXL3_FWDH_CASE(3)
         EXL3_FWDH_CASE(4)
