@@ -60,6 +60,47 @@ __device__ __forceinline__ void lane_butterflies(int g, int (&m)[Geo<K>::GPL], i
     }
 }
 
+// The scaled levels v = rn(scale * c) of the lane's 64 states.  K = 2..4 keep
+// them as binary32 registers.  K = 1 needs 32 more registers for the
+// predecessor costs it snapshots (single LDS buffer), so it keeps the binary16
+// code values two per register and forms v in each step with one
+// v_fma_mix_f32 (the binary16 operand converts exactly, the product with the
+// binary32 scale is rounded once: the same v).
+template <int K>
+struct Levels {
+    using G = Geo<K>;
+    float v[G::GPL][G::NB][G::BPL];
+    __device__ __forceinline__ void set(int i, int k, int bb, uint16_t c, float scale) {
+        v[i][k][bb] = scale * half_bits_to_float(c);
+    }
+    __device__ __forceinline__ float at(int i, int k, int bb) const { return v[i][k][bb]; }
+};
+
+template <>
+struct Levels<1> {
+    using G = Geo<1>;
+    uint32_t h[G::GPL][G::NB];   // code values of b = 0 (low half) and b = 1 (high half)
+    float scale;
+    __device__ __forceinline__ void set(int i, int k, int bb, uint16_t c, float s) {
+        scale = s;
+        if (bb == 0)
+            h[i][k] = c;
+        else
+            h[i][k] |= (uint32_t)c << 16;
+    }
+    __device__ __forceinline__ float at(int i, int k, int bb) const {
+        // volatile: recomputed where used, never hoisted out of the step loop
+        float r;
+        if (bb == 0)
+            asm volatile("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]"
+                         : "=v"(r) : "v"(h[i][k]), "v"(scale));
+        else
+            asm volatile("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+                         : "=v"(r) : "v"(h[i][k]), "v"(scale));
+        return r;
+    }
+};
+
 // Append one bit per lane to acc: acc = 2 * acc + mask[lane] in one VALU op
 // (add with carry-in taken from the 64-bit lane mask).
 // The carry-outs go to scratch scalar pairs that nothing reads (writing VCC
@@ -214,7 +255,7 @@ __device__ __forceinline__ float min_only(const float (&a)[NB]) {
 template <int K, bool BITS>
 __device__ __forceinline__ uint32_t trellis_step(
     float xt, const float *__restrict__ Mc, float *__restrict__ Mn,
-    const float (&v)[Geo<K>::GPL][Geo<K>::NB][Geo<K>::BPL], const int (&m)[Geo<K>::GPL], int b0) {
+    const Levels<K> &lv, const int (&m)[Geo<K>::GPL], int b0) {
     using G = Geo<K>;
     float Mk[G::GPL][G::NB];
 #pragma unroll
@@ -236,7 +277,7 @@ __device__ __forceinline__ uint32_t trellis_step(
                 const int i = e / G::BPL, bb = e % G::BPL;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    float d = xt - v[i][k][bb];
+                    float d = xt - lv.at(i, k, bb);
                     float q = d * d;
                     a[k] = Mk[i][k] + q;
                 }
@@ -277,7 +318,7 @@ __device__ __forceinline__ uint32_t trellis_step(
                 float a[G::NB];
 #pragma unroll
                 for (int k = 0; k < G::NB; ++k) {
-                    float d = xt - v[i][k][bb];
+                    float d = xt - lv.at(i, k, bb);
                     float q = d * d;
                     a[k] = Mk[i][k] + q;
                 }
@@ -323,7 +364,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
     lane_butterflies<K>(g, m, b0);
 
     // levels of the lane's 64 states, scaled once per pass
-    float v[G::GPL][G::NB][G::BPL];
+    Levels<K> lv;
 #pragma unroll
     for (int i = 0; i < G::GPL; ++i)
 #pragma unroll
@@ -331,7 +372,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
 #pragma unroll
             for (int bb = 0; bb < G::BPL; ++bb) {
                 uint32_t s = ((uint32_t)k << G::Kr) | ((uint32_t)m[i] << K) | (uint32_t)(b0 + bb);
-                v[i][k][bb] = scale * half_bits_to_float(levels[s]);
+                lv.set(i, k, bb, levels[s], scale);
             }
 
     const uint32_t xm = (PASS == 1) ? 0u : ((uint32_t)X_in[b] & (uint32_t)(G::T - 1));
@@ -352,28 +393,28 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
     if constexpr (PASS == 1) {
         for (; t + 1 < t_first; t += 2) {           // steps 0..125 in pairs
             const float xn = xs[t + 1];
-            trellis_step<K, false>(xt, B0, B1, v, m, b0);
+            trellis_step<K, false>(xt, B0, B1, lv, m, b0);
             __syncthreads();
             xt = xs[t + 2];
-            trellis_step<K, false>(xn, B1, B0, v, m, b0);
+            trellis_step<K, false>(xn, B1, B0, lv, m, b0);
             __syncthreads();
         }
         {                                           // step 126: B0 -> B1
             const float xn = xs[t + 1];
-            trellis_step<K, false>(xt, B0, B1, v, m, b0);
+            trellis_step<K, false>(xt, B0, B1, lv, m, b0);
             __syncthreads();
             xt = xn;
             ++t;
         }
         for (; t < kSteps - 1; t += 2) {            // steps 127..254: B1 -> B0 -> B1
             const float xn = xs[t + 1];
-            uint32_t w = trellis_step<K, true>(xt, B1, B0, v, m, b0);
+            uint32_t w = trellis_step<K, true>(xt, B1, B0, lv, m, b0);
             bp_tile[(size_t)(t - t_first) * kLanes + g] = (bp_t)w;
             __syncthreads();
             xt = xn;
             if (t + 1 < kSteps - 1) {
                 xt = xs[t + 2];
-                w = trellis_step<K, true>(xn, B0, B1, v, m, b0);
+                w = trellis_step<K, true>(xn, B0, B1, lv, m, b0);
                 bp_tile[(size_t)(t + 1 - t_first) * kLanes + g] = (bp_t)w;
                 __syncthreads();
             }
@@ -381,25 +422,25 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
     } else if constexpr (PASS == 3) {
         for (; t < kSteps - 1; t += 2) {            // steps 0..254, no backpointers
             const float xn = xs[t + 1];
-            trellis_step<K, false>(xt, B0, B1, v, m, b0);
+            trellis_step<K, false>(xt, B0, B1, lv, m, b0);
             __syncthreads();
             xt = xn;
             if (t + 1 < kSteps - 1) {
                 xt = xs[t + 2];
-                trellis_step<K, false>(xn, B1, B0, v, m, b0);
+                trellis_step<K, false>(xn, B1, B0, lv, m, b0);
                 __syncthreads();
             }
         }
     } else {
         for (; t < kSteps - 1; t += 2) {            // steps 0..254: B0 -> B1 -> B0
             const float xn = xs[t + 1];
-            uint32_t w = trellis_step<K, true>(xt, B0, B1, v, m, b0);
+            uint32_t w = trellis_step<K, true>(xt, B0, B1, lv, m, b0);
             bp_tile[(size_t)t * kLanes + g] = (bp_t)w;
             __syncthreads();
             xt = xn;
             if (t + 1 < kSteps - 1) {
                 xt = xs[t + 2];
-                w = trellis_step<K, true>(xn, B1, B0, v, m, b0);
+                w = trellis_step<K, true>(xn, B1, B0, lv, m, b0);
                 bp_tile[(size_t)(t + 1) * kLanes + g] = (bp_t)w;
                 __syncthreads();
             }
@@ -419,7 +460,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
                 float mk = Mc[(k << G::MBITS) | m[i]];
 #pragma unroll
                 for (int bb = 0; bb < G::BPL; ++bb) {
-                    float d = xt - v[i][k][bb];
+                    float d = xt - lv.at(i, k, bb);
                     float q = d * d;
                     float c = mk + q;
                     uint32_t s = ((uint32_t)k << G::Kr) | ((uint32_t)m[i] << K) | (uint32_t)(b0 + bb);
@@ -466,7 +507,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
                 for (int bb = 0; bb < G::BPL; ++bb) {
                     uint32_t s = ((uint32_t)k << G::Kr) | ((uint32_t)m[i] << K) | (uint32_t)(b0 + bb);
                     if (s == X) {
-                        float d = xt - v[i][k][bb];
+                        float d = xt - lv.at(i, k, bb);
                         float q = d * d;
                         cost_out[b] = mk + q;
                     }
