@@ -201,6 +201,8 @@ def pack_states(states, K):
     """[n, 256] states -> [n, 16*K] uint16 words (MSB-first stream, then SWAP16)."""
     states = np.asarray(states, dtype=np.int64)
     n, L = states.shape
+    if n == 0:
+        return np.zeros((0, (L * K) // 16), np.uint16)
     b = states & ((1 << K) - 1)
     # stream bit j = bit (K-1-(j mod K)) of b_(j div K)
     shifts = np.arange(K - 1, -1, -1)
@@ -425,6 +427,69 @@ def quantize_matrix(w, su, sv, K, had_block=128, gss=(12, 0.5, 2.0), fixed_scale
         for e in r["sse"].tolist():
             total += float(e)
         out["mse"] = total / (R * C)
+    return out
+
+
+# --------------------------------------------------------------------------
+# LDLQ error feedback  [P1 item 3: one-sided block LDLQ, bottom-up span
+# traversal, additive target correction from the strictly lower L blocks]
+# --------------------------------------------------------------------------
+def ldlq(w_reg, L, K, scale, levels=None, threads=None):
+    """Quantize the regularized matrix span by span with LDLQ error feedback.
+
+    Readings (listed in the design notes): H = L D L^T over the columns, L unit
+    block-lower-triangular with 16x16 blocks (only the blocks below the
+    diagonal are read); spans are 16-column tile columns, processed from the
+    last to the first; the target of span j is
+        T_j = W_j + sum_{i > j} E_i L_ij,   E_i = W_i - What_i   (binary32),
+    accumulated per element in the order i ascending, then row t of the block
+    ascending, each product and each sum rounded on its own; span j's tiles are
+    then encoded at the fixed scale and What_j = v[states].
+    Returns dict(what [R, C], targets [R, C], states [TR*TC, 256] in tile order,
+    packed [TR*TC, 16K], err: per tile sequential binary32 sum of (W - What)^2).
+    """
+    W = np.asarray(w_reg, dtype=np.float32)
+    L = np.asarray(L, dtype=np.float32)
+    R, C = W.shape
+    TR, TC = R // 16, C // 16
+    if levels is None:
+        levels = mul1_levels_fp16()
+    v = scaled_levels(levels, scale)
+    what = np.empty((R, C), np.float32)
+    E = np.empty((R, C), np.float32)
+    targets = np.empty((R, C), np.float32)
+    states = np.empty((TR, TC, 256), np.int32)
+    for j in range(TC - 1, -1, -1):
+        cj = slice(16 * j, 16 * j + 16)
+        T = W[:, cj].copy()
+        for i in range(j + 1, TC):
+            for t in range(16):
+                col = 16 * i + t
+                T = T + E[:, col:col + 1] * L[col:col + 1, cj]
+        targets[:, cj] = T
+        r = encode_tiles(to_tiles(T), K, scale, levels, threads)
+        states[:, j, :] = r["states"]
+        what[:, cj] = from_tiles(v[r["states"]], R, 16)
+        E[:, cj] = W[:, cj] - what[:, cj]
+    st = states.reshape(TR * TC, 256)
+    return {"what": what, "targets": targets, "states": st,
+            "packed": pack_states(st, K), "err": tile_sse(to_tiles(W), st, v)}
+
+
+def quantize_matrix_ldlq(w, su, sv, K, L, had_block=128, gss=(12, 0.5, 2.0), fixed_scale=1.0,
+                         levels=None, threads=None):
+    """Regularize, choose the scale exactly as quantize_matrix does (on the
+    matrix without feedback), then run ldlq at that scale."""
+    base = quantize_matrix(w, su, sv, K, had_block, gss, fixed_scale, levels, threads,
+                           tiles_subset=np.zeros(0, np.int64))
+    R, C = np.asarray(w).shape
+    w_reg = from_tiles(base["tiles"], R, C)
+    out = ldlq(w_reg, L, K, base["scale"], levels, threads)
+    total = 0.0
+    for e in out["err"].tolist():
+        total += float(e)
+    out.update({"scale": base["scale"], "rms": base["rms"], "w_reg": w_reg,
+                "mse": total / (R * C)})
     return out
 
 

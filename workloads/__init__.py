@@ -121,3 +121,21 @@ def random_tiles(n: int, seed: int, std: float = 1.0) -> np.ndarray:
     """n tile inputs [n, 256] of i.i.d. N(0, std^2) in float32."""
     r = np.random.Generator(np.random.PCG64(seed))
     return (r.standard_normal((n, 256)) * std).astype(np.float32)
+
+
+def ldl_factor(cols: int, seed: int, off_std: float = 1.0):
+    """A synthetic block LDL factorisation H = L D L^T of an input-side Hessian.
+
+    L [cols, cols] float32: identity 16x16 diagonal blocks, i.i.d.
+    N(0, off_std^2 / cols) entries in the blocks below the diagonal, zeros above.
+    D [cols/16, 16, 16] float64: symmetric positive definite blocks A A^T / 16 + 0.1 I.
+    Drawn directly (no Hessian is factorised), seeded with PCG64(seed)."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    nb = cols // 16
+    L = (r.standard_normal((cols, cols)) * (off_std / math.sqrt(cols))).astype(np.float32)
+    blk = np.arange(cols) // 16
+    L[blk[:, None] <= blk[None, :]] = 0.0
+    L[np.arange(cols), np.arange(cols)] = 1.0
+    A = r.standard_normal((nb, 16, 16))
+    D = A @ A.transpose(0, 2, 1) / 16.0 + 0.1 * np.eye(16)[None]
+    return L, D
