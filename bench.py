@@ -189,6 +189,37 @@ def f16_mode(ctx, w, su, sv, scale, n_tiles, steps):
     return res
 
 
+def ldlq_mode(ctx, m, w, su, sv, steps):
+    """The same matrix through exl3_quantize_matrix_ldlq at K = 2 with a synthetic
+    block LDL factor of the input-side Hessian (workloads.ldl_factor, drawn once
+    and uploaded outside the timed region): scale search, then 256 spans of 256
+    tiles quantized from the last to the first with error feedback."""
+    import numpy as np
+    import torch
+    import workloads
+    R, C = m.w.shape
+    L, _ = workloads.ldl_factor(C, 2102)
+    Ld = torch.from_numpy(L).to(w.device)
+    out = ctx.quantize_matrix_ldlq(w, 2, su, sv, Ld, gss=m.gss)
+    torch.cuda.synchronize()
+    n = max(1, steps // 2)
+    ctx.set_timing(True)
+    t0 = time.perf_counter()
+    for _ in range(n):
+        out = ctx.quantize_matrix_ldlq(w, 2, su, sv, Ld, gss=m.gss)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    f1 = ctx.read_timing("fwd1")
+    f2 = ctx.read_timing("fwd2")
+    ctx.set_timing(False)
+    tiles = (R // 16) * (C // 16)
+    return {"workload": "the same 4096x4096 matrix, K=2, golden-section scale, LDLQ over 256 "
+                        "spans with a synthetic block LDL factor (off-diagonal N(0, 1/4096))",
+            "tiles_per_s": round(tiles * n / dt, 1), "ms_per_step": round(1000.0 * dt / n, 3),
+            "mse": out["mse"], "scale": out["scale"],
+            "fwd_ms_per_step": round((f1[0] + f2[0]) / n, 3)}
+
+
 def run_steps(ctx, w, su, sv, K, gss, steps):
     import torch
     out = None
@@ -207,6 +238,8 @@ def main():
     ap.add_argument("--cpu-tiles", type=int, default=8192)
     ap.add_argument("--no-other-k", action="store_true",
                     help="skip the K=3 and K=4 runs on the same matrix")
+    ap.add_argument("--no-ldlq", action="store_true",
+                    help="skip the LDLQ (error feedback) run on the same matrix")
     ap.add_argument("--no-f16", action="store_true",
                     help="skip the binary16-mode encode of the same matrix")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -317,6 +350,7 @@ def main():
                                   / (time.perf_counter() - t2), 1)
 
     f16 = None if args.no_f16 else f16_mode(ctx, w, su, sv, out["scale"], n_tiles, args.steps)
+    ldlq = None if args.no_ldlq else ldlq_mode(ctx, m, w, su, sv, args.steps)
 
     cpu = None
     if not args.no_cpu_baseline and rank == 0:
@@ -350,6 +384,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "f16_mode": f16,
+        "ldlq_mode": ldlq,
     }
     if rank == 0:
         print(json.dumps(line), flush=True)

@@ -185,6 +185,32 @@ int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, in
                          const exl3_gss *gss, float fixed_scale, uint16_t *packed,
                          float *scale_out, double *mse_out, float *w_hat, float *tile_sse);
 
+/*
+ * Whole-matrix quantization with LDLQ error feedback [P1 section 3: one-sided
+ * block LDLQ].  Regularization and the scale exactly as exl3_quantize_matrix
+ * (the scale is chosen on the matrix without feedback); then the 16-column
+ * tile spans are quantized from the last to the first, span j at the target
+ *     T_j = W_j + sum_{i > j} (W_i - What_i) L_ij
+ * (W the regularized matrix, L_ij the 16x16 block of L at rows 16i.., columns
+ * 16j..), summed per element over i ascending, then the block row ascending,
+ * each product and sum rounded to binary32 on its own.
+ *   L        float [cols][cols] row-major, device: unit block-lower-triangular
+ *            factor of H = L D L^T over the regularized columns; only the
+ *            blocks below the diagonal are read
+ *   packed, scale_out, w_hat : as exl3_quantize_matrix
+ *   mse_out  optional HOST double [1]: binary64 ascending sum over tiles of
+ *            tile_err, / (rows*cols)
+ *   tile_err optional float [tiles]: per tile, the sequential binary32 sum of
+ *            (W - What)^2 (squared error against the weight, not the target)
+ * Synchronizes the stream.  Errors: as exl3_quantize_matrix; EXL3_EINVAL for a
+ * null L.
+ */
+int exl3_quantize_matrix_ldlq(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
+                              int K, int had_block, const float *su, const float *sv,
+                              const exl3_gss *gss, float fixed_scale, const float *L,
+                              uint16_t *packed, float *scale_out, double *mse_out, float *w_hat,
+                              float *tile_err);
+
 /* Kernel kinds for exl3_ctx_read_timing. */
 enum {
     EXL3_KERNEL_FWD1 = 0,        /* forward pass 1 (rotated input, free start) */

@@ -43,6 +43,16 @@ struct exl3_ctx {
     float *d_sse = nullptr;
     size_t sse_cap = 0;
     int *d_flag = nullptr;
+    // LDLQ: error of the quantized spans (tile-major), one span's target,
+    // dequantized values and container words
+    float *d_err_tiles = nullptr;
+    size_t err_tiles_cap = 0;
+    float *d_span_target = nullptr;
+    size_t span_target_cap = 0;
+    float *d_span_what = nullptr;
+    size_t span_what_cap = 0;
+    uint16_t *d_span_packed = nullptr;
+    size_t span_packed_cap = 0;
     std::string err;
     // optional per-launch timing (HIP events on the context's stream)
     struct Timed {
@@ -324,8 +334,10 @@ void exl3_ctx_destroy(exl3_ctx *ctx) {
     (void)hipSetDevice(ctx->device);
     (void)hipStreamSynchronize(ctx->stream);
     clear_timing(ctx);
-    void *bufs[] = {ctx->d_levels, ctx->d_bp, ctx->d_end, ctx->d_X,   ctx->d_cost,
-                    ctx->d_idx,    ctx->d_wreg, ctx->d_sumsq, ctx->d_sse, ctx->d_flag};
+    void *bufs[] = {ctx->d_levels,      ctx->d_bp,          ctx->d_end,         ctx->d_X,
+                    ctx->d_cost,        ctx->d_idx,         ctx->d_wreg,        ctx->d_sumsq,
+                    ctx->d_sse,         ctx->d_flag,        ctx->d_err_tiles,   ctx->d_span_target,
+                    ctx->d_span_what,   ctx->d_span_packed};
     for (void *p : bufs)
         if (p) (void)hipFree(p);
     delete ctx;
@@ -456,10 +468,17 @@ int exl3_decode_tiles(exl3_ctx *ctx, const uint16_t *packed, int64_t n, int K, f
     return EXL3_OK;
 }
 
-int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols, int K,
-                         int had_block, const float *su, const float *sv, const exl3_gss *gss,
-                         float fixed_scale, uint16_t *packed, float *scale_out, double *mse_out,
-                         float *w_hat, float *tile_sse) {
+}  // extern "C"
+
+namespace {
+
+// Validation, regularization (tile-major, into the context), statistics and the
+// scale (fixed or golden-section search on the tile sample): the common front
+// of the whole-matrix calls.
+int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
+                                int K, int had_block, const float *su, const float *sv,
+                                const exl3_gss *gss, float fixed_scale, uint16_t *packed,
+                                float *scale_out, float *scale_chosen) {
     if (!ctx) return EXL3_EINVAL;
     int rc;
     if ((rc = check_matrix_args(ctx, w, w_dtype, rows, cols, had_block, su, sv)) != EXL3_OK)
@@ -577,6 +596,24 @@ int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, in
         }
     }
 
+    *scale_chosen = scale;
+    return EXL3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols, int K,
+                         int had_block, const float *su, const float *sv, const exl3_gss *gss,
+                         float fixed_scale, uint16_t *packed, float *scale_out, double *mse_out,
+                         float *w_hat, float *tile_sse) {
+    float scale = 0.0f;
+    int rc = regularize_and_choose_scale(ctx, w, w_dtype, rows, cols, K, had_block, su, sv, gss,
+                                         fixed_scale, packed, scale_out, &scale);
+    if (rc != EXL3_OK) return rc;
+    const int64_t ntiles = (int64_t)(rows / 16) * (cols / 16);
+    const size_t nel = (size_t)rows * cols;
     // 4. final encode of every tile at the chosen scale
     float *sse_dev = tile_sse;
     if (!sse_dev) {
@@ -593,6 +630,58 @@ int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, in
         EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
         double tot = 0.0;
         for (int64_t i = 0; i < ntiles; ++i) tot += (double)sse[(size_t)i];
+        *mse_out = tot / (double)nel;
+    }
+    EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    *scale_out = scale;
+    return EXL3_OK;
+}
+
+int exl3_quantize_matrix_ldlq(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
+                              int K, int had_block, const float *su, const float *sv,
+                              const exl3_gss *gss, float fixed_scale, const float *L,
+                              uint16_t *packed, float *scale_out, double *mse_out, float *w_hat,
+                              float *tile_err) {
+    if (!ctx) return EXL3_EINVAL;
+    if (!L) return fail(ctx, EXL3_EINVAL, "null factor L");
+    float scale = 0.0f;
+    int rc = regularize_and_choose_scale(ctx, w, w_dtype, rows, cols, K, had_block, su, sv, gss,
+                                         fixed_scale, packed, scale_out, &scale);
+    if (rc != EXL3_OK) return rc;
+    const int TR = rows / 16, TC = cols / 16;
+    const int64_t ntiles = (int64_t)TR * TC;
+    const size_t nel = (size_t)rows * cols;
+    if ((rc = ensure(ctx, ctx->d_err_tiles, ctx->err_tiles_cap, nel)) != EXL3_OK) return rc;
+    if ((rc = ensure(ctx, ctx->d_span_target, ctx->span_target_cap, (size_t)TR * 256)) != EXL3_OK)
+        return rc;
+    if ((rc = ensure(ctx, ctx->d_span_what, ctx->span_what_cap, (size_t)TR * 256)) != EXL3_OK)
+        return rc;
+    if ((rc = ensure(ctx, ctx->d_span_packed, ctx->span_packed_cap, (size_t)TR * 16 * K)) !=
+        EXL3_OK)
+        return rc;
+    float *err_dev = tile_err;
+    if (!err_dev) {
+        if ((rc = ensure(ctx, ctx->d_sse, ctx->sse_cap, (size_t)ntiles)) != EXL3_OK) return rc;
+        err_dev = ctx->d_sse;
+    }
+    // spans from the last tile column to the first: target, encode, commit
+    for (int j = TC - 1; j >= 0; --j) {
+        EXL3_HIP(ctx, exl3::launch_ldlq_target(ctx->d_wreg, ctx->d_err_tiles, L, TR, TC, j,
+                                               ctx->d_span_target, ctx->stream));
+        if ((rc = encode_chain(ctx, ctx->d_span_target, nullptr, TR, K, scale, ctx->d_span_packed,
+                               nullptr, nullptr, ctx->d_span_what, nullptr)) != EXL3_OK)
+            return rc;
+        EXL3_HIP(ctx, exl3::launch_ldlq_commit(ctx->d_wreg, ctx->d_span_what, ctx->d_span_packed,
+                                               TR, TC, j, K, packed, ctx->d_err_tiles, w_hat,
+                                               err_dev, ctx->stream));
+    }
+    if (mse_out) {
+        std::vector<float> err((size_t)ntiles);
+        EXL3_HIP(ctx, hipMemcpyAsync(err.data(), err_dev, (size_t)ntiles * sizeof(float),
+                                     hipMemcpyDeviceToHost, ctx->stream));
+        EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+        double tot = 0.0;
+        for (int64_t i = 0; i < ntiles; ++i) tot += (double)err[(size_t)i];
         *mse_out = tot / (double)nel;
     }
     EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));

@@ -1,0 +1,93 @@
+// LDLQ error feedback around the tile encoder on gfx950.
+//
+// Source: "EXL3 Intel Arc Quantizer" README, Core Implemented Architecture
+// item 3 (one-sided block LDLQ: spans traversed bottom-up, each span's target
+// corrected additively from the strictly lower blocks of L, the residual of
+// the spans already quantized fed back).
+//
+// The matrix lives tile-major ([TR*TC][256], tile tr*TC + tc, element 16r + c).
+// Span j is tile column j: the TR tiles (tr, j).  Its target is
+//     T_j = W_j + sum_{i > j} E_i L_ij,      E_i = W_i - What_i,
+// accumulated per element in the order i ascending, then t (row of the 16x16
+// block L_ij) ascending, each product and each sum a separately rounded
+// binary32 operation (this file is built with -ffp-contract=off).  One
+// workgroup of 256 lanes per tile row: lane (r, c) owns one element; per block
+// i the tile's error block E(tr, i) and the factor block L_ij are staged in LDS.
+#include "exl3_internal.h"
+
+namespace exl3 {
+namespace {
+
+__global__ void __launch_bounds__(256)
+ldlq_target_kernel(const float *__restrict__ w_tiles, const float *__restrict__ e_tiles,
+                   const float *__restrict__ L, int TC, int j, float *__restrict__ target) {
+    __shared__ float Es[16][17];
+    __shared__ float Ls[16][17];
+    const int tr = blockIdx.x;
+    const int e = threadIdx.x, r = e >> 4, c = e & 15;
+    const size_t C = (size_t)TC * 16;
+    float acc = w_tiles[((size_t)tr * TC + j) * 256 + e];
+    for (int i = j + 1; i < TC; ++i) {
+        Es[r][c] = e_tiles[((size_t)tr * TC + i) * 256 + e];          // E[16tr + r][16i + c]
+        Ls[r][c] = L[(size_t)(16 * i + r) * C + 16 * (size_t)j + c];  // L[16i + r][16j + c]
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const float p = Es[r][t] * Ls[t][c];
+            acc = acc + p;
+        }
+        __syncthreads();
+    }
+    target[(size_t)tr * 256 + e] = acc;
+}
+
+// Commit span j: scatter the span's container words, keep its error for the
+// spans below, optionally write the dequantized tiles, and the per-tile
+// sequential binary32 sum of (W - What)^2.
+__global__ void __launch_bounds__(256)
+ldlq_commit_kernel(const float *__restrict__ w_tiles, const float *__restrict__ what_span,
+                   const uint16_t *__restrict__ packed_span, int TC, int j, int K,
+                   uint16_t *__restrict__ packed, float *__restrict__ e_tiles,
+                   float *__restrict__ w_hat, float *__restrict__ tile_err) {
+    __shared__ float sq[256];
+    const int tr = blockIdx.x;
+    const int e = threadIdx.x;
+    const size_t tile = (size_t)tr * TC + j;
+    const float w = w_tiles[tile * 256 + e];
+    const float wh = what_span[(size_t)tr * 256 + e];
+    const float d = w - wh;
+    e_tiles[tile * 256 + e] = d;
+    if (w_hat) w_hat[tile * 256 + e] = wh;
+    if (e < 16 * K) packed[tile * 16 * K + e] = packed_span[(size_t)tr * 16 * K + e];
+    sq[e] = d * d;
+    __syncthreads();
+    if (e == 0) {
+        float acc = 0.0f;
+        for (int t = 0; t < 256; ++t) acc = acc + sq[t];
+        tile_err[tile] = acc;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_ldlq_target(const float *w_tiles, const float *e_tiles, const float *L, int TR,
+                              int TC, int j, float *target, hipStream_t stream) {
+    if (TR <= 0) return hipSuccess;
+    if (j < 0 || j >= TC) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(ldlq_target_kernel, dim3((unsigned)TR), dim3(256), 0, stream, w_tiles,
+                       e_tiles, L, TC, j, target);
+    return hipGetLastError();
+}
+
+hipError_t launch_ldlq_commit(const float *w_tiles, const float *what_span,
+                              const uint16_t *packed_span, int TR, int TC, int j, int K,
+                              uint16_t *packed, float *e_tiles, float *w_hat, float *tile_err,
+                              hipStream_t stream) {
+    if (TR <= 0) return hipSuccess;
+    if (j < 0 || j >= TC || K < 1 || K > 16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(ldlq_commit_kernel, dim3((unsigned)TR), dim3(256), 0, stream, w_tiles,
+                       what_span, packed_span, TC, j, K, packed, e_tiles, w_hat, tile_err);
+    return hipGetLastError();
+}
+
+}  // namespace exl3

@@ -31,15 +31,6 @@
 namespace exl3 {
 namespace {
 
-template <int N>
-struct Log2 {
-    static constexpr int v = 1 + Log2<N / 2>::v;
-};
-template <>
-struct Log2<1> {
-    static constexpr int v = 0;
-};
-
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
