@@ -106,16 +106,27 @@ traceback2_kernel(const typename Geo<K>::bp_t *__restrict__ bp, int64_t n,
         for (int t = 0; t < kSteps; ++t) states_out[(size_t)tile * kSteps + t] = S[lt][t];
     if (!x) return;
 
-    // dequantise and sequential squared error (equals the search's path cost)
+    // dequantise and sequential squared error (equals the search's path cost);
+    // the loads of a chunk are issued together, then consumed in step order
     const float *xt = x + (size_t)tile * kSteps;
     float sse = 0.0f;
-    for (int t = 0; t < kSteps; ++t) {
-        uint32_t st = S[lt][t];
-        float v = scale * half_bits_to_float(levels[st]);
-        float d = xt[t] - v;
-        float q = d * d;
-        sse = sse + q;
-        if (w_hat) w_hat[(size_t)tile * kSteps + t] = v;
+    constexpr int kChunk = 16;
+    for (int t0 = 0; t0 < kSteps; t0 += kChunk) {
+        uint16_t c[kChunk];
+        float xv[kChunk];
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            c[u] = levels[S[lt][t0 + u]];
+            xv[u] = xt[t0 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const float v = scale * half_bits_to_float(c[u]);
+            const float d = xv[u] - v;
+            const float q = d * d;
+            sse = sse + q;
+            if (w_hat) w_hat[(size_t)tile * kSteps + t0 + u] = v;
+        }
     }
     if (sse_out) sse_out[tile] = sse;
 }
