@@ -218,7 +218,10 @@ enum {
                                     scale search, its cost-only form */
     EXL3_KERNEL_TB1 = 2,         /* traceback to X */
     EXL3_KERNEL_TB2 = 3,         /* traceback, packing, squared error */
-    EXL3_KERNEL_REGULARIZE = 4
+    EXL3_KERNEL_REGULARIZE = 4,
+    EXL3_KERNEL_FWD_SIDE = 5     /* forward passes of a scale-search probe's last
+                                    partial round, run on a second stream beside
+                                    the main part (their durations overlap) */
 };
 
 /*

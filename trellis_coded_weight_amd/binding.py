@@ -33,7 +33,7 @@ EXPORTED = [
     "exl3_quantize_matrix_ldlq", "exl3_scratch_per_tile",
     "exl3_ctx_set_timing", "exl3_ctx_read_timing",
 ]
-KERNEL_KINDS = {"fwd1": 0, "fwd2": 1, "tb1": 2, "tb2": 3, "regularize": 4}
+KERNEL_KINDS = {"fwd1": 0, "fwd2": 1, "tb1": 2, "tb2": 3, "regularize": 4, "fwd_side": 5}
 
 
 class Exl3Error(RuntimeError):

@@ -26,6 +26,10 @@ struct exl3_ctx {
     int device = 0;
     int n_cu = 256;
     hipStream_t stream = nullptr;
+    // second stream (default priority) for the last partial round of a
+    // scale-search probe, with the events that order it against `stream`
+    hipStream_t aux = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     size_t scratch_limit = 0;
     uint16_t *d_levels = nullptr;
     void *d_bp = nullptr;
@@ -59,6 +63,7 @@ struct exl3_ctx {
         int kind;
         int64_t tiles;
         hipEvent_t start, stop;
+        hipStream_t stream;
     };
     bool timing = false;
     std::vector<Timed> timed;
@@ -124,22 +129,23 @@ void clear_timing(exl3_ctx *ctx) {
     ctx->timed.clear();
 }
 
-// Bracket one launch with events when timing is on.  Returns the record index
-// (or -1); close_timed() records the stop event.
-int open_timed(exl3_ctx *ctx, int kind, int64_t tiles) {
+// Bracket one launch with events when timing is on (on the stream the launch
+// goes to).  Returns the record index (or -1); close_timed() records the stop
+// event.
+int open_timed(exl3_ctx *ctx, int kind, int64_t tiles, hipStream_t s = nullptr) {
     if (!ctx->timing) return -1;
-    exl3_ctx::Timed r{kind, tiles, nullptr, nullptr};
+    exl3_ctx::Timed r{kind, tiles, nullptr, nullptr, s ? s : ctx->stream};
     if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) {
         (void)hipGetLastError();
         return -1;
     }
-    (void)hipEventRecord(r.start, ctx->stream);
+    (void)hipEventRecord(r.start, r.stream);
     ctx->timed.push_back(r);
     return (int)ctx->timed.size() - 1;
 }
 
 void close_timed(exl3_ctx *ctx, int id) {
-    if (id >= 0) (void)hipEventRecord(ctx->timed[(size_t)id].stop, ctx->stream);
+    if (id >= 0) (void)hipEventRecord(ctx->timed[(size_t)id].stop, ctx->timed[(size_t)id].stream);
 }
 
 int ensure_small(exl3_ctx *ctx, size_t n) {
@@ -162,6 +168,61 @@ int ensure_small(exl3_ctx *ctx, size_t n) {
         return fail(ctx, EXL3_ENOMEM, "device allocation of per-tile bookkeeping failed");
     }
     ctx->small_cap = m;
+    return EXL3_OK;
+}
+
+int ensure_aux(exl3_ctx *ctx) {
+    if (ctx->aux) return EXL3_OK;
+    EXL3_HIP(ctx, hipStreamCreateWithFlags(&ctx->aux, hipStreamNonBlocking));
+    EXL3_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming));
+    EXL3_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_join, hipEventDisableTiming));
+    return EXL3_OK;
+}
+
+// Path costs of n sample tiles (scale-search probe) when they fill some whole
+// rounds of one tile per compute unit plus a small remainder: the remainder's
+// chain runs on the second stream, so its pass 1 shares a round with the main
+// part's pass 2 instead of leaving the chip idle for a round of its own.
+int probe_split(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, int K, float scale,
+                float *cost_out) {
+    const int64_t rem = n % ctx->n_cu, a = n - rem;
+    const size_t per_tile = exl3::bp_bytes_per_tile(K);
+    char *bp = static_cast<char *>(ctx->d_bp);
+    int rc;
+    if ((rc = ensure_aux(ctx)) != EXL3_OK) return rc;
+    EXL3_HIP(ctx, hipEventRecord(ctx->ev_fork, ctx->stream));
+    EXL3_HIP(ctx, hipStreamWaitEvent(ctx->aux, ctx->ev_fork, 0));
+    struct Part {
+        hipStream_t s;
+        int64_t first, count;
+    } parts[2] = {{ctx->stream, 0, a}, {ctx->aux, a, rem}};
+    // the remainder's forward launches are timed as their own kind: they run
+    // beside the main part's, so their durations overlap other launches
+    for (const Part &p : parts) {
+        int id = open_timed(ctx, p.s == ctx->stream ? EXL3_KERNEL_FWD1 : EXL3_KERNEL_FWD_SIDE,
+                            p.count, p.s);
+        EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 1, x, idx + p.first, 0, p.count, ctx->d_levels,
+                                               scale, nullptr, bp + p.first * per_tile,
+                                               ctx->d_end + p.first, nullptr, p.s));
+        close_timed(ctx, id);
+    }
+    for (const Part &p : parts) {
+        int id = open_timed(ctx, EXL3_KERNEL_TB1, p.count, p.s);
+        EXL3_HIP(ctx, exl3::launch_traceback(K, 1, false, bp + p.first * per_tile, p.count,
+                                             ctx->d_end + p.first, ctx->d_X + p.first, nullptr,
+                                             nullptr, 0, nullptr, 0.0f, nullptr, nullptr,
+                                             nullptr, nullptr, p.s));
+        close_timed(ctx, id);
+        id = open_timed(ctx, p.s == ctx->stream ? EXL3_KERNEL_FWD2 : EXL3_KERNEL_FWD_SIDE,
+                        p.count, p.s);
+        EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 3, x, idx + p.first, 0, p.count, ctx->d_levels,
+                                               scale, ctx->d_X + p.first,
+                                               bp + p.first * per_tile, nullptr,
+                                               cost_out + p.first, p.s));
+        close_timed(ctx, id);
+    }
+    EXL3_HIP(ctx, hipEventRecord(ctx->ev_join, ctx->aux));
+    EXL3_HIP(ctx, hipStreamWaitEvent(ctx->stream, ctx->ev_join, 0));
     return EXL3_OK;
 }
 
@@ -188,6 +249,9 @@ int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, i
     ctx->d_bp = bp;
     ctx->bp_cap = bytes_cap;
     if ((rc = ensure_small(ctx, (size_t)batch)) != EXL3_OK) return rc;
+    if (cost_only && idx && batch == n && n > ctx->n_cu && n % ctx->n_cu != 0 &&
+        n % ctx->n_cu <= ctx->n_cu / 8)
+        return probe_split(ctx, x, idx, n, K, scale, cost_only);
     for (int64_t i0 = 0; i0 < n; i0 += batch) {
         const int64_t nb = std::min<int64_t>(batch, n - i0);
         const int32_t *idx_b = idx ? idx + i0 : nullptr;
@@ -333,7 +397,11 @@ void exl3_ctx_destroy(exl3_ctx *ctx) {
     if (!ctx) return;
     (void)hipSetDevice(ctx->device);
     (void)hipStreamSynchronize(ctx->stream);
+    if (ctx->aux) (void)hipStreamSynchronize(ctx->aux);
     clear_timing(ctx);
+    if (ctx->ev_fork) (void)hipEventDestroy(ctx->ev_fork);
+    if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
+    if (ctx->aux) (void)hipStreamDestroy(ctx->aux);
     void *bufs[] = {ctx->d_levels,      ctx->d_bp,          ctx->d_end,         ctx->d_X,
                     ctx->d_cost,        ctx->d_idx,         ctx->d_wreg,        ctx->d_sumsq,
                     ctx->d_sse,         ctx->d_flag,        ctx->d_err_tiles,   ctx->d_span_target,
