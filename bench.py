@@ -257,8 +257,8 @@ def main():
                          indent=1))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the encoder's tiles are independent and "
-              "this build runs on a single MI355X; --gpus %d is not supported" % args.gpus,
+        print("bench.py measures one GPU only (the encoder's tiles are independent; sharding "
+              "across GPUs is not implemented); --gpus %d is not supported" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     rank = int(os.environ.get("RANK", "0"))

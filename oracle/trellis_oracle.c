@@ -18,9 +18,10 @@
  *     equal e are (k << Kr) | e for k = 0 .. 2^K - 1;
  *   * branch metric at step t for state s: (x_t - v[s])^2, v = scaled levels.
  *
- * Numeric contract (a reading: the pages' own encoder works in fp16 with a fused
- * multiply-add; this build fixes binary32 with every operation rounded on its
- * own, which the file is compiled for with -ffp-contract=off):
+ * Numeric contract of this part (a reading: the pages' own encoder works in fp16
+ * with a fused multiply-add, which the binary16 functions further down follow;
+ * here binary32 with every operation rounded on its own, which the file is
+ * compiled for with -ffp-contract=off):
  *   d = x_t - v[s];  q = d * d;  C[s] = M[s >> K] + q        (three roundings)
  *   M'[e] = first strict minimum over k ascending of C[(k << Kr) | e]
  *   bp[t][e] = the k that produced it (lowest k among equal costs).
