@@ -11,30 +11,41 @@
 // accumulated per element in the order i ascending, then t (row of the 16x16
 // block L_ij) ascending, each product and each sum a separately rounded
 // binary32 operation (this file is built with -ffp-contract=off).  One
-// workgroup of 256 lanes per tile row: lane (r, c) owns one element; per block
-// i the tile's error block E(tr, i) and the factor block L_ij are staged in LDS.
+// workgroup of 256 lanes per tile row: lane (r, c) owns one element; the
+// tile's error blocks E(tr, i) and the factor blocks L_ij of 16 later spans at
+// a time are staged in LDS (one round trip to memory per 16 spans).
 #include "exl3_internal.h"
 
 namespace exl3 {
 namespace {
 
+constexpr int kBlocksPerChunk = 16;   // later spans staged in LDS per round trip
+
 __global__ void __launch_bounds__(256)
 ldlq_target_kernel(const float *__restrict__ w_tiles, const float *__restrict__ e_tiles,
                    const float *__restrict__ L, int TC, int j, float *__restrict__ target) {
-    __shared__ float Es[16][17];
-    __shared__ float Ls[16][17];
+    // error blocks E(tr, i) and factor blocks L_ij of up to 16 later spans at a
+    // time (32 KiB); reads of a row of Es / a column of Ls are bank-conflict-free
+    __shared__ float Es[kBlocksPerChunk][16][16];
+    __shared__ float Ls[kBlocksPerChunk][16][16];
     const int tr = blockIdx.x;
     const int e = threadIdx.x, r = e >> 4, c = e & 15;
     const size_t C = (size_t)TC * 16;
     float acc = w_tiles[((size_t)tr * TC + j) * 256 + e];
-    for (int i = j + 1; i < TC; ++i) {
-        Es[r][c] = e_tiles[((size_t)tr * TC + i) * 256 + e];          // E[16tr + r][16i + c]
-        Ls[r][c] = L[(size_t)(16 * i + r) * C + 16 * (size_t)j + c];  // L[16i + r][16j + c]
+    for (int i0 = j + 1; i0 < TC; i0 += kBlocksPerChunk) {
+        const int ni = (TC - i0) < kBlocksPerChunk ? (TC - i0) : kBlocksPerChunk;
+        for (int q = 0; q < ni; ++q) {
+            const int i = i0 + q;
+            Es[q][r][c] = e_tiles[((size_t)tr * TC + i) * 256 + e];          // E[16tr + r][16i + c]
+            Ls[q][r][c] = L[(size_t)(16 * i + r) * C + 16 * (size_t)j + c];  // L[16i + r][16j + c]
+        }
         __syncthreads();
+        for (int q = 0; q < ni; ++q) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const float p = Es[r][t] * Ls[t][c];
-            acc = acc + p;
+            for (int t = 0; t < 16; ++t) {
+                const float p = Es[q][r][t] * Ls[q][t][c];
+                acc = acc + p;
+            }
         }
         __syncthreads();
     }
