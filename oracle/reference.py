@@ -362,6 +362,56 @@ def golden_section(f, lo, hi, iters):
     return (a + b) / 2.0, trace
 
 
+GRID_DEFAULT = (0.1, 1.9, 0.1, 2, 0.075, 0.025, 0.01)
+
+
+def grid_search(f_sub, f_full, grid=GRID_DEFAULT):
+    """The pages' scale search over a multiplier g of the matrix rms
+    [P1 item 8: coarse grid on a strided subsample, fine grid around the
+    coarse minimum on the full sample, parabolic refinement with a floor].
+
+    grid = (coarse_lo, coarse_hi, coarse_step, stride, fine_radius, fine_step,
+    floor); f_sub / f_full map g to the objective on the subsample / full
+    sample.  Readings: coarse points lo + k * step for k = 0 .. round((hi - lo) /
+    step); the least objective wins, the lowest g on ties; fine points g_c + m *
+    fine_step for |m| <= round(fine_radius / fine_step); if the fine minimum g_f
+    is interior and d = f(g_f - h) - 2 f(g_f) + f(g_f + h) > 0, the vertex
+    g_f + h (f(g_f - h) - f(g_f + h)) / (2 d) replaces it; the result is at least
+    floor.  Returns (g, trace)."""
+    lo, hi, step, _stride, radius, fstep, floor = grid
+    n_c = int(round((hi - lo) / step))
+    trace = []
+    best_g, best_f = None, None
+    for k in range(n_c + 1):
+        g = lo + k * step
+        v = f_sub(g)
+        trace.append(("coarse", g, v))
+        if best_f is None or v < best_f:
+            best_g, best_f = g, v
+    g_c = best_g
+    M = int(round(radius / fstep))
+    fine = []
+    for m in range(-M, M + 1):
+        g = g_c + m * fstep
+        v = f_full(g)
+        trace.append(("fine", g, v))
+        fine.append((g, v))
+    i_best = 0
+    for i in range(1, len(fine)):
+        if fine[i][1] < fine[i_best][1]:
+            i_best = i
+    g_f, f0 = fine[i_best]
+    g = g_f
+    if 0 < i_best < len(fine) - 1:
+        fm, fp = fine[i_best - 1][1], fine[i_best + 1][1]
+        d = fm - 2.0 * f0 + fp
+        if d > 0.0:
+            g = g_f + fstep * (fm - fp) / (2.0 * d)
+    g = max(g, floor)
+    trace.append(("result", g, None))
+    return g, trace
+
+
 def encode_tiles(tiles, K, scale, levels=None, threads=None):
     """Encode tiles [n, 256] at a fixed binary32 scale.
 
@@ -376,12 +426,14 @@ def encode_tiles(tiles, K, scale, levels=None, threads=None):
 
 
 def quantize_matrix(w, su, sv, K, had_block=128, gss=(12, 0.5, 2.0), fixed_scale=1.0,
-                    levels=None, threads=None, tiles_subset=None):
+                    levels=None, threads=None, tiles_subset=None, grid=None):
     """Whole-matrix path: regularize, statistics, scale search, final encode.
 
-    gss=None uses fixed_scale.  tiles_subset, if given, restricts the FINAL
-    encode to those tile indices (the scale search always uses its full sample),
-    which is how large matrices are checked one sampled tile at a time.
+    gss=None uses fixed_scale; grid (a GRID_DEFAULT-shaped tuple), if given,
+    replaces the golden-section search with grid_search, the scale being
+    (float)(g * rms).  tiles_subset, if given, restricts the FINAL encode to
+    those tile indices (the scale search always uses its full sample), which is
+    how large matrices are checked one sampled tile at a time.
     """
     w = np.asarray(w, dtype=np.float32)
     R, C = w.shape
@@ -393,7 +445,28 @@ def quantize_matrix(w, su, sv, K, had_block=128, gss=(12, 0.5, 2.0), fixed_scale
     sumsq = tile_sumsq(tiles)
     rms = matrix_rms(sumsq, R * C)
     out = {"tiles": tiles, "sumsq": sumsq, "rms": rms}
-    if gss is None:
+    if grid is not None:
+        sample = sample_tiles(TR, TC, sumsq)
+        out["sample"] = sample
+        if rms == 0.0:
+            scale = np.float32(0.0)
+            out["trace"] = []
+        else:
+            stride = grid[3]
+
+            def objective(g, idx):
+                r = encode_tiles(tiles[idx], K, np.float32(g * rms), levels, threads)
+                total = 0.0
+                for e in r["sse"].tolist():
+                    total += float(e)
+                return total
+
+            sub = sample[::stride]
+            g, trace = grid_search(lambda g: objective(g, sub), lambda g: objective(g, sample),
+                                   grid)
+            scale = np.float32(g * rms)
+            out["trace"] = trace
+    elif gss is None:
         scale = np.float32(fixed_scale)
         out["sample"] = []
         out["trace"] = []
