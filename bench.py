@@ -220,6 +220,26 @@ def ldlq_mode(ctx, m, w, su, sv, steps):
             "fwd_ms_per_step": round((f1[0] + f2[0]) / n, 3)}
 
 
+def grid_mode(ctx, w, su, sv, n_tiles, steps):
+    """The same matrix at K = 2 with the pages' grid + parabolic scale search
+    (19 coarse probes on every other sample tile, 7 fine probes on all of them)
+    in place of the golden section."""
+    import torch
+    import trellis_coded_weight_amd as T
+    out = ctx.quantize_matrix_grid(w, 2, su, sv, grid=T.GRID_PAGES)
+    torch.cuda.synchronize()
+    n = max(1, steps // 2)
+    t0 = time.perf_counter()
+    for _ in range(n):
+        out = ctx.quantize_matrix_grid(w, 2, su, sv, grid=T.GRID_PAGES)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    return {"workload": "the same 4096x4096 matrix, K=2, grid {0.1..1.9 step 0.1 on every other "
+                        "sample tile; +-0.075 step 0.025 on all; parabolic; floor 0.01}",
+            "tiles_per_s": round(n_tiles * n / dt, 1), "ms_per_step": round(1000.0 * dt / n, 3),
+            "scale": out["scale"], "mse": out["mse"]}
+
+
 def run_steps(ctx, w, su, sv, K, gss, steps):
     import torch
     out = None
@@ -238,6 +258,8 @@ def main():
     ap.add_argument("--cpu-tiles", type=int, default=8192)
     ap.add_argument("--no-other-k", action="store_true",
                     help="skip the K=3 and K=4 runs on the same matrix")
+    ap.add_argument("--no-grid", action="store_true",
+                    help="skip the grid + parabolic scale-search run on the same matrix")
     ap.add_argument("--no-ldlq", action="store_true",
                     help="skip the LDLQ (error feedback) run on the same matrix")
     ap.add_argument("--no-f16", action="store_true",
@@ -358,6 +380,7 @@ def main():
 
     f16 = None if args.no_f16 else f16_mode(ctx, w, su, sv, out["scale"], n_tiles, args.steps)
     ldlq = None if args.no_ldlq else ldlq_mode(ctx, m, w, su, sv, args.steps)
+    grid = None if args.no_grid else grid_mode(ctx, w, su, sv, n_tiles, args.steps)
 
     cpu = None
     if not args.no_cpu_baseline and rank == 0:
@@ -392,6 +415,7 @@ def main():
         "cpu_baseline": cpu,
         "f16_mode": f16,
         "ldlq_mode": ldlq,
+        "grid_search_mode": grid,
     }
     if rank == 0:
         print(json.dumps(line), flush=True)

@@ -186,6 +186,35 @@ int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, in
                          float *scale_out, double *mse_out, float *w_hat, float *tile_sse);
 
 /*
+ * Whole-matrix quantization with the pages' grid + parabolic scale search
+ * [P1 section 8] instead of the golden section: the search runs over a
+ * multiplier g of the matrix rms.  Coarse points g = coarse_lo + k*coarse_step,
+ * k = 0 .. round((coarse_hi - coarse_lo) / coarse_step), are scored on every
+ * stride-th tile of the scale-search tile set (the set of exl3_quantize_matrix),
+ * fine points g_c + m*fine_step, |m| <= round(fine_radius / fine_step), around
+ * the best coarse point g_c on the whole set; the objective is the binary64
+ * sum, in ascending tile order, of the path costs at scale (float)(g * rms);
+ * the least value wins (lowest g on ties).  If the best fine point is interior,
+ * the vertex of the parabola through it and its two neighbours replaces it; the
+ * result is at least `floor`, and the scale is (float)(g * rms) (0 when rms is 0).
+ * The pages' values: {0.1, 1.9, 0.1, 2, 0.075, 0.025, 0.01}.
+ * Outputs and errors as exl3_quantize_matrix; EXL3_EINVAL for a null or
+ * malformed grid (coarse_lo <= 0, steps <= 0, stride < 1, floor < 0, more than
+ * 1000 points per stage).
+ */
+typedef struct {
+    double coarse_lo, coarse_hi, coarse_step;
+    int stride;
+    double fine_radius, fine_step;
+    double floor;
+} exl3_grid;
+
+int exl3_quantize_matrix_grid(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
+                              int K, int had_block, const float *su, const float *sv,
+                              const exl3_grid *grid, uint16_t *packed, float *scale_out,
+                              double *mse_out, float *w_hat, float *tile_sse);
+
+/*
  * Whole-matrix quantization with LDLQ error feedback [P1 section 3: one-sided
  * block LDLQ].  Regularization and the scale exactly as exl3_quantize_matrix
  * (the scale is chosen on the matrix without feedback); then the 16-column

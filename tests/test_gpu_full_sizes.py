@@ -172,3 +172,30 @@ def test_workload5_layer_all_k(ctx):
             assert 2.0 ** (-2 * K) < nmse < _lloyd(K)
             mses.append(got["mse"])
         assert mses[0] > mses[1] > mses[2]
+
+
+def test_workload2_grid_search_scale(ctx):
+    """The pages' grid + parabolic search on the 4096x4096 matrix: the chosen scale is
+    the oracle's (19 coarse probes on 129 sample tiles, 7 fine probes on 258)."""
+    import trellis_coded_weight_amd as T
+    m = workloads.config(2)[0]
+    R, C = m.w.shape
+    print("\ngrid search 4096x4096 K=2", flush=True)
+    w = torch.from_numpy(m.w).to(torch.bfloat16).to(DEV)
+    su, sv = torch.from_numpy(m.su).to(DEV), torch.from_numpy(m.sv).to(DEV)
+    got = ctx.quantize_matrix_grid(w, 2, su, sv, grid=T.GRID_PAGES, want_tile_sse=True)
+    reg, sums, _ = ctx.regularize(w, su, sv, 128)
+    sums = sums.cpu().numpy()
+    rms = oracle.matrix_rms(sums, R * C)
+    sample = oracle.sample_tiles(R // 16, C // 16, sums)
+    xs = _oracle_tiles(m, sample)
+
+    def f(idx_pos):
+        def obj(g):
+            r = oracle.encode_tiles(xs[idx_pos], 2, np.float32(g * rms))
+            return sum(float(e) for e in r["sse"].tolist())
+        return obj
+
+    g, _ = oracle.grid_search(f(np.arange(len(sample))[::2]), f(np.arange(len(sample))),
+                              oracle.GRID_DEFAULT)
+    assert np.float32(got["scale"]) == np.float32(g * rms)

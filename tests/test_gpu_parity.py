@@ -174,6 +174,33 @@ def test_small_matrix_with_scale_search(ctx, K):
     assert got["mse"] == want["mse"]
 
 
+@pytest.mark.parametrize("K", [2, 3])
+def test_small_matrix_with_grid_search(ctx, K):
+    import trellis_coded_weight_amd as T
+    m = workloads.gaussian(256, 384, 0.02, 35 + K, 45 + K, K=K)
+    want = oracle.quantize_matrix(m.w, m.su, m.sv, K, had_block=128, gss=None,
+                                  grid=oracle.GRID_DEFAULT)
+    got = ctx.quantize_matrix_grid(torch.from_numpy(m.w).to(torch.bfloat16).to(DEV), K,
+                                   torch.from_numpy(m.su).to(DEV), torch.from_numpy(m.sv).to(DEV),
+                                   grid=T.GRID_PAGES, want_tile_sse=True)
+    assert np.float32(got["scale"]) == want["scale"]
+    assert np.array_equal(_u16(got["packed"]).reshape(-1, 16 * K), want["packed"])
+    assert np.array_equal(_bits(got["tile_sse"].cpu().numpy()), _bits(want["sse"]))
+    assert got["mse"] == want["mse"]
+
+
+def test_grid_rejects_malformed_grid(ctx):
+    import trellis_coded_weight_amd as T
+    m = workloads.gaussian(128, 128, 0.02, 1, 2, K=2)
+    w = torch.from_numpy(m.w).to(torch.bfloat16).to(DEV)
+    su, sv = torch.from_numpy(m.su).to(DEV), torch.from_numpy(m.sv).to(DEV)
+    for bad in [(0.0, 1.9, 0.1, 2, 0.075, 0.025, 0.01), (0.1, 1.9, 0.0, 2, 0.075, 0.025, 0.01),
+                (0.1, 1.9, 0.1, 0, 0.075, 0.025, 0.01), (0.1, 1.9, 0.1, 2, 0.075, 0.025, -1.0)]:
+        with pytest.raises(T.Exl3Error) as e:
+            ctx.quantize_matrix_grid(w, 2, su, sv, grid=bad)
+        assert e.value.code == T.EXL3_EINVAL
+
+
 def test_batching_does_not_change_results():
     import trellis_coded_weight_amd as T
     x = workloads.random_tiles(11, 77)

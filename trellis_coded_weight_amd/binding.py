@@ -30,7 +30,7 @@ EXPORTED = [
     "exl3_version", "exl3_ctx_create", "exl3_ctx_destroy", "exl3_last_error",
     "exl3_ctx_set_stream", "exl3_set_codebook", "exl3_get_codebook", "exl3_regularize",
     "exl3_encode_tiles", "exl3_encode_tiles_f16", "exl3_decode_tiles", "exl3_quantize_matrix",
-    "exl3_quantize_matrix_ldlq", "exl3_scratch_per_tile",
+    "exl3_quantize_matrix_ldlq", "exl3_quantize_matrix_grid", "exl3_scratch_per_tile",
     "exl3_ctx_set_timing", "exl3_ctx_read_timing",
 ]
 KERNEL_KINDS = {"fwd1": 0, "fwd2": 1, "tb1": 2, "tb2": 3, "regularize": 4, "fwd_side": 5}
@@ -45,6 +45,16 @@ class Exl3Error(RuntimeError):
 
 class GSS(ctypes.Structure):
     _fields_ = [("iters", ctypes.c_int), ("lo", ctypes.c_double), ("hi", ctypes.c_double)]
+
+
+class Grid(ctypes.Structure):
+    _fields_ = [("coarse_lo", ctypes.c_double), ("coarse_hi", ctypes.c_double),
+                ("coarse_step", ctypes.c_double), ("stride", ctypes.c_int),
+                ("fine_radius", ctypes.c_double), ("fine_step", ctypes.c_double),
+                ("floor", ctypes.c_double)]
+
+
+GRID_PAGES = (0.1, 1.9, 0.1, 2, 0.075, 0.025, 0.01)
 
 
 _lib = None
@@ -96,6 +106,10 @@ def load_library():
     lib.exl3_quantize_matrix_ldlq.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp,
                                               ctypes.POINTER(GSS), f32, vp, vp,
                                               ctypes.POINTER(f32), ctypes.POINTER(f64), vp, vp]
+    lib.exl3_quantize_matrix_grid.restype = i32
+    lib.exl3_quantize_matrix_grid.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp,
+                                              ctypes.POINTER(Grid), vp, ctypes.POINTER(f32),
+                                              ctypes.POINTER(f64), vp, vp]
     lib.exl3_scratch_per_tile.restype = sz
     lib.exl3_scratch_per_tile.argtypes = [i32]
     lib.exl3_ctx_set_timing.restype = i32
@@ -287,6 +301,34 @@ class Context:
         self._check(self.lib.exl3_quantize_matrix(
             self.handle, _ptr(w), dt, rows, cols, K, had_block, _ptr(su.contiguous()),
             _ptr(sv.contiguous()), g, float(scale), _ptr(packed), ctypes.byref(s_out),
+            ctypes.byref(mse), _ptr(w_hat), _ptr(tsse)))
+        return {"packed": packed, "scale": s_out.value, "mse": mse.value, "w_hat": w_hat,
+                "tile_sse": tsse}
+
+    def quantize_matrix_grid(self, w: torch.Tensor, K: int, su: torch.Tensor, sv: torch.Tensor,
+                             had_block: int = 128, grid: Tuple = GRID_PAGES,
+                             want_w_hat: bool = False, want_tile_sse: bool = False):
+        """Whole-matrix path with the grid + parabolic scale search.
+        Returns dict(packed int16 [R/16, C/16, 16K], scale, mse, w_hat?, tile_sse?)."""
+        rows, cols = w.shape
+        dt = {torch.float32: EXL3_F32, torch.bfloat16: EXL3_BF16}.get(w.dtype)
+        if dt is None:
+            raise ValueError("w must be float32 or bfloat16")
+        w = w.contiguous()
+        dev = w.device
+        packed = torch.empty(rows // 16, cols // 16, 16 * K, dtype=torch.int16, device=dev)
+        w_hat = (torch.empty((rows // 16) * (cols // 16), 256, dtype=torch.float32, device=dev)
+                 if want_w_hat else None)
+        tsse = (torch.empty((rows // 16) * (cols // 16), dtype=torch.float32, device=dev)
+                if want_tile_sse else None)
+        g = Grid(float(grid[0]), float(grid[1]), float(grid[2]), int(grid[3]), float(grid[4]),
+                 float(grid[5]), float(grid[6]))
+        s_out = ctypes.c_float(0.0)
+        mse = ctypes.c_double(0.0)
+        self._sync_stream()
+        self._check(self.lib.exl3_quantize_matrix_grid(
+            self.handle, _ptr(w), dt, rows, cols, K, had_block, _ptr(su.contiguous()),
+            _ptr(sv.contiguous()), ctypes.byref(g), _ptr(packed), ctypes.byref(s_out),
             ctypes.byref(mse), _ptr(w_hat), _ptr(tsse)))
         return {"packed": packed, "scale": s_out.value, "mse": mse.value, "w_hat": w_hat,
                 "tile_sse": tsse}

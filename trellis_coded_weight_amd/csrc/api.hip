@@ -540,20 +540,65 @@ int exl3_decode_tiles(exl3_ctx *ctx, const uint16_t *packed, int64_t n, int K, f
 
 namespace {
 
+// Grid + parabolic search for the multiplier of the rms ("EXL3 Intel Arc
+// Quantizer" README, Core Implemented Architecture section 8): coarse points
+// lo + k*step on the subsample (least objective, lowest on ties), fine points
+// g_c + m*fine_step on the full sample, then the vertex of the parabola through
+// an interior fine minimum and its neighbours; at least `floor`.
+template <typename FS, typename FF>
+double grid_search(const exl3_grid &grid, FS f_sub, FF f_full) {
+    const long n_c = std::lround((grid.coarse_hi - grid.coarse_lo) / grid.coarse_step);
+    double g_c = grid.coarse_lo, best = 0.0;
+    for (long k = 0; k <= n_c; ++k) {
+        const double g = grid.coarse_lo + (double)k * grid.coarse_step;
+        const double v = f_sub(g);
+        if (k == 0 || v < best) {
+            best = v;
+            g_c = g;
+        }
+    }
+    const long M = std::lround(grid.fine_radius / grid.fine_step);
+    std::vector<double> gs, fs;
+    for (long m = -M; m <= M; ++m) {
+        const double g = g_c + (double)m * grid.fine_step;
+        gs.push_back(g);
+        fs.push_back(f_full(g));
+    }
+    size_t ib = 0;
+    for (size_t i = 1; i < fs.size(); ++i)
+        if (fs[i] < fs[ib]) ib = i;
+    double g = gs[ib];
+    if (ib > 0 && ib + 1 < fs.size()) {
+        const double fm = fs[ib - 1], f0 = fs[ib], fp = fs[ib + 1];
+        const double d = fm - 2.0 * f0 + fp;
+        if (d > 0.0) g = gs[ib] + grid.fine_step * (fm - fp) / (2.0 * d);
+    }
+    return std::max(g, grid.floor);
+}
+
 // Validation, regularization (tile-major, into the context), statistics and the
 // scale (fixed or golden-section search on the tile sample): the common front
 // of the whole-matrix calls.
 int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
                                 int K, int had_block, const float *su, const float *sv,
-                                const exl3_gss *gss, float fixed_scale, uint16_t *packed,
-                                float *scale_out, float *scale_chosen) {
+                                const exl3_gss *gss, const exl3_grid *grid, float fixed_scale,
+                                uint16_t *packed, float *scale_out, float *scale_chosen) {
     if (!ctx) return EXL3_EINVAL;
     int rc;
     if ((rc = check_matrix_args(ctx, w, w_dtype, rows, cols, had_block, su, sv)) != EXL3_OK)
         return rc;
     if (!k_supported(K)) return fail(ctx, EXL3_EUNSUPPORTED, "K = %d (supported: 1, 2, 3, 4)", K);
     if (!packed || !scale_out) return fail(ctx, EXL3_EINVAL, "null output");
-    if (gss) {
+    if (grid) {
+        const double n_c = grid->coarse_step > 0.0
+                               ? (grid->coarse_hi - grid->coarse_lo) / grid->coarse_step : -1.0;
+        const double n_f = grid->fine_step > 0.0 ? grid->fine_radius / grid->fine_step : -1.0;
+        if (!(grid->coarse_lo > 0.0) || !(n_c >= 0.0) || n_c > 1000.0 || grid->stride < 1 ||
+            !(n_f >= 0.0) || n_f > 1000.0 || !(grid->floor >= 0.0) || !std::isfinite(grid->floor))
+            return fail(ctx, EXL3_EINVAL, "grid search {%g..%g step %g, stride %d, +-%g step %g, "
+                        "floor %g}", grid->coarse_lo, grid->coarse_hi, grid->coarse_step,
+                        grid->stride, grid->fine_radius, grid->fine_step, grid->floor);
+    } else if (gss) {
         if (gss->iters < 1 || gss->iters > 64 || !(gss->lo > 0.0) || !(gss->hi > gss->lo) ||
             !std::isfinite(gss->hi))
             return fail(ctx, EXL3_EINVAL, "scale search {iters %d, lo %g, hi %g}", gss->iters,
@@ -594,7 +639,7 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
 
     // 3. scale
     float scale = fixed_scale;
-    if (gss) {
+    if (gss || grid) {
         if (rms == 0.0) {
             scale = 0.0f;
         } else {
@@ -611,21 +656,30 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
             pick.insert(imin);
             std::vector<int32_t> sample(pick.begin(), pick.end());
             const int64_t ns = (int64_t)sample.size();
-            if ((rc = ensure(ctx, ctx->d_idx, ctx->idx_cap, (size_t)ns)) != EXL3_OK) return rc;
+            // device index list: the sample, then (grid search) every stride-th entry of it
+            std::vector<int32_t> idx_all(sample);
+            int64_t ns_sub = 0;
+            if (grid)
+                for (size_t i = 0; i < sample.size(); i += (size_t)grid->stride, ++ns_sub)
+                    idx_all.push_back(sample[i]);
+            if ((rc = ensure(ctx, ctx->d_idx, ctx->idx_cap, idx_all.size())) != EXL3_OK) return rc;
             if ((rc = ensure(ctx, ctx->d_sse, ctx->sse_cap,
                              std::max<size_t>((size_t)ns, (size_t)ntiles))) != EXL3_OK)
                 return rc;
-            EXL3_HIP(ctx, hipMemcpyAsync(ctx->d_idx, sample.data(), (size_t)ns * sizeof(int32_t),
+            EXL3_HIP(ctx, hipMemcpyAsync(ctx->d_idx, idx_all.data(),
+                                         idx_all.size() * sizeof(int32_t),
                                          hipMemcpyHostToDevice, ctx->stream));
             std::vector<float> costs((size_t)ns);
             int err = EXL3_OK;
-            auto objective = [&](double s) -> double {
+            // binary64 sum, in ascending tile order, of the path costs of the
+            // tiles idx[off .. off+cnt) at scale (float)s
+            auto objective_on = [&](double s, int64_t off, int64_t cnt) -> double {
                 if (err != EXL3_OK) return 0.0;
-                int r = encode_chain(ctx, ctx->d_wreg, ctx->d_idx, ns, K, (float)s, nullptr,
-                                     nullptr, nullptr, nullptr, ctx->d_sse);
+                int r = encode_chain(ctx, ctx->d_wreg, ctx->d_idx + off, cnt, K, (float)s,
+                                     nullptr, nullptr, nullptr, nullptr, ctx->d_sse);
                 if (r == EXL3_OK) {
                     hipError_t e = hipMemcpyAsync(costs.data(), ctx->d_sse,
-                                                  (size_t)ns * sizeof(float),
+                                                  (size_t)cnt * sizeof(float),
                                                   hipMemcpyDeviceToHost, ctx->stream);
                     if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
                     if (e != hipSuccess)
@@ -637,9 +691,18 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
                     return 0.0;
                 }
                 double f = 0.0;
-                for (int64_t i = 0; i < ns; ++i) f += (double)costs[(size_t)i];
+                for (int64_t i = 0; i < cnt; ++i) f += (double)costs[(size_t)i];
                 return f;
             };
+            if (grid) {
+                const double mult = grid_search(
+                    *grid, [&](double m) { return objective_on(m * rms, ns, ns_sub); },
+                    [&](double m) { return objective_on(m * rms, 0, ns); });
+                if (err != EXL3_OK) return err;
+                *scale_chosen = (float)(mult * rms);
+                return EXL3_OK;
+            }
+            auto objective = [&](double s) { return objective_on(s, 0, ns); };
             const double g = (std::sqrt(5.0) - 1.0) / 2.0;
             double a = gss->lo * rms, b = gss->hi * rms;
             double p = b - (b - a) * g, q = a + (b - a) * g;
@@ -668,18 +731,11 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
     return EXL3_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols, int K,
-                         int had_block, const float *su, const float *sv, const exl3_gss *gss,
-                         float fixed_scale, uint16_t *packed, float *scale_out, double *mse_out,
-                         float *w_hat, float *tile_sse) {
-    float scale = 0.0f;
-    int rc = regularize_and_choose_scale(ctx, w, w_dtype, rows, cols, K, had_block, su, sv, gss,
-                                         fixed_scale, packed, scale_out, &scale);
-    if (rc != EXL3_OK) return rc;
+// Final encode of every tile of the regularized matrix at the chosen scale,
+// the mean squared error in binary64 (ascending tile order) and the scale.
+int encode_whole_matrix(exl3_ctx *ctx, int rows, int cols, int K, float scale, uint16_t *packed,
+                        float *scale_out, double *mse_out, float *w_hat, float *tile_sse) {
+    int rc;
     const int64_t ntiles = (int64_t)(rows / 16) * (cols / 16);
     const size_t nel = (size_t)rows * cols;
     // 4. final encode of every tile at the chosen scale
@@ -705,6 +761,36 @@ int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, in
     return EXL3_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols, int K,
+                         int had_block, const float *su, const float *sv, const exl3_gss *gss,
+                         float fixed_scale, uint16_t *packed, float *scale_out, double *mse_out,
+                         float *w_hat, float *tile_sse) {
+    float scale = 0.0f;
+    int rc = regularize_and_choose_scale(ctx, w, w_dtype, rows, cols, K, had_block, su, sv, gss,
+                                         nullptr, fixed_scale, packed, scale_out, &scale);
+    if (rc != EXL3_OK) return rc;
+    return encode_whole_matrix(ctx, rows, cols, K, scale, packed, scale_out, mse_out, w_hat,
+                               tile_sse);
+}
+
+int exl3_quantize_matrix_grid(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
+                              int K, int had_block, const float *su, const float *sv,
+                              const exl3_grid *grid, uint16_t *packed, float *scale_out,
+                              double *mse_out, float *w_hat, float *tile_sse) {
+    if (!ctx) return EXL3_EINVAL;
+    if (!grid) return fail(ctx, EXL3_EINVAL, "null grid");
+    float scale = 0.0f;
+    int rc = regularize_and_choose_scale(ctx, w, w_dtype, rows, cols, K, had_block, su, sv,
+                                         nullptr, grid, 0.0f, packed, scale_out, &scale);
+    if (rc != EXL3_OK) return rc;
+    return encode_whole_matrix(ctx, rows, cols, K, scale, packed, scale_out, mse_out, w_hat,
+                               tile_sse);
+}
+
 int exl3_quantize_matrix_ldlq(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
                               int K, int had_block, const float *su, const float *sv,
                               const exl3_gss *gss, float fixed_scale, const float *L,
@@ -714,7 +800,7 @@ int exl3_quantize_matrix_ldlq(exl3_ctx *ctx, const void *w, int w_dtype, int row
     if (!L) return fail(ctx, EXL3_EINVAL, "null factor L");
     float scale = 0.0f;
     int rc = regularize_and_choose_scale(ctx, w, w_dtype, rows, cols, K, had_block, su, sv, gss,
-                                         fixed_scale, packed, scale_out, &scale);
+                                         nullptr, fixed_scale, packed, scale_out, &scale);
     if (rc != EXL3_OK) return rc;
     const int TR = rows / 16, TC = cols / 16;
     const int64_t ntiles = (int64_t)TR * TC;
