@@ -139,6 +139,20 @@ def cpu_baseline(m, K, scale, n_tiles, threads, sample_tiles):
     oracle.encode_tiles(tiles[idx], K, np.float32(scale), levels, threads=threads)
     t_enc = time.perf_counter() - t1
     per_tile = t_enc / sample_tiles
+    # one thread on a small slice of the same sample
+    n1 = max(1, min(64, sample_tiles // 64))
+    t2 = time.perf_counter()
+    oracle.encode_tiles(tiles[idx[:n1]], K, np.float32(scale), levels, threads=1)
+    per_tile_1 = (time.perf_counter() - t2) / n1
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     TR, TC = m.w.shape[0] // 16, m.w.shape[1] // 16
     encodes = n_tiles + (m.gss[0] + 2) * sample_size(TR, TC)
     total = t_reg + per_tile * encodes
@@ -153,6 +167,8 @@ def cpu_baseline(m, K, scale, n_tiles, threads, sample_tiles):
                    % (m.w.shape[0], m.w.shape[1], sample_tiles, encodes, encodes - n_tiles)),
         "measured_s": round(t_reg + t_enc, 2),
         "tile_encodes_per_s": 1.0 / per_tile,
+        "single_thread_tile_encodes_per_s": 1.0 / per_tile_1,
+        "cpu_model": cpu_model,
     }
 
 
