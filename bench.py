@@ -256,6 +256,36 @@ def grid_mode(ctx, w, su, sv, n_tiles, steps):
             "scale": out["scale"], "mse": out["mse"]}
 
 
+def layer_mode(ctx):
+    """One transformer layer's seven matrices (q, k, v, o, gate, up, down; 753,664
+    tiles, uploaded before timing) quantized back to back on one stream with the
+    golden-section search, once at each of K = 2, 3, 4."""
+    import torch
+    import workloads
+    dev = torch.device("cuda", 0)
+    mats = []
+    for m in workloads.config(5):
+        mats.append((torch.from_numpy(m.w).to(torch.bfloat16).to(dev),
+                     torch.from_numpy(m.su).to(dev), torch.from_numpy(m.sv).to(dev), m.gss,
+                     m.n_tiles))
+    tiles = sum(x[4] for x in mats)
+    res = {"workload": "q 4096x4096, k/v 4096x1024, o 4096x4096, gate/up 4096x12288, "
+                       "down 12288x4096 bf16 N(0, 0.02^2), back to back, golden-section scale",
+           "tiles": tiles, "tiles_per_s_by_K": {}, "s_by_K": {}}
+    for K in (2, 3, 4):
+        ctx.quantize_matrix(mats[1][0], K, mats[1][1], mats[1][2], gss=mats[1][3])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for w, su, sv, gss, _ in mats:
+            ctx.quantize_matrix(w, K, su, sv, gss=gss)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        res["tiles_per_s_by_K"][str(K)] = round(tiles / dt, 1)
+        res["s_by_K"][str(K)] = round(dt, 3)
+    del mats
+    return res
+
+
 def run_steps(ctx, w, su, sv, K, gss, steps):
     import torch
     out = None
@@ -274,6 +304,8 @@ def main():
     ap.add_argument("--cpu-tiles", type=int, default=8192)
     ap.add_argument("--no-other-k", action="store_true",
                     help="skip the K=3 and K=4 runs on the same matrix")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the transformer-layer run (seven matrices at K = 2, 3, 4)")
     ap.add_argument("--no-grid", action="store_true",
                     help="skip the grid + parabolic scale-search run on the same matrix")
     ap.add_argument("--no-ldlq", action="store_true",
@@ -397,6 +429,7 @@ def main():
     f16 = None if args.no_f16 else f16_mode(ctx, w, su, sv, out["scale"], n_tiles, args.steps)
     ldlq = None if args.no_ldlq else ldlq_mode(ctx, m, w, su, sv, args.steps)
     grid = None if args.no_grid else grid_mode(ctx, w, su, sv, n_tiles, args.steps)
+    layer = None if args.no_layer else layer_mode(ctx)
 
     cpu = None
     if not args.no_cpu_baseline and rank == 0:
@@ -432,6 +465,7 @@ def main():
         "f16_mode": f16,
         "ldlq_mode": ldlq,
         "grid_search_mode": grid,
+        "layer_mode": layer,
     }
     if rank == 0:
         print(json.dumps(line), flush=True)
