@@ -216,6 +216,31 @@ def test_batching_does_not_change_results():
             assert np.array_equal(a, b)
 
 
+def test_failed_scratch_allocation_halves_the_batch():
+    """A scratch bound larger than the free device memory: the first allocation fails,
+    the batch is halved, and the results equal those of the default context."""
+    import trellis_coded_weight_amd as T
+    K = 2
+    per_tile = T.scratch_per_tile(K)
+    free, _ = torch.cuda.mem_get_info()
+    n = int(1.25 * free / per_tile) + 1               # one batch would not fit
+    print("\nhalving: %d tiles, %.1f GB free" % (n, free / 1e9), flush=True)
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    x = torch.randn(n, 256, generator=gen, device=DEV)
+    with T.Context(0, scratch_bytes=n * per_tile) as big:
+        big.set_timing(True)
+        p1, _, e1 = big.encode_tiles(x, K, 1.0, want_states=False)
+        torch.cuda.synchronize()
+        _, launches, tiles = big.read_timing("fwd1")
+        big.set_timing(False)
+        assert launches >= 2 and tiles == n
+        p1, e1 = p1.cpu(), e1.cpu()
+    with T.Context(0) as small:
+        p2, _, e2 = small.encode_tiles(x, K, 1.0, want_states=False)
+        torch.cuda.synchronize()
+    assert torch.equal(p1, p2.cpu()) and torch.equal(e1, e2.cpu())
+
+
 def test_errors_leave_outputs_untouched(ctx):
     import trellis_coded_weight_amd as T
     x = torch.zeros(2, 256, device=DEV)

@@ -171,6 +171,40 @@ int ensure_small(exl3_ctx *ctx, size_t n) {
     return EXL3_OK;
 }
 
+// Admission of a batch of tiles: the largest number whose backpointer scratch
+// fits the context's bound (whole rounds of one tile per compute unit when
+// several batches are needed, so no batch ends in a mostly idle round).  If the
+// device allocation fails, the batch is halved and tried again; the scratch is
+// released before each attempt, never held twice.  Results do not depend on
+// the batch size.
+int admit_batch(exl3_ctx *ctx, int64_t n, int K, int64_t *batch_out) {
+    const size_t per_tile = exl3::bp_bytes_per_tile(K);
+    const size_t max_batch = ctx->scratch_limit / per_tile;
+    if (max_batch == 0)
+        return fail(ctx, EXL3_ENOMEM, "scratch limit %zu B is below one tile's %zu B",
+                    ctx->scratch_limit, per_tile);
+    int64_t batch = (int64_t)std::min<size_t>((size_t)n, max_batch);
+    if (batch < n && batch > ctx->n_cu) batch -= batch % ctx->n_cu;
+    bool retried = false;
+    for (;;) {
+        size_t bytes_cap = ctx->bp_cap;
+        char *bp = static_cast<char *>(ctx->d_bp);
+        int rc = ensure(ctx, bp, bytes_cap, (size_t)batch * per_tile);
+        ctx->d_bp = bp;
+        ctx->bp_cap = bytes_cap;
+        if (rc == EXL3_OK) break;
+        if (rc != EXL3_ENOMEM || batch == 1) return rc;
+        batch = std::max<int64_t>(1, batch / 2);
+        if (batch > ctx->n_cu) batch -= batch % ctx->n_cu;
+        retried = true;
+    }
+    int rc = ensure_small(ctx, (size_t)batch);
+    if (rc != EXL3_OK) return rc;
+    if (retried) ctx->err.clear();     // the failed attempts are not the call's error
+    *batch_out = batch;
+    return EXL3_OK;
+}
+
 int ensure_aux(exl3_ctx *ctx) {
     if (ctx->aux) return EXL3_OK;
     EXL3_HIP(ctx, hipStreamCreateWithFlags(&ctx->aux, hipStreamNonBlocking));
@@ -233,22 +267,9 @@ int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, i
                  float scale, uint16_t *packed, uint16_t *states, float *sse, float *w_hat,
                  float *cost_only) {
     if (n == 0) return EXL3_OK;
-    const size_t per_tile = exl3::bp_bytes_per_tile(K);
-    const size_t max_batch = ctx->scratch_limit / per_tile;
-    if (max_batch == 0)
-        return fail(ctx, EXL3_ENOMEM, "scratch limit %zu B is below one tile's %zu B",
-                    ctx->scratch_limit, per_tile);
-    int64_t batch = (int64_t)std::min<size_t>((size_t)n, max_batch);
-    // when several batches are needed, keep each a whole number of rounds of
-    // one tile per compute unit so no batch ends in a mostly idle round
-    if (batch < n && batch > ctx->n_cu) batch -= batch % ctx->n_cu;
+    int64_t batch = 0;
     int rc;
-    size_t bytes_cap = ctx->bp_cap;
-    char *bp = static_cast<char *>(ctx->d_bp);
-    if ((rc = ensure(ctx, bp, bytes_cap, (size_t)batch * per_tile)) != EXL3_OK) return rc;
-    ctx->d_bp = bp;
-    ctx->bp_cap = bytes_cap;
-    if ((rc = ensure_small(ctx, (size_t)batch)) != EXL3_OK) return rc;
+    if ((rc = admit_batch(ctx, n, K, &batch)) != EXL3_OK) return rc;
     if (cost_only && idx && batch == n && n > ctx->n_cu && n % ctx->n_cu != 0 &&
         n % ctx->n_cu <= ctx->n_cu / 8)
         return probe_split(ctx, x, idx, n, K, scale, cost_only);
@@ -287,20 +308,9 @@ int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, i
 int encode_chain_f16(exl3_ctx *ctx, const uint16_t *x, int64_t n, int K, uint16_t *packed,
                      uint16_t *states, uint16_t *cost) {
     if (n == 0) return EXL3_OK;
-    const size_t per_tile = exl3::bp_bytes_per_tile(K);
-    const size_t max_batch = ctx->scratch_limit / per_tile;
-    if (max_batch == 0)
-        return fail(ctx, EXL3_ENOMEM, "scratch limit %zu B is below one tile's %zu B",
-                    ctx->scratch_limit, per_tile);
-    int64_t batch = (int64_t)std::min<size_t>((size_t)n, max_batch);
-    if (batch < n && batch > ctx->n_cu) batch -= batch % ctx->n_cu;
+    int64_t batch = 0;
     int rc;
-    size_t bytes_cap = ctx->bp_cap;
-    char *bp = static_cast<char *>(ctx->d_bp);
-    if ((rc = ensure(ctx, bp, bytes_cap, (size_t)batch * per_tile)) != EXL3_OK) return rc;
-    ctx->d_bp = bp;
-    ctx->bp_cap = bytes_cap;
-    if ((rc = ensure_small(ctx, (size_t)batch)) != EXL3_OK) return rc;
+    if ((rc = admit_batch(ctx, n, K, &batch)) != EXL3_OK) return rc;
     uint16_t *cost_tmp = reinterpret_cast<uint16_t *>(ctx->d_cost);
     for (int64_t i0 = 0; i0 < n; i0 += batch) {
         const int64_t nb = std::min<int64_t>(batch, n - i0);
