@@ -286,6 +286,43 @@ def layer_mode(ctx):
     return res
 
 
+def other_workloads(ctx):
+    """The remaining workloads at their own K: the 64x64 fp32 matrix at fixed scale
+    (latency, median of 100 calls), the heavy-tailed 4096x4096 at K = 4 and the two
+    MLP-shaped matrices at K = 3 (golden-section search; inputs uploaded before timing)."""
+    import torch
+    import workloads
+    dev = torch.device("cuda", 0)
+    out = {}
+    m = workloads.config(1)[0]
+    w = torch.from_numpy(m.w).to(dev)
+    su, sv = torch.from_numpy(m.su).to(dev), torch.from_numpy(m.sv).to(dev)
+    ts = []
+    for _ in range(101):
+        t0 = time.perf_counter()
+        ctx.quantize_matrix(w, m.K, su, sv, had_block=m.had_block, gss=None, scale=m.fixed_scale)
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    med = sorted(ts[1:])[50]
+    out["64x64_fp32_k2_fixed_scale"] = {"median_ms": round(1000 * med, 4),
+                                        "tiles_per_s": round(m.n_tiles / med, 1)}
+    for n, key, reps in ((3, "4096x4096_heavy_tailed_k4", 2), (4, "mlp_4096x12288_12288x4096_k3", 1)):
+        mats = [(torch.from_numpy(x.w).to(torch.bfloat16).to(dev), torch.from_numpy(x.su).to(dev),
+                 torch.from_numpy(x.sv).to(dev), x) for x in workloads.config(n)]
+        ctx.quantize_matrix(mats[0][0], mats[0][3].K, mats[0][1], mats[0][2], gss=mats[0][3].gss)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            for w, su, sv, x in mats:
+                ctx.quantize_matrix(w, x.K, su, sv, gss=x.gss)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / reps
+        tiles = sum(x.n_tiles for _, _, _, x in mats)
+        out[key] = {"tiles": tiles, "s": round(dt, 3), "tiles_per_s": round(tiles / dt, 1)}
+        del mats
+    return out
+
+
 def run_steps(ctx, w, su, sv, K, gss, steps):
     import torch
     out = None
@@ -305,7 +342,8 @@ def main():
     ap.add_argument("--no-other-k", action="store_true",
                     help="skip the K=3 and K=4 runs on the same matrix")
     ap.add_argument("--no-layer", action="store_true",
-                    help="skip the transformer-layer run (seven matrices at K = 2, 3, 4)")
+                    help="skip the transformer-layer run (seven matrices at K = 2, 3, 4) and "
+                         "the other workloads (64x64, heavy-tailed K=4, MLP K=3)")
     ap.add_argument("--no-grid", action="store_true",
                     help="skip the grid + parabolic scale-search run on the same matrix")
     ap.add_argument("--no-ldlq", action="store_true",
@@ -430,6 +468,7 @@ def main():
     ldlq = None if args.no_ldlq else ldlq_mode(ctx, m, w, su, sv, args.steps)
     grid = None if args.no_grid else grid_mode(ctx, w, su, sv, n_tiles, args.steps)
     layer = None if args.no_layer else layer_mode(ctx)
+    others = None if args.no_layer else other_workloads(ctx)
 
     cpu = None
     if not args.no_cpu_baseline and rank == 0:
@@ -466,6 +505,7 @@ def main():
         "ldlq_mode": ldlq,
         "grid_search_mode": grid,
         "layer_mode": layer,
+        "other_workloads": others,
     }
     if rank == 0:
         print(json.dumps(line), flush=True)
