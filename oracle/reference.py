@@ -288,6 +288,40 @@ def unregularize(w_reg, su, sv, B):
     return (y * np.asarray(su, np.float32)[:, None]) * np.asarray(sv, np.float32)[None, :]
 
 
+CHANNEL_FLOOR = 0.1
+
+
+def channel_normalize(w, su, floor=CHANNEL_FLOOR):
+    """Out-channel RMS normalization with the scale folded into the sign vector.
+
+    [P1 item 8: out-channel RMS normalization, sign + scale folding, the
+    zero-channel floor and the zero-sign rule.]  The output channels are the
+    rows of W (the LDLQ factor acts on the columns, the input side), so the
+    scale folds into su.  Per row i, in this order:
+      r_i  = sqrt(sum_j (double)w_ij^2 / C), j ascending, binary64;
+      r_i  = floor if r_i == 0 (an all-zero channel), and su'_i = 0;
+      f_i  = (float)(1.0 / r_i)              (binary64 divide, one rounding);
+      w'_ij = rn32(w_ij * f_i);  su'_i = su_i * (float)r_i.
+    Regularizing W' with the +-1 su and decoding with su' gives back W up to
+    the roundings of f_i, w' and (float)r_i.  Returns (w', su', r) with r the
+    binary64 rms before the floor.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    su = np.asarray(su, dtype=np.float32)
+    R, C = w.shape
+    r = np.empty(R, dtype=np.float64)
+    for i in range(R):
+        acc = 0.0
+        for val in w[i].tolist():
+            acc += val * val                 # binary64; the square of a binary32 is exact
+        r[i] = math.sqrt(acc / C)
+    r_eff = np.where(r == 0.0, float(floor), r)
+    f = np.array([np.float32(1.0 / x) for x in r_eff.tolist()], dtype=np.float32)
+    w_n = (w * f[:, None]).astype(np.float32)
+    su_f = np.where(r == 0.0, np.float32(0.0), su * r.astype(np.float32)).astype(np.float32)
+    return np.ascontiguousarray(w_n), su_f, r
+
+
 def to_tiles(m):
     """[R, C] -> [R/16 * C/16, 256]; tile tr*TC + tc, element 16*r + c."""
     R, C = m.shape

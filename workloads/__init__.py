@@ -15,6 +15,9 @@ here.  Matrices of the same shapes and value distributions stand in for them:
   5  one transformer layer's projections (q, k, v, o, gate, up, down), bf16,
      N(0, 0.02^2), each at K=2, 3 and 4, scale search
 
+For the out-channel normalization, ``channel_spread`` draws rows of unequal
+scale (log-normal spread of the row std) with a few all-zero rows.
+
 Seeds: weights use PCG64(1000 + config), signs PCG64(2000 + config); matrix m of
 the layer set uses PCG64(10000 + m) and PCG64(20000 + m).  Signs are drawn as
 2*integers(0, 2) - 1.  bf16 values come from torch's round-to-nearest-even cast.
@@ -95,6 +98,25 @@ def heavy_tailed(rows, cols, seed_w, seed_s, K=4, gss=GSS_DEFAULT, name="w"):
     w = to_bf16_values(w)
     rs = np.random.Generator(np.random.PCG64(seed_s))
     return Matrix(name, w, "bf16", signs(rs, rows), signs(rs, cols), 128, K, gss)
+
+
+def channel_spread(rows, cols, seed_w, seed_s, std=0.02, spread=0.5, dead=0.002, K=2,
+                   bf16=True, gss=GSS_DEFAULT, name="w"):
+    """Rows (output channels) of unequal scale, as trained projections have.
+
+    Row i is N(0, (std * exp(spread * z_i))^2) with z_i ~ N(0, 1); round(dead *
+    rows) rows (at least one when dead > 0), chosen from the same seed, are all
+    zero (dead channels).  Signs as for the other workloads."""
+    rw = np.random.Generator(np.random.PCG64(seed_w))
+    row_std = std * np.exp(spread * rw.standard_normal(rows))
+    w = (rw.standard_normal((rows, cols)) * row_std[:, None]).astype(np.float32)
+    n_dead = max(1, int(round(dead * rows))) if dead > 0 else 0
+    w[rw.choice(rows, size=n_dead, replace=False)] = 0.0
+    if bf16:
+        w = to_bf16_values(w)
+    rs = np.random.Generator(np.random.PCG64(seed_s))
+    return Matrix(name, w, "bf16" if bf16 else "f32", signs(rs, rows), signs(rs, cols), 128, K,
+                  gss)
 
 
 def config(n: int) -> List[Matrix]:
