@@ -256,6 +256,44 @@ def grid_mode(ctx, w, su, sv, n_tiles, steps):
             "scale": out["scale"], "mse": out["mse"]}
 
 
+def channel_mode(ctx, n_tiles, steps):
+    """Out-channel RMS normalization on a 4096x4096 bf16 matrix whose rows have
+    unequal scale (log-normal spread, 0.2% all-zero rows): the normalization
+    kernel alone (median of 20 calls; HBM-bound: 2 B read and 4 B written per
+    element), then normalization + K = 2 quantization with the golden section."""
+    import torch
+    import workloads
+    dev = torch.device("cuda", 0)
+    m = workloads.channel_spread(4096, 4096, 1002, 2002)
+    w = torch.from_numpy(m.w).to(torch.bfloat16).to(dev)
+    su, sv = torch.from_numpy(m.su).to(dev), torch.from_numpy(m.sv).to(dev)
+    ctx.channel_normalize(w, su)
+    ts = []
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ctx.channel_normalize(w, su)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = sorted(ts)[10]
+    nbytes = 4096 * 4096 * (2 + 4)
+    n = max(1, steps // 2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        w_n, su_f, _ = ctx.channel_normalize(w, su)
+        out = ctx.quantize_matrix(w_n, 2, su, sv, gss=m.gss)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / n
+    return {"workload": "4096x4096 bf16, row std 0.02*exp(0.5 z), 8 all-zero rows; K=2, "
+                        "golden-section scale",
+            "normalize_ms": round(ms, 4),
+            "normalize_gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "normalize_hbm_frac": round(nbytes / (ms * 1e-3) / 8e12, 4),
+            "tiles_per_s": round(n_tiles / dt, 1), "scale": out["scale"], "mse": out["mse"]}
+
+
 def layer_mode(ctx):
     """One transformer layer's seven matrices (q, k, v, o, gate, up, down; 753,664
     tiles, uploaded before timing) quantized back to back on one stream with the
@@ -345,7 +383,8 @@ def main():
                     help="skip the transformer-layer run (seven matrices at K = 2, 3, 4) and "
                          "the other workloads (64x64, heavy-tailed K=4, MLP K=3)")
     ap.add_argument("--no-grid", action="store_true",
-                    help="skip the grid + parabolic scale-search run on the same matrix")
+                    help="skip the grid + parabolic scale-search run on the same matrix and "
+                         "the out-channel normalization run")
     ap.add_argument("--no-ldlq", action="store_true",
                     help="skip the LDLQ (error feedback) run on the same matrix")
     ap.add_argument("--no-f16", action="store_true",
@@ -467,6 +506,7 @@ def main():
     f16 = None if args.no_f16 else f16_mode(ctx, w, su, sv, out["scale"], n_tiles, args.steps)
     ldlq = None if args.no_ldlq else ldlq_mode(ctx, m, w, su, sv, args.steps)
     grid = None if args.no_grid else grid_mode(ctx, w, su, sv, n_tiles, args.steps)
+    chan = None if args.no_grid else channel_mode(ctx, n_tiles, args.steps)
     layer = None if args.no_layer else layer_mode(ctx)
     others = None if args.no_layer else other_workloads(ctx)
 
@@ -504,6 +544,7 @@ def main():
         "f16_mode": f16,
         "ldlq_mode": ldlq,
         "grid_search_mode": grid,
+        "channel_norm_mode": chan,
         "layer_mode": layer,
         "other_workloads": others,
     }

@@ -113,6 +113,32 @@ int exl3_regularize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int col
                     int out_layout, float *tile_sumsq, int *nonfinite);
 
 /*
+ * Out-channel RMS normalization with the scale folded into the row signs
+ * [P1 section 8: out-channel RMS normalization, sign + scale folding, the
+ * zero-channel floor, a zero sign for all-zero channels].  The output channels
+ * are the rows of W (the LDLQ factor of exl3_quantize_matrix_ldlq acts on the
+ * columns, the input side).  Per row i:
+ *   r_i        = sqrt(sum_j w_ij^2 / cols) in binary64, j ascending
+ *   f_i        = (float)(1.0 / r_i), with r_i replaced by `floor` (the pages:
+ *                0.1) when it is 0
+ *   w_norm_ij  = rn32(w_ij * f_i)
+ *   su_folded_i = su_i * (float)r_i, or +0 when r_i is 0
+ * Quantizing w_norm with the +-1 signs su and decoding with su_folded in
+ * place of su gives back W (up to the roundings above).
+ *   w          [rows][cols] row-major, w_dtype EXL3_F32 or EXL3_BF16
+ *   su         float [rows], every entry exactly +1 or -1
+ *   w_norm     float [rows][cols] row-major; must not overlap w
+ *   su_folded  float [rows]
+ *   row_rms    optional double [rows]: r_i before the floor
+ * Non-finite weights give non-finite rows of w_norm (exl3_quantize_matrix
+ * then rejects them).  rows, cols >= 1; floor finite and > 0.  Asynchronous.
+ * Errors: EXL3_EINVAL, EXL3_EHIP.
+ */
+int exl3_channel_normalize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
+                           const float *su, double floor, float *w_norm, float *su_folded,
+                           double *row_rms);
+
+/*
  * Encode n tiles at a fixed binary32 scale [P1 sections 1, 4, 5]:
  * a two-pass tail-biting Viterbi search over the 16-bit bitshift trellis that
  * shifts in K bits per step, comparing each input with v[s] = rn(scale*c[s]).

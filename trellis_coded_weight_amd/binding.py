@@ -29,7 +29,7 @@ EXL3_TILE_MAJOR = 1
 EXPORTED = [
     "exl3_version", "exl3_ctx_create", "exl3_ctx_destroy", "exl3_last_error",
     "exl3_ctx_set_stream", "exl3_set_codebook", "exl3_get_codebook", "exl3_regularize",
-    "exl3_encode_tiles", "exl3_encode_tiles_f16", "exl3_decode_tiles", "exl3_quantize_matrix",
+    "exl3_channel_normalize", "exl3_encode_tiles", "exl3_encode_tiles_f16", "exl3_decode_tiles", "exl3_quantize_matrix",
     "exl3_quantize_matrix_ldlq", "exl3_quantize_matrix_grid", "exl3_scratch_per_tile",
     "exl3_ctx_set_timing", "exl3_ctx_read_timing",
 ]
@@ -92,6 +92,8 @@ def load_library():
     lib.exl3_get_codebook.argtypes = [vp, vp]
     lib.exl3_regularize.restype = i32
     lib.exl3_regularize.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
+    lib.exl3_channel_normalize.restype = i32
+    lib.exl3_channel_normalize.argtypes = [vp, vp, i32, i32, i32, vp, f64, vp, vp, vp]
     lib.exl3_encode_tiles.restype = i32
     lib.exl3_encode_tiles.argtypes = [vp, vp, i64, i32, f32, vp, vp, vp]
     lib.exl3_encode_tiles_f16.restype = i32
@@ -239,6 +241,23 @@ class Context:
             _ptr(sv.contiguous()), _ptr(out), EXL3_TILE_MAJOR if tile_major else EXL3_ROW_MAJOR,
             _ptr(sums), _ptr(flag)))
         return out, sums, flag
+
+    def channel_normalize(self, w: torch.Tensor, su: torch.Tensor, floor: float = 0.1):
+        """Out-channel RMS normalization: returns (w_norm float32 [rows, cols],
+        su_folded float32 [rows], row_rms float64 [rows])."""
+        rows, cols = w.shape
+        dt = {torch.float32: EXL3_F32, torch.bfloat16: EXL3_BF16}.get(w.dtype)
+        if dt is None:
+            raise ValueError("w must be float32 or bfloat16")
+        w = w.contiguous()
+        out = torch.empty(rows, cols, dtype=torch.float32, device=w.device)
+        su_f = torch.empty(rows, dtype=torch.float32, device=w.device)
+        rms = torch.empty(rows, dtype=torch.float64, device=w.device)
+        self._sync_stream()
+        self._check(self.lib.exl3_channel_normalize(
+            self.handle, _ptr(w), dt, rows, cols, _ptr(su.contiguous()), float(floor), _ptr(out),
+            _ptr(su_f), _ptr(rms)))
+        return out, su_f, rms
 
     def encode_tiles(self, x: torch.Tensor, K: int, scale: float, want_states: bool = True,
                      want_sse: bool = True):

@@ -17,7 +17,7 @@ LIB = os.path.join(OUT_DIR, "libexl3_gfx950.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.hip", "viterbi_fwd.hip", "viterbi_fwd_f16.hip", "traceback.hip", "regularize.hip",
-           "ldlq.hip", "codebook.cpp"]
+           "channel.hip", "ldlq.hip", "codebook.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

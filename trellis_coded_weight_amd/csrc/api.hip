@@ -507,6 +507,29 @@ int exl3_regularize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int col
     return EXL3_OK;
 }
 
+int exl3_channel_normalize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
+                           const float *su, double floor, float *w_norm, float *su_folded,
+                           double *row_rms) {
+    if (!ctx) return EXL3_EINVAL;
+    if (!w || !su || !w_norm || !su_folded)
+        return fail(ctx, EXL3_EINVAL, "null weight, sign or output pointer");
+    if (w_dtype != EXL3_F32 && w_dtype != EXL3_BF16)
+        return fail(ctx, EXL3_EINVAL, "weight dtype %d is not EXL3_F32 or EXL3_BF16", w_dtype);
+    if (rows <= 0 || cols <= 0) return fail(ctx, EXL3_EINVAL, "shape %d x %d", rows, cols);
+    if (!(floor > 0.0) || !std::isfinite(floor))
+        return fail(ctx, EXL3_EINVAL, "zero-channel floor %g is not finite and positive", floor);
+    const size_t in_bytes = (size_t)rows * cols * (w_dtype == EXL3_BF16 ? 2 : 4);
+    const char *wb = static_cast<const char *>(w), *ob = reinterpret_cast<const char *>(w_norm);
+    if (ob < wb + in_bytes && wb < ob + (size_t)rows * cols * sizeof(float))
+        return fail(ctx, EXL3_EINVAL, "w_norm overlaps w");
+    int rc;
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    if ((rc = check_signs(ctx, su, rows, "su")) != EXL3_OK) return rc;
+    EXL3_HIP(ctx, exl3::launch_channel_normalize(w, w_dtype, rows, cols, su, floor, w_norm,
+                                                 su_folded, row_rms, ctx->stream));
+    return EXL3_OK;
+}
+
 int exl3_encode_tiles(exl3_ctx *ctx, const float *x, int64_t n, int K, float scale,
                       uint16_t *packed, uint16_t *states, float *tile_sse) {
     if (!ctx) return EXL3_EINVAL;
