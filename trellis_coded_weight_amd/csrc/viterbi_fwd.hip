@@ -377,8 +377,14 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
     // at a time so both buffer addresses are constants.  Pass 1 keeps
     // backpointers only from step 127 on (odd), pass 2 from step 0.
     constexpr int t_first = (PASS == 1) ? 127 : 0;
+    // At K = 2 the second buffer starts 64 KiB in, past the 16-bit immediate
+    // offsets of the LDS instructions; with its offset opaque to the compiler
+    // both buffers are addressed as one base register plus immediates
+    // (ds_read2st64 / ds_write_b128), not one address register per access.
+    int b1_off = (NBUF - 1) * G::T;
+    if constexpr (G::T * sizeof(float) >= 65536) asm volatile("" : "+v"(b1_off));
     float *const B0 = Mbuf[0];
-    float *const B1 = Mbuf[NBUF - 1];
+    float *const B1 = &Mbuf[0][0] + b1_off;
     float xt = xs[0];
     int t = 0;
     if constexpr (PASS == 1) {

@@ -57,9 +57,17 @@ constexpr uint32_t kSignBytes = 0x0B0A0908u;
 __device__ __forceinline__ uint32_t flag(h2 c, uint32_t guard) { return u32(c) - guard; }
 __device__ __forceinline__ uint32_t guard_of(h2 m) { return u32(m) + 0x80008001u; }
 
-// cond ? a : b, bitwise (only bits 15 and 31 matter)
+// cond ? a : b, bitwise (for a flag word only bits 15 and 31 of the result
+// matter; for a half mask whole halves are selected)
 __device__ __forceinline__ uint32_t sel(uint32_t cond, uint32_t a, uint32_t b) {
     return __builtin_amdgcn_bitop3_b32(a, b, cond, kSel);
+}
+
+// Flag word -> half mask: each half becomes all ones where its flag bit (15 or
+// 31) is set, all zeros otherwise (one v_pk_ashrrev_i16)
+__device__ __forceinline__ uint32_t half_mask(uint32_t f) {
+    typedef short s2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(s2, f) >> (s2){15, 15});
 }
 
 // Four flags -> bit `pos` of each byte of acc: byte 0 / 1 <- bit 15 / 31 of
@@ -112,12 +120,16 @@ struct AcsH<3, BITS> {
         const h2 m4567 = hmin3(m45, a[6], a[7]);
         const h2 m = hmin(m0123, m4567);
         if (BITS) {
+            // walk down with half masks: select the chosen subtree's left child
+            // first, then flag only that one
             const uint32_t gd = guard_of(m);
             r[2] = flag(m0123, gd);                                   // index in 4..7
-            r[1] = sel(r[2], flag(m45, gd), flag(m01, gd));
-            const uint32_t lo = sel(r[1], flag(a[2], gd), flag(a[0], gd));
-            const uint32_t hi = sel(r[1], flag(a[6], gd), flag(a[4], gd));
-            r[0] = sel(r[2], hi, lo);
+            const uint32_t k2 = half_mask(r[2]);
+            r[1] = flag(as_h2(sel(k2, u32(m45), u32(m01))), gd);
+            const uint32_t k1 = half_mask(r[1]);
+            const uint32_t e0 = sel(k2, u32(a[4]), u32(a[0]));
+            const uint32_t e1 = sel(k2, u32(a[6]), u32(a[2]));
+            r[0] = flag(as_h2(sel(k1, e1, e0)), gd);
         }
         return m;
     }
@@ -139,17 +151,20 @@ struct AcsH<4, BITS> {
         if (BITS) {
             const uint32_t gd = guard_of(m);
             r[3] = flag(m0_7, gd);                                    // index in 8..15
-            r[2] = sel(r[3], flag(m8_11, gd), flag(m0_3, gd));
-            const uint32_t qlo = sel(r[2], flag(m45, gd), flag(m01, gd));
-            const uint32_t qhi = sel(r[2], flag(mCD, gd), flag(m89, gd));
-            r[1] = sel(r[3], qhi, qlo);
-            const uint32_t p0 = sel(r[1], flag(a[2], gd), flag(a[0], gd));
-            const uint32_t p1 = sel(r[1], flag(a[6], gd), flag(a[4], gd));
-            const uint32_t p2 = sel(r[1], flag(a[10], gd), flag(a[8], gd));
-            const uint32_t p3 = sel(r[1], flag(a[14], gd), flag(a[12], gd));
-            const uint32_t h0 = sel(r[2], p1, p0);
-            const uint32_t h1 = sel(r[2], p3, p2);
-            r[0] = sel(r[3], h1, h0);
+            const uint32_t k3 = half_mask(r[3]);
+            r[2] = flag(as_h2(sel(k3, u32(m8_11), u32(m0_3))), gd);  // left quad of the half
+            const uint32_t k2 = half_mask(r[2]);
+            const uint32_t plo = sel(k3, u32(m89), u32(m01));
+            const uint32_t phi = sel(k3, u32(mCD), u32(m45));
+            r[1] = flag(as_h2(sel(k2, phi, plo)), gd);               // left pair of the quad
+            const uint32_t k1 = half_mask(r[1]);
+            const uint32_t e0 = sel(k3, u32(a[8]), u32(a[0]));
+            const uint32_t e1 = sel(k3, u32(a[10]), u32(a[2]));
+            const uint32_t e2 = sel(k3, u32(a[12]), u32(a[4]));
+            const uint32_t e3 = sel(k3, u32(a[14]), u32(a[6]));
+            const uint32_t f0 = sel(k2, e2, e0);
+            const uint32_t f1 = sel(k2, e3, e1);
+            r[0] = flag(as_h2(sel(k1, f1, f0)), gd);                 // left leaf of the pair
         }
         return m;
     }
