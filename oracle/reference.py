@@ -122,6 +122,40 @@ def mul1_levels_fp16() -> np.ndarray:
     return z.astype(np.float16)                         # round-to-nearest-even
 
 
+# The two other procedural codebooks (README item 5 names them and prints their
+# counts of distinct levels, 10,746 and 10,598).  Both map a state to a 32-bit
+# word, keep the sign bit and 12 low bits of each 16-bit half and xor in a
+# fixed pattern, which puts each half's exponent field in 12..15, so each half
+# is a binary16 number of magnitude in [1/8, 2); the level is the binary16 sum
+# of the two halves.  3INST is the published three-instruction decoder of the
+# QTIP trellis codes (a 32-bit linear congruential step, the mask, the xor);
+# mcg replaces the congruential step by a multiplicative one, with the
+# multiplier chosen here (it reproduces the printed count).
+INST3_A, INST3_B = 89226354, 64248484
+MCG_MULTIPLIER = 0xCBAC1FED
+HALVES_MASK, HALVES_XOR = 0x8FFF8FFF, 0x3B603B60
+
+
+def _halves_sum_fp16(words: np.ndarray) -> np.ndarray:
+    m = (words & np.uint64(HALVES_MASK)) ^ np.uint64(HALVES_XOR)
+    lo = (m & np.uint64(0xFFFF)).astype(np.uint16).view(np.float16).astype(np.float64)
+    hi = (m >> np.uint64(16)).astype(np.uint16).view(np.float16).astype(np.float64)
+    return (lo + hi).astype(np.float16)        # exact binary64 sum, one RNE rounding
+
+
+def inst3_levels_fp16() -> np.ndarray:
+    s = np.arange(1 << STATE_BITS, dtype=np.uint64)
+    return _halves_sum_fp16((s * np.uint64(INST3_A) + np.uint64(INST3_B)) & np.uint64(0xFFFFFFFF))
+
+
+def mcg_levels_fp16() -> np.ndarray:
+    s = np.arange(1 << STATE_BITS, dtype=np.uint64)
+    return _halves_sum_fp16((s * np.uint64(MCG_MULTIPLIER)) & np.uint64(0xFFFFFFFF))
+
+
+CODEBOOKS = {"mul1": mul1_levels_fp16, "mcg": mcg_levels_fp16, "3inst": inst3_levels_fp16}
+
+
 def scaled_levels(levels_fp16: np.ndarray, scale) -> np.ndarray:
     """v[s] = rn(scale * level[s]) in binary32."""
     return (np.float32(scale) * levels_fp16.astype(np.float32)).astype(np.float32)
