@@ -256,6 +256,24 @@ def grid_mode(ctx, w, su, sv, n_tiles, steps):
             "scale": out["scale"], "mse": out["mse"]}
 
 
+def codebook_mode(ctx, w, su, sv, n_tiles):
+    """The same matrix at K = 2 with the mcg and 3INST level tables (golden
+    section; the kernels are the same, only the table differs)."""
+    import torch
+    out = {}
+    for name in ("mcg", "3inst"):
+        ctx.set_codebook_kind(name)
+        ctx.quantize_matrix(w, 2, su, sv, gss=(12, 0.5, 2.0))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        r = ctx.quantize_matrix(w, 2, su, sv, gss=(12, 0.5, 2.0))
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        out[name] = {"tiles_per_s": round(n_tiles / dt, 1), "scale": r["scale"], "mse": r["mse"]}
+    ctx.set_codebook_kind("mul1")
+    return out
+
+
 def channel_mode(ctx, n_tiles, steps):
     """Out-channel RMS normalization on a 4096x4096 bf16 matrix whose rows have
     unequal scale (log-normal spread, 0.2% all-zero rows): the normalization
@@ -378,7 +396,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tiles", type=int, default=8192)
     ap.add_argument("--no-other-k", action="store_true",
-                    help="skip the K=3 and K=4 runs on the same matrix")
+                    help="skip the K=3, K=4 and K=1 runs and the mcg / 3INST codebook runs "
+                         "on the same matrix")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the transformer-layer run (seven matrices at K = 2, 3, 4) and "
                          "the other workloads (64x64, heavy-tailed K=4, MLP K=3)")
@@ -503,6 +522,7 @@ def main():
             by_k[str(k2)] = round(n_tiles * max(1, args.steps // 2)
                                   / (time.perf_counter() - t2), 1)
 
+    codebooks = None if args.no_other_k else codebook_mode(ctx, w, su, sv, n_tiles)
     f16 = None if args.no_f16 else f16_mode(ctx, w, su, sv, out["scale"], n_tiles, args.steps)
     ldlq = None if args.no_ldlq else ldlq_mode(ctx, m, w, su, sv, args.steps)
     grid = None if args.no_grid else grid_mode(ctx, w, su, sv, n_tiles, args.steps)
@@ -536,6 +556,7 @@ def main():
         },
         "tile_encodes_per_s": round(encodes_per_s, 1),
         "tiles_per_s_by_K": by_k,
+        "codebooks_k2": codebooks,
         "scale": out["scale"],
         "mse": out["mse"],
         "stages_ms_per_step": stages,

@@ -92,6 +92,23 @@ int exl3_set_codebook(exl3_ctx *ctx, const uint16_t *levels_fp16_host);
 int exl3_get_codebook(exl3_ctx *ctx, uint16_t *levels_fp16_host);
 
 /*
+ * Select one of the procedural codebooks [P1 section 5: mul1, mcg, 3INST; the
+ * pages print their counts of distinct levels, 913, 10,746 and 10,598] as the
+ * level table of later calls (binary32 and binary16 modes, encode and decode).
+ *   EXL3_CB_MUL1   the default table (see exl3_set_codebook)
+ *   EXL3_CB_MCG    w = 0xCBAC1FED * s mod 2^32
+ *   EXL3_CB_3INST  w = 89226354 * s + 64248484 mod 2^32 (the QTIP three-
+ *                  instruction decoder)
+ * For mcg and 3INST, w = (w & 0x8FFF8FFF) ^ 0x3B603B60 and the level is the
+ * binary16 sum (round to nearest even) of w's two halves read as binary16.
+ * Levels of mcg and 3INST have a standard deviation near 1.24 (mul1: 1), so
+ * the best scale is near rms / 1.24, inside the default search bracket.
+ * Synchronizes the stream.  Errors: EXL3_EUNSUPPORTED (unknown kind), EXL3_EHIP.
+ */
+enum { EXL3_CB_MUL1 = 0, EXL3_CB_MCG = 1, EXL3_CB_3INST = 2 };
+int exl3_set_codebook_kind(exl3_ctx *ctx, int kind);
+
+/*
  * Regularize a weight matrix [P1 sections 7 and 8]:
  *   W_reg = H_l diag(su) W diag(sv) H_r
  * where H_l / H_r apply the natural-order Sylvester Hadamard of size had_block

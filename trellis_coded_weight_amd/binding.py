@@ -28,11 +28,13 @@ EXL3_TILE_MAJOR = 1
 
 EXPORTED = [
     "exl3_version", "exl3_ctx_create", "exl3_ctx_destroy", "exl3_last_error",
-    "exl3_ctx_set_stream", "exl3_set_codebook", "exl3_get_codebook", "exl3_regularize",
+    "exl3_ctx_set_stream", "exl3_set_codebook", "exl3_get_codebook", "exl3_set_codebook_kind",
+    "exl3_regularize",
     "exl3_channel_normalize", "exl3_encode_tiles", "exl3_encode_tiles_f16", "exl3_decode_tiles", "exl3_quantize_matrix",
     "exl3_quantize_matrix_ldlq", "exl3_quantize_matrix_grid", "exl3_scratch_per_tile",
     "exl3_ctx_set_timing", "exl3_ctx_read_timing",
 ]
+CODEBOOK_KINDS = {"mul1": 0, "mcg": 1, "3inst": 2}
 KERNEL_KINDS = {"fwd1": 0, "fwd2": 1, "tb1": 2, "tb2": 3, "regularize": 4, "fwd_side": 5}
 
 
@@ -89,6 +91,8 @@ def load_library():
     lib.exl3_set_codebook.restype = i32
     lib.exl3_set_codebook.argtypes = [vp, vp]
     lib.exl3_get_codebook.restype = i32
+    lib.exl3_set_codebook_kind.restype = i32
+    lib.exl3_set_codebook_kind.argtypes = [vp, i32]
     lib.exl3_get_codebook.argtypes = [vp, vp]
     lib.exl3_regularize.restype = i32
     lib.exl3_regularize.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
@@ -213,6 +217,11 @@ class Context:
         if lv.numel() != 65536:
             raise ValueError("need 65536 levels")
         self._check(self.lib.exl3_set_codebook(self.handle, ctypes.c_void_p(lv.data_ptr())))
+
+    def set_codebook_kind(self, name: str):
+        """Select a procedural codebook by name: "mul1", "mcg" or "3inst"."""
+        self._sync_stream()
+        self._check(self.lib.exl3_set_codebook_kind(self.handle, CODEBOOK_KINDS[name]))
 
     def get_codebook(self) -> torch.Tensor:
         out = torch.empty(65536, dtype=torch.int16)

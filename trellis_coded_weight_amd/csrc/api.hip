@@ -481,6 +481,23 @@ int exl3_set_codebook(exl3_ctx *ctx, const uint16_t *levels_fp16_host) {
     return EXL3_OK;
 }
 
+int exl3_set_codebook_kind(exl3_ctx *ctx, int kind) {
+    if (!ctx) return EXL3_EINVAL;
+    std::vector<uint16_t> lv(65536);
+    switch (kind) {
+        case EXL3_CB_MUL1: exl3::build_mul1_levels(lv.data()); break;
+        case EXL3_CB_MCG: exl3::build_mcg_levels(lv.data()); break;
+        case EXL3_CB_3INST: exl3::build_3inst_levels(lv.data()); break;
+        default: return fail(ctx, EXL3_EUNSUPPORTED, "codebook kind %d (supported: 0, 1, 2)", kind);
+    }
+    int rc;
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    EXL3_HIP(ctx, hipMemcpyAsync(ctx->d_levels, lv.data(), 65536 * sizeof(uint16_t),
+                                 hipMemcpyHostToDevice, ctx->stream));
+    EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    return EXL3_OK;
+}
+
 int exl3_get_codebook(exl3_ctx *ctx, uint16_t *levels_fp16_host) {
     if (!ctx || !levels_fp16_host) return fail(ctx, EXL3_EINVAL, "null argument");
     int rc;

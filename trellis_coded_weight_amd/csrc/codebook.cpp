@@ -1,4 +1,5 @@
-// Host generator of the mul1 level table used by the gfx950 encoder.
+// Host generators of the level tables used by the gfx950 encoder: mul1 (the
+// default), mcg and 3INST.
 //
 // Source: "EXL3 Intel Arc Quantizer" README, Core Implemented Architecture
 // section 5 names the mul1 procedural codebook (a level for each 16-bit state;
@@ -65,5 +66,40 @@ void build_mul1_levels(uint16_t *out) {
         out[s] = f64_to_f16_bits(z);
     }
 }
+
+// mcg and 3INST [P1 section 5 names them and prints their counts of distinct
+// levels, 10,746 and 10,598].  A state gives a 32-bit word: 3INST is the
+// published three-instruction decoder of the QTIP trellis codes (linear
+// congruential step w = a*s + b mod 2^32), mcg a multiplicative step
+// w = A*s mod 2^32 (A chosen here; it gives the printed count).  Then
+// w = (w & 0x8FFF8FFF) ^ 0x3B603B60 leaves each 16-bit half a binary16 number
+// of magnitude [1/8, 2) (exponent field 12..15), and the level is the
+// binary16 round-to-nearest-even of the sum of the two halves (the binary64
+// sum of two such numbers is exact).
+namespace {
+
+constexpr uint32_t kInst3A = 89226354u, kInst3B = 64248484u;
+constexpr uint32_t kMcgA = 0xCBAC1FEDu;
+
+double f16_bits_to_double(uint16_t h) {
+    const int e = (h >> 10) & 0x1F;
+    const int f = h & 0x3FF;
+    double v = e == 0 ? std::ldexp((double)f, -24) : std::ldexp((double)(1024 + f), e - 25);
+    return (h & 0x8000u) ? -v : v;
+}
+
+void build_halves_sum(uint32_t a, uint32_t b, uint16_t *out) {
+    for (uint32_t s = 0; s < 65536u; ++s) {
+        const uint32_t w = ((a * s + b) & 0x8FFF8FFFu) ^ 0x3B603B60u;
+        const double sum = f16_bits_to_double((uint16_t)(w & 0xFFFFu)) +
+                           f16_bits_to_double((uint16_t)(w >> 16));
+        out[s] = f64_to_f16_bits(sum);
+    }
+}
+
+}  // namespace
+
+void build_mcg_levels(uint16_t *out) { build_halves_sum(kMcgA, 0u, out); }
+void build_3inst_levels(uint16_t *out) { build_halves_sum(kInst3A, kInst3B, out); }
 
 }  // namespace exl3

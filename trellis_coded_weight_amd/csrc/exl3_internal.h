@@ -173,7 +173,9 @@ hipError_t launch_decode(const uint16_t *packed, int64_t n, int K, float scale,
 hipError_t launch_gather_tiles(const float *src, const int32_t *idx, int64_t n, float *dst,
                                hipStream_t stream);
 
-// Host-side generator of the mul1 level table (fp16 bit patterns).
+// Host-side generators of the level tables (fp16 bit patterns).
 void build_mul1_levels(uint16_t *out65536);
+void build_mcg_levels(uint16_t *out65536);
+void build_3inst_levels(uint16_t *out65536);
 
 }  // namespace exl3

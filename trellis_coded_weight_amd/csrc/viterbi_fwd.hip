@@ -382,7 +382,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
     // both buffers are addressed as one base register plus immediates
     // (ds_read2st64 / ds_write_b128), not one address register per access.
     int b1_off = (NBUF - 1) * G::T;
-    if constexpr (G::T * sizeof(float) >= 65536) asm volatile("" : "+v"(b1_off));
+    if constexpr (NBUF == 2 && G::T * sizeof(float) >= 65536) asm volatile("" : "+v"(b1_off));
     float *const B0 = Mbuf[0];
     float *const B1 = &Mbuf[0][0] + b1_off;
     float xt = xs[0];
