@@ -13,40 +13,77 @@
 // binary32 operation (this file is built with -ffp-contract=off).  One
 // workgroup of 256 lanes per tile row: lane (r, c) owns one element; the
 // tile's error blocks E(tr, i) and the factor blocks L_ij of 16 later spans at
-// a time are staged in LDS (one round trip to memory per 16 spans).
+// a time are staged in LDS, the next 16 loading while the current ones are
+// summed.
 #include "exl3_internal.h"
 
 namespace exl3 {
 namespace {
 
 constexpr int kBlocksPerChunk = 16;   // later spans staged in LDS per round trip
+constexpr int kLtPad = 20;            // row pitch of the transposed factor blocks (16-byte aligned)
 
+// Target of span j for tile row tr = blockIdx.x, lane (r, c) = element 16r + c.
+// Chunks of 16 later spans are double-buffered: the global loads of chunk n+1
+// are in flight while chunk n is summed from LDS.  The factor blocks are
+// stored transposed so that both operands of a lane's 16-term sum are read 4
+// at a time (ds_read_b128): the error row E(tr, i)[r][0..15] and the factor
+// column L_ij[0..15][c].
 __global__ void __launch_bounds__(256)
 ldlq_target_kernel(const float *__restrict__ w_tiles, const float *__restrict__ e_tiles,
                    const float *__restrict__ L, int TC, int j, float *__restrict__ target) {
-    // error blocks E(tr, i) and factor blocks L_ij of up to 16 later spans at a
-    // time (32 KiB); reads of a row of Es / a column of Ls are bank-conflict-free
-    __shared__ float Es[kBlocksPerChunk][16][16];
-    __shared__ float Ls[kBlocksPerChunk][16][16];
+    __shared__ __attribute__((aligned(16))) float Es[2][kBlocksPerChunk][16][16];
+    __shared__ __attribute__((aligned(16))) float Lt[2][kBlocksPerChunk][16][kLtPad];
     const int tr = blockIdx.x;
     const int e = threadIdx.x, r = e >> 4, c = e & 15;
     const size_t C = (size_t)TC * 16;
     float acc = w_tiles[((size_t)tr * TC + j) * 256 + e];
-    for (int i0 = j + 1; i0 < TC; i0 += kBlocksPerChunk) {
-        const int ni = (TC - i0) < kBlocksPerChunk ? (TC - i0) : kBlocksPerChunk;
-        for (int q = 0; q < ni; ++q) {
-            const int i = i0 + q;
-            Es[q][r][c] = e_tiles[((size_t)tr * TC + i) * 256 + e];          // E[16tr + r][16i + c]
-            Ls[q][r][c] = L[(size_t)(16 * i + r) * C + 16 * (size_t)j + c];  // L[16i + r][16j + c]
-        }
-        __syncthreads();
-        for (int q = 0; q < ni; ++q) {
+    // take the load's wait here, once, not at acc's first use inside the loop
+    // (where it would also wait for the next chunk's loads)
+    asm volatile("" : "+v"(acc));
+    const int n_later = TC - 1 - j;
+    const int n_chunks = (n_later + kBlocksPerChunk - 1) / kBlocksPerChunk;
+    float pe[kBlocksPerChunk], pl[kBlocksPerChunk];
+    // loads of chunk n into registers (spans i = j + 1 + 16n + q)
+    auto fetch = [&](int n) {
+        const int i0 = j + 1 + n * kBlocksPerChunk;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const float p = Es[q][r][t] * Ls[q][t][c];
-                acc = acc + p;
+        for (int q = 0; q < kBlocksPerChunk; ++q) {
+            // past the last span: a valid address whose value is never summed
+            const int i = (i0 + q) < TC ? (i0 + q) : (TC - 1);
+            pe[q] = e_tiles[((size_t)tr * TC + i) * 256 + e];          // E[16tr + r][16i + c]
+            pl[q] = L[(size_t)(16 * i + r) * C + 16 * (size_t)j + c];  // L_ij[r][c]
+        }
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < kBlocksPerChunk; ++q) {
+            Es[buf][q][r][c] = pe[q];
+            Lt[buf][q][c][r] = pl[q];
+        }
+    };
+    if (n_chunks > 0) {
+        fetch(0);
+        stage(0);
+        __syncthreads();
+    }
+    for (int n = 0; n < n_chunks; ++n) {
+        const int buf = n & 1;
+        if (n + 1 < n_chunks) fetch(n + 1);
+        const int nq = (n_later - n * kBlocksPerChunk) < kBlocksPerChunk
+                           ? (n_later - n * kBlocksPerChunk) : kBlocksPerChunk;
+        for (int q = 0; q < nq; ++q) {
+#pragma unroll
+            for (int t4 = 0; t4 < 16; t4 += 4) {
+                const float4 ev = *reinterpret_cast<const float4 *>(&Es[buf][q][r][t4]);
+                const float4 lv = *reinterpret_cast<const float4 *>(&Lt[buf][q][c][t4]);
+                acc = acc + ev.x * lv.x;
+                acc = acc + ev.y * lv.y;
+                acc = acc + ev.z * lv.z;
+                acc = acc + ev.w * lv.w;
             }
         }
+        if (n + 1 < n_chunks) stage(buf ^ 1);
         __syncthreads();
     }
     target[(size_t)tr * 256 + e] = acc;

@@ -15,6 +15,7 @@ namespace exl3 {
 namespace {
 
 constexpr int kTbThreads = 64;   // tiles per traceback workgroup (one wave)
+constexpr int64_t kWaveTbMaxTiles = 1024;   // up to this many tiles: one wave per tile
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
@@ -131,6 +132,136 @@ traceback2_kernel(const typename Geo<K>::bp_t *__restrict__ bp, int64_t n,
     if (sse_out) sse_out[tile] = sse;
 }
 
+// Small batches (a scale-search probe, an LDLQ span): one wave per tile, and
+// the walk's chain of dependent reads is shortened by speculation.  Knowing
+// S_t, the backpointer of step t-1 is one word; the one of step t-2 is one of
+// 2^K words (one per value k1 of the first backpointer), the one of step t-3
+// one of 2^2K, and so on.  Lane (d, h) reads the word of step t-1-d under
+// hypothesis h = k1 + 2^K k2 + ... (the d backpointers before it), all in one
+// round trip; then the wave resolves the D steps in order by reading the lane
+// that holds the true hypothesis.  Under h the state at step t-d is
+//     (h << (16 - K d)) | (S_t >> (K d)),
+// since each step shifts K bits out at the bottom and the backpointer in at
+// the top.  Look-ahead depth D: the largest with 1 + 2^K + ... + 2^(K(D-1))
+// <= 64 lanes.
+template <int K>
+struct Look {
+    static constexpr int D = (K == 1) ? 6 : (K == 2) ? 3 : 2;
+    static constexpr int offset(int d) {   // first lane of depth d
+        int off = 0;
+        for (int i = 0; i < d; ++i) off += 1 << (K * i);
+        return off;
+    }
+};
+
+// Walk `count` transitions back from state s: the first reads slot `slot0`,
+// the next slot0 - 1, ...  If S is given, S[pos0 - 1 - i] receives the state
+// after transition i.  Returns the last state (uniform across the wave).
+// Every read stays inside slots [slot0 - count + 1, slot0].
+template <int K, bool H>
+__device__ uint32_t walk_wave(const typename Geo<K>::bp_t *__restrict__ bp_tile, uint32_t s,
+                              int slot0, int count, uint16_t *S, int pos0) {
+    using G = Geo<K>;
+    using L = Look<K>;
+    constexpr int D = L::D;
+    const int lane = threadIdx.x & 63;
+    // this lane's depth and hypothesis bits (lanes past the last depth stay idle)
+    int d = -1;
+    uint32_t hs = 0;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        const int off = L::offset(i);
+        if (lane >= off && lane < off + (1 << (K * i))) {
+            d = i;
+            hs = i == 0 ? 0u : (uint32_t)(lane - off) << (16 - K * i);
+        }
+    }
+    const uint32_t shift = d > 0 ? (uint32_t)(K * d) : 0u;
+    int done = 0;
+    while (done < count) {
+        const int r = (count - done) < D ? (count - done) : D;   // steps this round
+        uint32_t val = 0;
+        if (d >= 0 && d < r) {
+            const uint32_t st = hs | (s >> shift);              // state at step t - d
+            val = bp_read<K, H>(bp_tile, slot0 - done - d, st >> K);
+        }
+        uint32_t hyp = 0;
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            if (i < r) {
+                const uint32_t k =
+                    (uint32_t)__builtin_amdgcn_readlane((int)val, L::offset(i) + (int)hyp);
+                s = (k << G::Kr) | (s >> K);
+                if (S && lane == 0) S[pos0 - 1 - done - i] = (uint16_t)s;
+                hyp |= k << (K * i);
+            }
+        }
+        done += r;
+    }
+    return s;
+}
+
+template <int K, bool H>
+__global__ void __launch_bounds__(64)
+traceback1_wave_kernel(const typename Geo<K>::bp_t *__restrict__ bp, int64_t n,
+                       const uint16_t *__restrict__ end_state, uint16_t *__restrict__ X_out) {
+    const int64_t b = blockIdx.x;
+    const typename Geo<K>::bp_t *bp_tile = bp + (size_t)b * kSlots * kLanes;
+    // rotated steps 255 -> 127: 128 transitions, slots 127 .. 0
+    const uint32_t X = walk_wave<K, H>(bp_tile, end_state[b], kSteps / 2 - 1, kSteps / 2,
+                                       nullptr, 0);
+    if (threadIdx.x == 0) X_out[b] = (uint16_t)X;
+}
+
+template <int K, bool H>
+__global__ void __launch_bounds__(64)
+traceback2_wave_kernel(const typename Geo<K>::bp_t *__restrict__ bp, int64_t n,
+                       const uint16_t *__restrict__ X_in, const float *__restrict__ x,
+                       const int32_t *__restrict__ tile_idx, int64_t tile0,
+                       const uint16_t *__restrict__ levels, float scale,
+                       uint16_t *__restrict__ packed, uint16_t *__restrict__ states_out,
+                       float *__restrict__ sse_out, float *__restrict__ w_hat) {
+    __shared__ uint16_t S[kSteps];
+    __shared__ float Q[kSteps];
+    const int lane = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const int64_t tile = tile_idx ? (int64_t)tile_idx[b] : tile0 + b;
+    const typename Geo<K>::bp_t *bp_tile = bp + (size_t)b * kSlots * kLanes;
+
+    const uint32_t X = X_in[b];
+    if (lane == 0) S[kSteps - 1] = (uint16_t)X;
+    walk_wave<K, H>(bp_tile, X, kSlots - 1, kSlots, S, kSteps - 1);
+    __syncthreads();
+
+    // container word w: stream bits 16w .. 16w+15, MSB first, pair swap
+    if (lane < 16 * K) {
+        uint32_t word = 0;
+        for (int j = 16 * lane; j < 16 * lane + 16; ++j) {
+            const int t = j / K;
+            word = (word << 1) | (((uint32_t)S[t] >> (K - 1 - (j - t * K))) & 1u);
+        }
+        packed[(size_t)tile * (16 * K) + (lane ^ 1)] = (uint16_t)word;
+    }
+    if (states_out)
+        for (int t = lane; t < kSteps; t += 64) states_out[(size_t)tile * kSteps + t] = S[t];
+    if (!x) return;
+
+    // dequantise; squared errors summed in step order by one lane
+    const float *xt = x + (size_t)tile * kSteps;
+    for (int t = lane; t < kSteps; t += 64) {
+        const float v = scale * half_bits_to_float(levels[S[t]]);
+        const float dd = xt[t] - v;
+        Q[t] = dd * dd;
+        if (w_hat) w_hat[(size_t)tile * kSteps + t] = v;
+    }
+    __syncthreads();
+    if (lane == 0 && sse_out) {
+        float sse = 0.0f;
+        for (int t = 0; t < kSteps; ++t) sse = sse + Q[t];
+        sse_out[tile] = sse;
+    }
+}
+
 __global__ void __launch_bounds__(256)
 decode_kernel(const uint16_t *__restrict__ packed, int K, float scale,
               const uint16_t *__restrict__ levels, float *__restrict__ out) {
@@ -165,6 +296,17 @@ hipError_t launch_tb_t(int pass, const void *bp, int64_t n, const uint16_t *star
                        const uint16_t *levels, float scale, uint16_t *packed, uint16_t *states,
                        float *sse, float *w_hat, hipStream_t stream) {
     using bp_t = typename Geo<K>::bp_t;
+    if (n <= kWaveTbMaxTiles) {
+        // small batch: one wave per tile with a speculative walk
+        if (pass == 1)
+            hipLaunchKernelGGL((traceback1_wave_kernel<K, H>), dim3((unsigned)n), dim3(64), 0,
+                               stream, reinterpret_cast<const bp_t *>(bp), n, start_state, X_out);
+        else
+            hipLaunchKernelGGL((traceback2_wave_kernel<K, H>), dim3((unsigned)n), dim3(64), 0,
+                               stream, reinterpret_cast<const bp_t *>(bp), n, start_state, x,
+                               tile_idx, tile0, levels, scale, packed, states, sse, w_hat);
+        return hipGetLastError();
+    }
     const unsigned blocks = (unsigned)((n + kTbThreads - 1) / kTbThreads);
     if (pass == 1)
         hipLaunchKernelGGL((traceback1_kernel<K, H>), dim3(blocks), dim3(kTbThreads), 0, stream,
