@@ -87,7 +87,7 @@ def _run(ctx, m, K):
     return got, reg, sums, flag
 
 
-def _check_matrix(ctx, m, K, exact_gss):
+def _check_matrix(ctx, m, K, exact_gss, levels=None):
     R, C = m.w.shape
     TR, TC = R // 16, C // 16
     print("\n%s %dx%d K=%d" % (m.name, R, C, K), flush=True)
@@ -115,10 +115,10 @@ def _check_matrix(ctx, m, K, exact_gss):
     if exact_gss:
         sample = oracle.sample_tiles(TR, TC, sums)
         xs = _oracle_tiles(m, sample)
-        levels = oracle.mul1_levels_fp16()
+        lv = oracle.mul1_levels_fp16() if levels is None else levels
 
         def f(s):
-            r = oracle.encode_tiles(xs, K, np.float32(s), levels)
+            r = oracle.encode_tiles(xs, K, np.float32(s), lv)
             tot = 0.0
             for e in r["sse"].tolist():
                 tot += float(e)
@@ -130,7 +130,7 @@ def _check_matrix(ctx, m, K, exact_gss):
     # sampled tiles of the final encode at the chosen scale
     ids = _sample_tiles(TR, TC, seed=R + C + K)
     xs = _oracle_tiles(m, ids)
-    want = oracle.encode_tiles(xs, K, scale)
+    want = oracle.encode_tiles(xs, K, scale, levels)
     packed = got["packed"].cpu().numpy().view(np.uint16).reshape(-1, 16 * K)
     tsse = got["tile_sse"].cpu().numpy()
     assert np.array_equal(packed[ids], want["packed"])
@@ -199,3 +199,38 @@ def test_workload2_grid_search_scale(ctx):
     g, _ = oracle.grid_search(f(np.arange(len(sample))[::2]), f(np.arange(len(sample))),
                               oracle.GRID_DEFAULT)
     assert np.float32(got["scale"]) == np.float32(g * rms)
+
+
+@pytest.mark.parametrize("name", ["mcg", "3inst"])
+def test_workload2_other_codebooks(ctx, name):
+    """The 4096x4096 matrix at K=2 with the mcg / 3INST tables: regularization blocks,
+    bracket, sampled final tiles and the MSE sum, as for mul1."""
+    m = workloads.config(2)[0]
+    ctx.set_codebook_kind(name)
+    try:
+        got, rms = _check_matrix(ctx, m, 2, exact_gss=False, levels=oracle.CODEBOOKS[name]())
+    finally:
+        ctx.set_codebook_kind("mul1")
+    assert 2.0 ** -4 < got["mse"] / rms ** 2 < _lloyd(2)
+
+
+@pytest.mark.parametrize("K", [2, 3, 4, 1])
+def test_workload2_binary16_all_tiles(ctx, K):
+    """All 65,536 tiles of the 4096x4096 matrix in binary16 mode (regularized, divided by
+    a scale, rounded to binary16 -- the benchmark's input), in the batches the benchmark
+    uses; sampled tiles bit-exact against the oracle's binary16 encoder."""
+    m = workloads.config(2)[0]
+    R, C = m.w.shape
+    print("\nbinary16 4096x4096 K=%d" % K, flush=True)
+    w = torch.from_numpy(m.w).to(torch.bfloat16).to(DEV)
+    su, sv = torch.from_numpy(m.su).to(DEV), torch.from_numpy(m.sv).to(DEV)
+    reg, _, _ = ctx.regularize(w, su, sv, 128)
+    xh = (reg / 0.0202).to(torch.float16).contiguous()
+    packed, states, cost = ctx.encode_tiles_f16(xh, K)
+    torch.cuda.synchronize()
+    ids = _sample_tiles(R // 16, C // 16, n=12, seed=K)
+    xb = xh.cpu().numpy().view(np.uint16)[ids]
+    want = oracle.encode_tiles_f16(xb, K)
+    assert np.array_equal(states.cpu().numpy().view(np.uint16)[ids], want["states"])
+    assert np.array_equal(packed.cpu().numpy().view(np.uint16)[ids], want["packed"])
+    assert np.array_equal(cost.cpu().numpy().view(np.uint16)[ids], np.asarray(want["cost"], np.uint16))
