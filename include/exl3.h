@@ -77,7 +77,12 @@ void exl3_ctx_destroy(exl3_ctx *ctx);
 /* Last error message of this context ("" if none); never NULL.  ctx may be NULL. */
 const char *exl3_last_error(const exl3_ctx *ctx);
 
-/* Change the stream later calls enqueue on (the caller still owns it). */
+/*
+ * Change the stream later calls enqueue on (the caller still owns it).  The new
+ * stream is made to wait (through an event, without blocking the host) for the
+ * work already enqueued on the old one, since that work may still use the
+ * context's buffers.  Errors: EXL3_EINVAL, EXL3_EHIP.
+ */
 int exl3_ctx_set_stream(exl3_ctx *ctx, void *hip_stream);
 
 /*

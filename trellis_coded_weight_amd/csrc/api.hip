@@ -30,6 +30,8 @@ struct exl3_ctx {
     // scale-search probe, with the events that order it against `stream`
     hipStream_t aux = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    // orders a new stream after the work already enqueued on the old one
+    hipEvent_t ev_switch = nullptr;
     size_t scratch_limit = 0;
     uint16_t *d_levels = nullptr;
     void *d_bp = nullptr;
@@ -135,8 +137,13 @@ void clear_timing(exl3_ctx *ctx) {
 int open_timed(exl3_ctx *ctx, int kind, int64_t tiles, hipStream_t s = nullptr) {
     if (!ctx->timing) return -1;
     exl3_ctx::Timed r{kind, tiles, nullptr, nullptr, s ? s : ctx->stream};
-    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) {
+    if (hipEventCreate(&r.start) != hipSuccess) {
         (void)hipGetLastError();
+        return -1;
+    }
+    if (hipEventCreate(&r.stop) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipEventDestroy(r.start);
         return -1;
     }
     (void)hipEventRecord(r.start, r.stream);
@@ -411,6 +418,7 @@ void exl3_ctx_destroy(exl3_ctx *ctx) {
     clear_timing(ctx);
     if (ctx->ev_fork) (void)hipEventDestroy(ctx->ev_fork);
     if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
+    if (ctx->ev_switch) (void)hipEventDestroy(ctx->ev_switch);
     if (ctx->aux) (void)hipStreamDestroy(ctx->aux);
     void *bufs[] = {ctx->d_levels,      ctx->d_bp,          ctx->d_end,         ctx->d_X,
                     ctx->d_cost,        ctx->d_idx,         ctx->d_wreg,        ctx->d_sumsq,
@@ -425,7 +433,17 @@ const char *exl3_last_error(const exl3_ctx *ctx) { return ctx ? ctx->err.c_str()
 
 int exl3_ctx_set_stream(exl3_ctx *ctx, void *hip_stream) {
     if (!ctx) return EXL3_EINVAL;
-    ctx->stream = static_cast<hipStream_t>(hip_stream);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (s == ctx->stream) return EXL3_OK;
+    // work already enqueued on the old stream may still use the context's
+    // buffers: the new stream waits for it (no host synchronization)
+    int rc;
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    if (!ctx->ev_switch)
+        EXL3_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_switch, hipEventDisableTiming));
+    EXL3_HIP(ctx, hipEventRecord(ctx->ev_switch, ctx->stream));
+    EXL3_HIP(ctx, hipStreamWaitEvent(s, ctx->ev_switch, 0));
+    ctx->stream = s;
     return EXL3_OK;
 }
 
