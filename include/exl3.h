@@ -22,7 +22,8 @@
  *   - Arithmetic contract: binary32, each subtract / multiply / add rounded on
  *     its own (no fused multiply-add), lowest index on equal costs.  Outputs
  *     are bit-identical for any batch size and scratch limit.
- *   - A context is not thread-safe; use one per host thread / stream.
+ *   - A context is not thread-safe; use one per host thread / stream.  Every
+ *     call makes the context's device current on the calling thread.
  *   - Tiles: a 16x16 tile is 256 consecutive floats, element t = 16*row + col;
  *     tile tau = tr * (cols/16) + tc of a rows x cols matrix.
  */
