@@ -28,8 +28,22 @@
 
 #include <math.h>
 
+
 namespace exl3 {
 namespace {
+
+// Wave priority across a step: 3 from the step's first update, 2 from half of
+// its updates, 1 from three quarters, 0 from seven eighths.  The 16 waves of a
+// tile meet at a barrier after every step; waves that are behind (their
+// predecessor costs arrived late) keep a higher priority than the ones
+// finishing, so fewer quad-cycles are left idle before the barrier (A/B on one
+// box: 2-4 % shorter forward launches at K = 2).
+__device__ __forceinline__ void step_priority(int e, int n) {
+    if (e == 0) __builtin_amdgcn_s_setprio(3);
+    if (e == n / 2) __builtin_amdgcn_s_setprio(2);
+    if (e == 3 * n / 4) __builtin_amdgcn_s_setprio(1);
+    if (e == 7 * n / 8) __builtin_amdgcn_s_setprio(0);
+}
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
@@ -263,6 +277,7 @@ __device__ __forceinline__ uint32_t trellis_step(
         bool r1[NE], r0[NE];
 #pragma unroll
         for (int e = 0; e < NE + 2; ++e) {
+            step_priority(e, NE);
             float a[4];
             if (e < NE) {
                 const int i = e / G::BPL, bb = e % G::BPL;
@@ -306,6 +321,7 @@ __device__ __forceinline__ uint32_t trellis_step(
             float outv[G::BPL];
 #pragma unroll
             for (int bb = 0; bb < G::BPL; ++bb) {
+                step_priority(i * G::BPL + bb, G::GPL * G::BPL);
                 float a[G::NB];
 #pragma unroll
                 for (int k = 0; k < G::NB; ++k) {
