@@ -77,6 +77,18 @@ __device__ __forceinline__ void merge(uint32_t &acc, uint32_t hi, uint32_t lo, i
     acc = __builtin_amdgcn_bitop3_b32(bytes, acc, 0x01010101u << pos, kSel);
 }
 
+// Wave priority across a step, stepped down from 3 to 0 (as in the binary32
+// kernel): waves that are behind keep priority over the ones finishing.  Used
+// at K = 1 only (one workgroup per compute unit: +12 % measured); where two
+// tiles' workgroups share a compute unit (K = 2, 3) it starves the other
+// workgroup (-44 % at K = 2), and K = 4 measured no gain.
+__device__ __forceinline__ void step_priority(int e, int n) {
+    if (e == 0) __builtin_amdgcn_s_setprio(3);
+    if (e == n / 2) __builtin_amdgcn_s_setprio(2);
+    if (e == 3 * n / 4) __builtin_amdgcn_s_setprio(1);
+    if (e == 7 * n / 8) __builtin_amdgcn_s_setprio(0);
+}
+
 __device__ __forceinline__ h2 hmin(h2 a, h2 b) { return __builtin_elementwise_min(a, b); }
 __device__ __forceinline__ h2 hmin3(h2 a, h2 b, h2 c) {
     return __builtin_elementwise_minimum(__builtin_elementwise_minimum(a, b), c);
@@ -237,6 +249,8 @@ __device__ __forceinline__ uint32_t step_h(
         for (int j = 0; j < G::NJ; ++j)
 #pragma unroll
             for (int p = 0; p < G::NP; ++p) {
+                if constexpr (K == 1)
+                    step_priority((i * G::NJ + j) * G::NP + p, G::NI * G::NJ * G::NP);
                 h2 a[G::NB];
 #pragma unroll
                 for (int k = 0; k < G::NB; ++k) {
