@@ -79,9 +79,10 @@ __device__ __forceinline__ void merge(uint32_t &acc, uint32_t hi, uint32_t lo, i
 
 // Wave priority across a step, stepped down from 3 to 0 (as in the binary32
 // kernel): waves that are behind keep priority over the ones finishing.  Used
-// at K = 1 only (one workgroup per compute unit: +12 % measured); where two
-// tiles' workgroups share a compute unit (K = 2, 3) it starves the other
-// workgroup (-44 % at K = 2), and K = 4 measured no gain.
+// at K = 1 only (one workgroup per compute unit: +12 % measured).  At K = 2
+// and 3 the kernel must fit 64 registers (two workgroups per compute unit) and
+// the priority changes inside the unrolled step made the compiler spill; K = 4
+// measured no gain.
 __device__ __forceinline__ void step_priority(int e, int n) {
     if (e == 0) __builtin_amdgcn_s_setprio(3);
     if (e == n / 2) __builtin_amdgcn_s_setprio(2);
