@@ -17,5 +17,6 @@ from .reference import (  # noqa: F401
     scaled_levels, tile_sse, tile_sumsq, to_tiles, unpack_states, unregularize,
     default_threads, encode_sequences_f16, encode_tiles_f16, f16_sqadd, f16_sub, forward_f16,
     ldlq, quantize_matrix_ldlq, grid_search, GRID_DEFAULT, channel_normalize, CHANNEL_FLOOR,
-    mcg_levels_fp16, inst3_levels_fp16, CODEBOOKS,
+    mcg_levels_fp16, inst3_levels_fp16, CODEBOOKS, to_f16_inputs, encode_tiles_f16_scaled,
+    quantize_matrix_f16,
 )

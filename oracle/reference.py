@@ -703,3 +703,81 @@ def encode_tiles_f16(x_bits, K, levels=None, threads=None):
         levels = mul1_levels_fp16()
     states, X, cost = encode_sequences_f16(x_bits, K, levels.view(np.uint16), threads=threads)
     return {"states": states, "X": X, "cost": cost, "packed": pack_states(states, K)}
+
+
+def to_f16_inputs(tiles, scale) -> np.ndarray:
+    """Binary16 encoder inputs of regularized tiles at a scale: each weight
+    divided by the scale (one binary32 division, correctly rounded), then
+    rounded to binary16 (nearest even); all zeros when the scale is 0.
+    Returned as binary16 bit patterns."""
+    t = np.asarray(tiles, np.float32)
+    s = np.float32(scale)
+    if s == 0:
+        return np.zeros(t.shape, np.uint16)
+    return (t / s).astype(np.float32).astype(np.float16).view(np.uint16)
+
+
+def encode_tiles_f16_scaled(tiles, K, scale, levels=None, threads=None):
+    """Binary16-mode search on fp16(w / scale); the result dequantized as
+    w_hat = rn32(scale * level) and scored with the same sequential binary32
+    squared error as the binary32 path (tile_sse)."""
+    if levels is None:
+        levels = mul1_levels_fp16()
+    x16 = to_f16_inputs(tiles, scale)
+    r = encode_tiles_f16(x16, K, levels, threads)
+    v = scaled_levels(levels, scale)
+    sse = tile_sse(np.asarray(tiles, np.float32), r["states"], v)
+    r.update({"x16": x16, "sse": sse})
+    return r
+
+
+def quantize_matrix_f16(w, su, sv, K, had_block=128, gss=(12, 0.5, 2.0), fixed_scale=1.0,
+                        levels=None, threads=None, tiles_subset=None):
+    """Whole-matrix path with the binary16 encoder inside the scale search.
+
+    Regularization, statistics, tile sample and golden section exactly as in
+    quantize_matrix; the objective at scale s is the binary64 ascending sum of
+    the binary32 squared errors of the sample tiles encoded by
+    encode_tiles_f16_scaled at s; the final encode likewise."""
+    w = np.asarray(w, dtype=np.float32)
+    R, C = w.shape
+    if levels is None:
+        levels = mul1_levels_fp16()
+    tiles = to_tiles(regularize(w, su, sv, had_block))
+    TR, TC = R // 16, C // 16
+    sumsq = tile_sumsq(tiles)
+    rms = matrix_rms(sumsq, R * C)
+    out = {"tiles": tiles, "sumsq": sumsq, "rms": rms}
+    if gss is None:
+        scale = np.float32(fixed_scale)
+        out["sample"], out["trace"] = [], []
+    else:
+        iters, lo, hi = gss
+        sample = sample_tiles(TR, TC, sumsq)
+        out["sample"] = sample
+        if rms == 0.0:
+            scale = np.float32(0.0)
+            out["trace"] = []
+        else:
+            xs = tiles[sample]
+
+            def objective(s):
+                r = encode_tiles_f16_scaled(xs, K, np.float32(s), levels, threads)
+                total = 0.0
+                for e in r["sse"].tolist():
+                    total += float(e)
+                return total
+
+            mid, trace = golden_section(objective, lo * rms, hi * rms, iters)
+            scale = np.float32(mid)
+            out["trace"] = trace
+    out["scale"] = scale
+    idx = np.arange(TR * TC) if tiles_subset is None else np.asarray(tiles_subset)
+    r = encode_tiles_f16_scaled(tiles[idx], K, scale, levels, threads)
+    out.update({"index": idx, "states": r["states"], "sse": r["sse"], "packed": r["packed"]})
+    if tiles_subset is None:
+        total = 0.0
+        for e in r["sse"].tolist():
+            total += float(e)
+        out["mse"] = total / (R * C)
+    return out
