@@ -175,7 +175,8 @@ def cpu_baseline(m, K, scale, n_tiles, threads, sample_tiles):
 def f16_mode(ctx, w, su, sv, scale, n_tiles, steps):
     """Binary16-mode encode of every tile of the same matrix (regularized,
     divided by the chosen scale, rounded to binary16; prepared outside the
-    timed region), for K = 1..4.  Rated like the binary32 path: the same
+    timed region), for K = 1..4; and the whole binary16 path
+    (exl3_quantize_matrix_f16: scale search with binary16 probes included).  Rated like the binary32 path: the same
     algorithmic operation count per tile over the forward kernel's own launch
     time, against the same vector peak (a packed binary16 FMA does two lanes'
     work per issue, as dual-issued binary32 does)."""
@@ -185,7 +186,16 @@ def f16_mode(ctx, w, su, sv, scale, n_tiles, steps):
     del reg
     res = {"workload": "the 4096x4096 matrix's 65,536 tiles as binary16 (regularized / scale)",
            "tiles_per_s_by_K": {}, "fwd_frac_by_K": {}, "fwd_avg_launch_ms_by_K": {}}
+    res["whole_matrix_tiles_per_s_by_K"] = {}
     for K in (2, 3, 4, 1):
+        # the whole path (regularize, golden section with binary16 probes, final
+        # encode, binary32 errors): exl3_quantize_matrix_f16
+        ctx.quantize_matrix_f16(w, K, su, sv)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ctx.quantize_matrix_f16(w, K, su, sv)
+        torch.cuda.synchronize()
+        res["whole_matrix_tiles_per_s_by_K"][str(K)] = round(n_tiles / (time.perf_counter() - t0), 1)
         ctx.encode_tiles_f16(xh, K, want_states=False, want_cost=True)
         torch.cuda.synchronize()
         ctx.set_timing(True)

@@ -235,6 +235,23 @@ int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, in
                          float *scale_out, double *mse_out, float *w_hat, float *tile_sse);
 
 /*
+ * Whole-matrix quantization with the binary16 encoder [P1 sections 1 and 4:
+ * the search runs in half precision; section 8: scale search] -- the
+ * exl3_quantize_matrix path with exl3_encode_tiles_f16 inside: at a scale s
+ * the encoder inputs are fp16(rn32(w / s)) (all zero at s = 0), the binary16
+ * two-pass search gives the states, and each tile is dequantized and scored
+ * as in exl3_quantize_matrix (w_hat = rn32(s * c[state]), sequential binary32
+ * squared error).  The golden-section objective is the binary64 ascending sum
+ * of those errors over the tile sample; gss == NULL uses fixed_scale.
+ * Arguments, outputs and errors as exl3_quantize_matrix (tile_sse: the
+ * binary32 squared errors).  Synchronizes the stream.
+ */
+int exl3_quantize_matrix_f16(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
+                             int K, int had_block, const float *su, const float *sv,
+                             const exl3_gss *gss, float fixed_scale, uint16_t *packed,
+                             float *scale_out, double *mse_out, float *w_hat, float *tile_sse);
+
+/*
  * Whole-matrix quantization with the pages' grid + parabolic scale search
  * [P1 section 8] instead of the golden section: the search runs over a
  * multiplier g of the matrix rms.  Coarse points g = coarse_lo + k*coarse_step,

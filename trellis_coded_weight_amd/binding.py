@@ -31,7 +31,7 @@ EXPORTED = [
     "exl3_ctx_set_stream", "exl3_set_codebook", "exl3_get_codebook", "exl3_set_codebook_kind",
     "exl3_regularize",
     "exl3_channel_normalize", "exl3_encode_tiles", "exl3_encode_tiles_f16", "exl3_decode_tiles", "exl3_quantize_matrix",
-    "exl3_quantize_matrix_ldlq", "exl3_quantize_matrix_grid", "exl3_scratch_per_tile",
+    "exl3_quantize_matrix_ldlq", "exl3_quantize_matrix_grid", "exl3_quantize_matrix_f16", "exl3_scratch_per_tile",
     "exl3_ctx_set_timing", "exl3_ctx_read_timing",
 ]
 CODEBOOK_KINDS = {"mul1": 0, "mcg": 1, "3inst": 2}
@@ -112,6 +112,10 @@ def load_library():
     lib.exl3_quantize_matrix_ldlq.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp,
                                               ctypes.POINTER(GSS), f32, vp, vp,
                                               ctypes.POINTER(f32), ctypes.POINTER(f64), vp, vp]
+    lib.exl3_quantize_matrix_f16.restype = i32
+    lib.exl3_quantize_matrix_f16.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp,
+                                             ctypes.POINTER(GSS), f32, vp, ctypes.POINTER(f32),
+                                             ctypes.POINTER(f64), vp, vp]
     lib.exl3_quantize_matrix_grid.restype = i32
     lib.exl3_quantize_matrix_grid.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp,
                                               ctypes.POINTER(Grid), vp, ctypes.POINTER(f32),
@@ -327,6 +331,35 @@ class Context:
         mse = ctypes.c_double(0.0)
         self._sync_stream()
         self._check(self.lib.exl3_quantize_matrix(
+            self.handle, _ptr(w), dt, rows, cols, K, had_block, _ptr(su.contiguous()),
+            _ptr(sv.contiguous()), g, float(scale), _ptr(packed), ctypes.byref(s_out),
+            ctypes.byref(mse), _ptr(w_hat), _ptr(tsse)))
+        return {"packed": packed, "scale": s_out.value, "mse": mse.value, "w_hat": w_hat,
+                "tile_sse": tsse}
+
+    def quantize_matrix_f16(self, w: torch.Tensor, K: int, su: torch.Tensor, sv: torch.Tensor,
+                            had_block: int = 128,
+                            gss: Optional[Tuple[int, float, float]] = (12, 0.5, 2.0),
+                            scale: float = 1.0, want_w_hat: bool = False,
+                            want_tile_sse: bool = False):
+        """Whole-matrix path with the binary16 encoder inside the scale search.
+        Returns dict(packed int16 [R/16, C/16, 16K], scale, mse, w_hat?, tile_sse?)."""
+        rows, cols = w.shape
+        dt = {torch.float32: EXL3_F32, torch.bfloat16: EXL3_BF16}.get(w.dtype)
+        if dt is None:
+            raise ValueError("w must be float32 or bfloat16")
+        w = w.contiguous()
+        dev = w.device
+        packed = torch.empty(rows // 16, cols // 16, 16 * K, dtype=torch.int16, device=dev)
+        w_hat = (torch.empty((rows // 16) * (cols // 16), 256, dtype=torch.float32, device=dev)
+                 if want_w_hat else None)
+        tsse = (torch.empty((rows // 16) * (cols // 16), dtype=torch.float32, device=dev)
+                if want_tile_sse else None)
+        g = None if gss is None else ctypes.byref(GSS(int(gss[0]), float(gss[1]), float(gss[2])))
+        s_out = ctypes.c_float(0.0)
+        mse = ctypes.c_double(0.0)
+        self._sync_stream()
+        self._check(self.lib.exl3_quantize_matrix_f16(
             self.handle, _ptr(w), dt, rows, cols, K, had_block, _ptr(su.contiguous()),
             _ptr(sv.contiguous()), g, float(scale), _ptr(packed), ctypes.byref(s_out),
             ctypes.byref(mse), _ptr(w_hat), _ptr(tsse)))

@@ -59,6 +59,14 @@ struct exl3_ctx {
     size_t span_what_cap = 0;
     uint16_t *d_span_packed = nullptr;
     size_t span_packed_cap = 0;
+    // binary16 whole-matrix path: the sample's binary32 tiles, binary16
+    // encoder inputs, and the probes' container words
+    float *d_gs = nullptr;
+    size_t gs_cap = 0;
+    uint16_t *d_x16 = nullptr;
+    size_t x16_cap = 0;
+    uint16_t *d_pk = nullptr;
+    size_t pk_cap = 0;
     std::string err;
     // optional per-launch timing (HIP events on the context's stream)
     struct Timed {
@@ -312,8 +320,11 @@ int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, i
 }
 
 // The same chain in binary16 arithmetic: costs come out of pass 2 directly.
+// With x32 given (the binary32 weights of the same tiles), the traceback also
+// dequantizes at `scale` and sums the binary32 squared errors (sse, w_hat).
 int encode_chain_f16(exl3_ctx *ctx, const uint16_t *x, int64_t n, int K, uint16_t *packed,
-                     uint16_t *states, uint16_t *cost) {
+                     uint16_t *states, uint16_t *cost, const float *x32 = nullptr,
+                     float scale = 0.0f, float *sse = nullptr, float *w_hat = nullptr) {
     if (n == 0) return EXL3_OK;
     int64_t batch = 0;
     int rc;
@@ -337,8 +348,8 @@ int encode_chain_f16(exl3_ctx *ctx, const uint16_t *x, int64_t n, int K, uint16_
         close_timed(ctx, id);
         id = open_timed(ctx, EXL3_KERNEL_TB2, nb);
         EXL3_HIP(ctx, exl3::launch_traceback(K, 2, true, ctx->d_bp, nb, ctx->d_X, nullptr,
-                                             nullptr, nullptr, i0, ctx->d_levels, 0.0f, packed,
-                                             states, nullptr, nullptr, ctx->stream));
+                                             x32, nullptr, i0, ctx->d_levels, scale, packed,
+                                             states, sse, w_hat, ctx->stream));
         close_timed(ctx, id);
     }
     return EXL3_OK;
@@ -423,7 +434,8 @@ void exl3_ctx_destroy(exl3_ctx *ctx) {
     void *bufs[] = {ctx->d_levels,      ctx->d_bp,          ctx->d_end,         ctx->d_X,
                     ctx->d_cost,        ctx->d_idx,         ctx->d_wreg,        ctx->d_sumsq,
                     ctx->d_sse,         ctx->d_flag,        ctx->d_err_tiles,   ctx->d_span_target,
-                    ctx->d_span_what,   ctx->d_span_packed};
+                    ctx->d_span_what,   ctx->d_span_packed, ctx->d_gs,          ctx->d_x16,
+                    ctx->d_pk};
     for (void *p : bufs)
         if (p) (void)hipFree(p);
     delete ctx;
@@ -650,7 +662,8 @@ double grid_search(const exl3_grid &grid, FS f_sub, FF f_full) {
 int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
                                 int K, int had_block, const float *su, const float *sv,
                                 const exl3_gss *gss, const exl3_grid *grid, float fixed_scale,
-                                uint16_t *packed, float *scale_out, float *scale_chosen) {
+                                uint16_t *packed, float *scale_out, float *scale_chosen,
+                                bool f16 = false) {
     if (!ctx) return EXL3_EINVAL;
     int rc;
     if ((rc = check_matrix_args(ctx, w, w_dtype, rows, cols, had_block, su, sv)) != EXL3_OK)
@@ -739,12 +752,33 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
                                          hipMemcpyHostToDevice, ctx->stream));
             std::vector<float> costs((size_t)ns);
             int err = EXL3_OK;
+            if (f16) {
+                // binary16 probes work on a contiguous copy of the sample
+                if ((rc = ensure(ctx, ctx->d_gs, ctx->gs_cap, (size_t)ns * 256)) != EXL3_OK ||
+                    (rc = ensure(ctx, ctx->d_x16, ctx->x16_cap, (size_t)ns * 256)) != EXL3_OK ||
+                    (rc = ensure(ctx, ctx->d_pk, ctx->pk_cap, (size_t)ns * 16 * K)) != EXL3_OK)
+                    return rc;
+                EXL3_HIP(ctx, exl3::launch_gather_tiles(ctx->d_wreg, ctx->d_idx, ns, ctx->d_gs,
+                                                        ctx->stream));
+            }
             // binary64 sum, in ascending tile order, of the path costs of the
             // tiles idx[off .. off+cnt) at scale (float)s
             auto objective_on = [&](double s, int64_t off, int64_t cnt) -> double {
                 if (err != EXL3_OK) return 0.0;
-                int r = encode_chain(ctx, ctx->d_wreg, ctx->d_idx + off, cnt, K, (float)s,
+                int r;
+                if (f16) {
+                    // binary16 search on fp16(w / s); the traceback scores the
+                    // dequantized tiles in binary32 (off is 0: no subsample)
+                    hipError_t e = exl3::launch_to_f16(ctx->d_gs, nullptr, cnt, (float)s,
+                                                       ctx->d_x16, ctx->stream);
+                    r = e == hipSuccess
+                            ? encode_chain_f16(ctx, ctx->d_x16, cnt, K, ctx->d_pk, nullptr,
+                                               nullptr, ctx->d_gs, (float)s, ctx->d_sse)
+                            : fail(ctx, EXL3_EHIP, "binary16 inputs: %s", hipGetErrorString(e));
+                } else {
+                    r = encode_chain(ctx, ctx->d_wreg, ctx->d_idx + off, cnt, K, (float)s,
                                      nullptr, nullptr, nullptr, nullptr, ctx->d_sse);
+                }
                 if (r == EXL3_OK) {
                     hipError_t e = hipMemcpyAsync(costs.data(), ctx->d_sse,
                                                   (size_t)cnt * sizeof(float),
@@ -857,6 +891,41 @@ int exl3_quantize_matrix_grid(exl3_ctx *ctx, const void *w, int w_dtype, int row
     if (rc != EXL3_OK) return rc;
     return encode_whole_matrix(ctx, rows, cols, K, scale, packed, scale_out, mse_out, w_hat,
                                tile_sse);
+}
+
+int exl3_quantize_matrix_f16(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
+                             int K, int had_block, const float *su, const float *sv,
+                             const exl3_gss *gss, float fixed_scale, uint16_t *packed,
+                             float *scale_out, double *mse_out, float *w_hat, float *tile_sse) {
+    if (!ctx) return EXL3_EINVAL;
+    float scale = 0.0f;
+    int rc = regularize_and_choose_scale(ctx, w, w_dtype, rows, cols, K, had_block, su, sv, gss,
+                                         nullptr, fixed_scale, packed, scale_out, &scale, true);
+    if (rc != EXL3_OK) return rc;
+    const int64_t ntiles = (int64_t)(rows / 16) * (cols / 16);
+    const size_t nel = (size_t)rows * cols;
+    float *sse_dev = tile_sse;
+    if (!sse_dev) {
+        if ((rc = ensure(ctx, ctx->d_sse, ctx->sse_cap, (size_t)ntiles)) != EXL3_OK) return rc;
+        sse_dev = ctx->d_sse;
+    }
+    if ((rc = ensure(ctx, ctx->d_x16, ctx->x16_cap, (size_t)ntiles * 256)) != EXL3_OK) return rc;
+    EXL3_HIP(ctx, exl3::launch_to_f16(ctx->d_wreg, nullptr, ntiles, scale, ctx->d_x16,
+                                      ctx->stream));
+    if ((rc = encode_chain_f16(ctx, ctx->d_x16, ntiles, K, packed, nullptr, nullptr, ctx->d_wreg,
+                               scale, sse_dev, w_hat)) != EXL3_OK)
+        return rc;
+    std::vector<float> sse((size_t)ntiles);
+    EXL3_HIP(ctx, hipMemcpyAsync(sse.data(), sse_dev, (size_t)ntiles * sizeof(float),
+                                 hipMemcpyDeviceToHost, ctx->stream));
+    EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    if (mse_out) {
+        double tot = 0.0;
+        for (int64_t i = 0; i < ntiles; ++i) tot += (double)sse[(size_t)i];
+        *mse_out = tot / (double)nel;
+    }
+    *scale_out = scale;
+    return EXL3_OK;
 }
 
 int exl3_quantize_matrix_ldlq(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,

@@ -170,6 +170,9 @@ hipError_t launch_channel_normalize(const void *w, int w_dtype, int rows, int co
 hipError_t launch_decode(const uint16_t *packed, int64_t n, int K, float scale,
                          const uint16_t *levels, float *out, hipStream_t stream);
 
+hipError_t launch_to_f16(const float *src, const int32_t *idx, int64_t n, float scale,
+                         uint16_t *dst, hipStream_t stream);
+
 hipError_t launch_gather_tiles(const float *src, const int32_t *idx, int64_t n, float *dst,
                                hipStream_t stream);
 

@@ -290,6 +290,18 @@ gather_tiles_kernel(const float *__restrict__ src, const int32_t *__restrict__ i
     dst[(size_t)b * kSteps + t] = src[(size_t)idx[b] * kSteps + t];
 }
 
+// Binary16 encoder inputs: fp16(rn32(w / scale)), all zero at scale 0; tile b
+// of the output is tile idx[b] (or b) of the input.
+__global__ void __launch_bounds__(256)
+to_f16_kernel(const float *__restrict__ src, const int32_t *__restrict__ idx, float scale,
+              uint16_t *__restrict__ dst) {
+    const int64_t b = blockIdx.x;
+    const int t = threadIdx.x;
+    const int64_t tile = idx ? (int64_t)idx[b] : b;
+    const float q = scale == 0.0f ? 0.0f : src[(size_t)tile * kSteps + t] / scale;
+    dst[(size_t)b * kSteps + t] = __builtin_bit_cast(uint16_t, (_Float16)q);
+}
+
 template <int K, bool H>
 hipError_t launch_tb_t(int pass, const void *bp, int64_t n, const uint16_t *start_state,
                        uint16_t *X_out, const float *x, const int32_t *tile_idx, int64_t tile0,
@@ -326,11 +338,6 @@ hipError_t launch_traceback(int K, int pass, bool f16, const void *bp, int64_t n
                             float scale, uint16_t *packed, uint16_t *states, float *sse,
                             float *w_hat, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    if (f16) {
-        x = nullptr;
-        sse = nullptr;
-        w_hat = nullptr;
-    }
 #define EXL3_TB_CASE(KK)                                                                     \
     case KK:                                                                                 \
         return f16 ? launch_tb_t<KK, true>(pass, bp, n, start_state, X_out, x, tile_idx,     \
@@ -356,6 +363,14 @@ hipError_t launch_decode(const uint16_t *packed, int64_t n, int K, float scale,
     if (K < 1 || K > 8) return hipErrorInvalidValue;
     hipLaunchKernelGGL(decode_kernel, dim3((unsigned)n), dim3(kSteps), 0, stream, packed, K, scale,
                        levels, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_to_f16(const float *src, const int32_t *idx, int64_t n, float scale,
+                         uint16_t *dst, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(to_f16_kernel, dim3((unsigned)n), dim3(kSteps), 0, stream, src, idx, scale,
+                       dst);
     return hipGetLastError();
 }
 
