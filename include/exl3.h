@@ -136,6 +136,23 @@ int exl3_regularize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int col
                     int out_layout, float *tile_sumsq, int *nonfinite);
 
 /*
+ * Inverse of exl3_regularize [P1 section 7: decode applies H_l, x su, H_r,
+ * x sv; H is its own inverse]: W = diag(su) H_l W_reg H_r diag(sv), evaluated
+ * as left transform, x rn32(1/sqrt(had_block)), right transform, the same
+ * factor, then x su[row], x sv[col].  su and sv may be any finite values (the
+ * folded signs of exl3_channel_normalize), so dequantized tiles go back to the
+ * original weights' domain.
+ *   w_reg     float [rows*cols], tile-major (as exl3_decode_tiles and the
+ *             w_hat outputs write it) or row-major (in_layout)
+ *   su, sv    float [rows], float [cols]
+ *   out       float [rows][cols] row-major; must not overlap w_reg
+ * rows and cols multiples of had_block (64 or 128).  Asynchronous.
+ * Errors: EXL3_EINVAL, EXL3_EUNSUPPORTED, EXL3_EHIP.
+ */
+int exl3_unregularize(exl3_ctx *ctx, const float *w_reg, int in_layout, int rows, int cols,
+                      int had_block, const float *su, const float *sv, float *out);
+
+/*
  * Out-channel RMS normalization with the scale folded into the row signs
  * [P1 section 8: out-channel RMS normalization, sign + scale folding, the
  * zero-channel floor, a zero sign for all-zero channels].  The output channels

@@ -84,3 +84,18 @@ def test_left_and_right_commute_exactly_on_integers():
     lr = oracle.fwht_rows_blockwise(oracle.fwht_rows_blockwise(a, 128).T, 128).T
     rl = oracle.fwht_rows_blockwise(oracle.fwht_rows_blockwise(a.T, 128).T, 128)
     assert np.array_equal(lr, rl)
+
+
+def test_unregularize_against_the_dense_definition():
+    """W = diag(su) H_l W_reg H_r diag(sv) in binary64, with non-unit su (folded channel
+    scales) -- the inverse's own order of operations is not reused."""
+    rng = np.random.default_rng(9)
+    B = 64
+    w_reg = rng.standard_normal((128, 192)).astype(np.float32)
+    su = (rng.standard_normal(128) * 0.3).astype(np.float32)
+    sv = (2 * rng.integers(0, 2, 192) - 1).astype(np.float32)
+    got = oracle.unregularize(w_reg, su, sv, B)
+    H = sylvester(B).astype(np.float64) / np.sqrt(B)
+    dense = (su[:, None].astype(np.float64) * (np.kron(np.eye(2), H) @ w_reg.astype(np.float64)
+                                               @ np.kron(np.eye(3), H)) * sv[None, :])
+    assert np.max(np.abs(got - dense)) <= 2e-6 * np.max(np.abs(dense))

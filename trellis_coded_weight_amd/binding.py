@@ -29,7 +29,7 @@ EXL3_TILE_MAJOR = 1
 EXPORTED = [
     "exl3_version", "exl3_ctx_create", "exl3_ctx_destroy", "exl3_last_error",
     "exl3_ctx_set_stream", "exl3_set_codebook", "exl3_get_codebook", "exl3_set_codebook_kind",
-    "exl3_regularize",
+    "exl3_regularize", "exl3_unregularize",
     "exl3_channel_normalize", "exl3_encode_tiles", "exl3_encode_tiles_f16", "exl3_decode_tiles", "exl3_quantize_matrix",
     "exl3_quantize_matrix_ldlq", "exl3_quantize_matrix_grid", "exl3_quantize_matrix_f16", "exl3_scratch_per_tile",
     "exl3_ctx_set_timing", "exl3_ctx_read_timing",
@@ -96,6 +96,8 @@ def load_library():
     lib.exl3_get_codebook.argtypes = [vp, vp]
     lib.exl3_regularize.restype = i32
     lib.exl3_regularize.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
+    lib.exl3_unregularize.restype = i32
+    lib.exl3_unregularize.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.exl3_channel_normalize.restype = i32
     lib.exl3_channel_normalize.argtypes = [vp, vp, i32, i32, i32, vp, f64, vp, vp, vp]
     lib.exl3_encode_tiles.restype = i32
@@ -254,6 +256,20 @@ class Context:
             _ptr(sv.contiguous()), _ptr(out), EXL3_TILE_MAJOR if tile_major else EXL3_ROW_MAJOR,
             _ptr(sums), _ptr(flag)))
         return out, sums, flag
+
+    def unregularize(self, w_reg: torch.Tensor, rows: int, cols: int, su: torch.Tensor,
+                     sv: torch.Tensor, had_block: int = 128, tile_major: bool = True):
+        """Inverse regularization of float32 weights (tile-major [tiles, 256] or row-major
+        [rows, cols]) -> row-major float32 [rows, cols]."""
+        _need(w_reg, torch.float32, tuple(w_reg.shape), "w_reg")
+        if w_reg.numel() != rows * cols:
+            raise ValueError("w_reg has %d elements, not %d" % (w_reg.numel(), rows * cols))
+        out = torch.empty(rows, cols, dtype=torch.float32, device=w_reg.device)
+        self._sync_stream()
+        self._check(self.lib.exl3_unregularize(
+            self.handle, _ptr(w_reg.contiguous()), EXL3_TILE_MAJOR if tile_major else EXL3_ROW_MAJOR,
+            rows, cols, had_block, _ptr(su.contiguous()), _ptr(sv.contiguous()), _ptr(out)))
+        return out
 
     def channel_normalize(self, w: torch.Tensor, su: torch.Tensor, floor: float = 0.1):
         """Out-channel RMS normalization: returns (w_norm float32 [rows, cols],

@@ -554,6 +554,27 @@ int exl3_regularize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int col
     return EXL3_OK;
 }
 
+int exl3_unregularize(exl3_ctx *ctx, const float *w_reg, int in_layout, int rows, int cols,
+                      int had_block, const float *su, const float *sv, float *out) {
+    if (!ctx) return EXL3_EINVAL;
+    if (!w_reg || !su || !sv || !out) return fail(ctx, EXL3_EINVAL, "null pointer");
+    if (in_layout != EXL3_ROW_MAJOR && in_layout != EXL3_TILE_MAJOR)
+        return fail(ctx, EXL3_EINVAL, "layout %d", in_layout);
+    if (had_block != 64 && had_block != 128)
+        return fail(ctx, EXL3_EUNSUPPORTED, "Hadamard block %d (supported: 64, 128)", had_block);
+    if (rows <= 0 || cols <= 0 || rows % had_block || cols % had_block)
+        return fail(ctx, EXL3_EINVAL, "shape %d x %d is not a positive multiple of %d", rows,
+                    cols, had_block);
+    const size_t bytes = (size_t)rows * cols * sizeof(float);
+    const char *ib = reinterpret_cast<const char *>(w_reg), *ob = reinterpret_cast<const char *>(out);
+    if (ob < ib + bytes && ib < ob + bytes) return fail(ctx, EXL3_EINVAL, "out overlaps w_reg");
+    int rc;
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    EXL3_HIP(ctx, exl3::launch_unregularize(w_reg, in_layout, rows, cols, had_block, su, sv, out,
+                                            ctx->stream));
+    return EXL3_OK;
+}
+
 int exl3_channel_normalize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
                            const float *su, double floor, float *w_norm, float *su_folded,
                            double *row_rms) {

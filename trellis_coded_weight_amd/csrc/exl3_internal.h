@@ -163,6 +163,9 @@ hipError_t launch_regularize(const void *w, int w_dtype, int rows, int cols, int
                              const float *su, const float *sv, float *out, int layout,
                              float *tile_sumsq, int *nonfinite, hipStream_t stream);
 
+hipError_t launch_unregularize(const float *in, int in_layout, int rows, int cols, int had_block,
+                               const float *su, const float *sv, float *out, hipStream_t stream);
+
 hipError_t launch_channel_normalize(const void *w, int w_dtype, int rows, int cols,
                                     const float *su, double floor_value, float *w_norm,
                                     float *su_folded, double *row_rms, hipStream_t stream);

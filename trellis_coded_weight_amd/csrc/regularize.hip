@@ -107,6 +107,57 @@ regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__
     }
 }
 
+// Inverse of the regularization (H is symmetric and orthonormal, so its own
+// inverse): W = diag(su) H_l W_reg H_r diag(sv), evaluated as left transform,
+// x rn(1/sqrt(B)), right transform, x rn(1/sqrt(B)), then x su[row], x sv[col]
+// (su, sv may be the folded channel scales, not only +-1).  Input tile-major
+// or row-major, output row-major.
+template <int B>
+__global__ void __launch_bounds__(B)
+unregularize_kernel(const float *__restrict__ in, int rows, int cols, int in_layout,
+                    const float *__restrict__ su, const float *__restrict__ sv,
+                    float *__restrict__ out) {
+    __shared__ float blk[B][B + 1];
+    const int j = threadIdx.x;
+    const int r0 = blockIdx.y * B, c0 = blockIdx.x * B;
+    const float c = norm_const<B>();
+    const int TC = cols / 16;
+    constexpr int TB = B / 16;
+    for (int idx = j; idx < B * B; idx += B) {
+        int rr, cc;
+        size_t src;
+        if (in_layout == 1) {
+            const int lt = idx >> 8, t = idx & 255, tr = lt / TB, tc = lt % TB;
+            rr = tr * 16 + (t >> 4);
+            cc = tc * 16 + (t & 15);
+            src = ((size_t)(r0 / 16 + tr) * TC + (c0 / 16 + tc)) * 256 + t;
+        } else {
+            rr = idx / B;
+            cc = idx % B;
+            src = (size_t)(r0 + rr) * cols + c0 + cc;
+        }
+        blk[rr][cc] = in[src];
+    }
+    __syncthreads();
+    float a[B];
+#pragma unroll
+    for (int r = 0; r < B; ++r) a[r] = blk[r][j];
+    fwht_regs<B>(a);
+#pragma unroll
+    for (int r = 0; r < B; ++r) blk[r][j] = a[r] * c;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < B; ++q) a[q] = blk[j][q];
+    fwht_regs<B>(a);
+#pragma unroll
+    for (int q = 0; q < B; ++q) blk[j][q] = a[q] * c;
+    __syncthreads();
+    for (int idx = j; idx < B * B; idx += B) {
+        const int rr = idx / B, cc = idx % B;
+        out[(size_t)(r0 + rr) * cols + c0 + cc] = (blk[rr][cc] * su[r0 + rr]) * sv[c0 + cc];
+    }
+}
+
 template <int B, typename Tin>
 hipError_t launch_reg_t(const void *w, int rows, int cols, const float *su, const float *sv,
                         float *out, int layout, float *tile_sumsq, int *nonfinite,
@@ -119,6 +170,21 @@ hipError_t launch_reg_t(const void *w, int rows, int cols, const float *su, cons
 }
 
 }  // namespace
+
+hipError_t launch_unregularize(const float *in, int in_layout, int rows, int cols, int had_block,
+                               const float *su, const float *sv, float *out,
+                               hipStream_t stream) {
+    if (rows <= 0 || cols <= 0) return hipSuccess;
+    if (had_block != 64 && had_block != 128) return hipErrorInvalidValue;
+    dim3 grid(cols / had_block, rows / had_block);
+    if (had_block == 64)
+        hipLaunchKernelGGL(unregularize_kernel<64>, grid, dim3(64), 0, stream, in, rows, cols,
+                           in_layout, su, sv, out);
+    else
+        hipLaunchKernelGGL(unregularize_kernel<128>, grid, dim3(128), 0, stream, in, rows, cols,
+                           in_layout, su, sv, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_regularize(const void *w, int w_dtype, int rows, int cols, int had_block,
                              const float *su, const float *sv, float *out, int layout,
