@@ -7,8 +7,9 @@
  *        tail-biting closure), section 4 (16-bit state algebra), section 5
  *        (mul1 codebook, MSB-first container with SWAP16), section 7 (blockwise
  *        Sylvester Hadamard), section 8 (regularization and scale search over a
- *        wrapped-diagonal tile sample), section 2 (bounded scratch, admission
- *        before work, batch halving that keeps results identical).
+ *        wrapped-diagonal tile sample; out-channel normalization), section 2
+ *        (bounded scratch, admission before work, batch halving that keeps
+ *        results identical).
  *   [P2] "JEV-9B EXL3 K=2 (mul1) Checkpoint" model card, section 2
  *        (golden-section scale search).
  *
@@ -18,10 +19,13 @@
  *     never keeps it beyond the work it enqueued on the context's stream.
  *   - Calls return EXL3_OK (0) or a negative EXL3_E* code and never throw.
  *     exl3_last_error() gives the message.  Arguments are validated before
- *     anything is enqueued: on an error return no output has been written.
+ *     anything is enqueued: on a validation error no output has been
+ *     written; a failure later in the call (EXL3_ENOMEM, EXL3_EHIP) may leave
+ *     outputs partly written.
  *   - Arithmetic contract: binary32, each subtract / multiply / add rounded on
- *     its own (no fused multiply-add), lowest index on equal costs.  Outputs
- *     are bit-identical for any batch size and scratch limit.
+ *     its own (no fused multiply-add), lowest index on equal costs (the *_f16
+ *     entry points state their binary16 contract).  Outputs are bit-identical
+ *     for any batch size and scratch limit.
  *   - A context is not thread-safe; use one per host thread / stream.  Every
  *     call makes the context's device current on the calling thread.
  *   - Tiles: a 16x16 tile is 256 consecutive floats, element t = 16*row + col;
@@ -189,7 +193,7 @@ int exl3_channel_normalize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, 
  *   states    optional uint16 [n][256]: the state sequence S_0..S_255
  *   tile_sse  optional float [n]: sequential binary32 sum of squared errors of
  *             the decoded tile, which equals the search's own path cost
- * K in {2, 3, 4}.  n may be 0.  Asynchronous (uses the context's scratch).
+ * K in {1, 2, 3, 4}.  n may be 0.  Asynchronous (uses the context's scratch).
  * Errors: EXL3_EINVAL, EXL3_EUNSUPPORTED, EXL3_ENOMEM, EXL3_EHIP.
  */
 int exl3_encode_tiles(exl3_ctx *ctx, const float *x, int64_t n, int K, float scale,
@@ -211,7 +215,7 @@ int exl3_encode_tiles(exl3_ctx *ctx, const float *x, int64_t n, int K, float sca
  *   states    optional uint16 [n][256]: the state sequence S_0..S_255
  *   cost      optional uint16 [n]: the path cost as binary16 bits (the
  *             binary16 sequential sum over the tile of fp16(fp16(x_t - c)^2 + acc))
- * K in {2, 3, 4}.  n may be 0.  Asynchronous (uses the context's scratch).
+ * K in {1, 2, 3, 4}.  n may be 0.  Asynchronous (uses the context's scratch).
  * Errors: EXL3_EINVAL, EXL3_EUNSUPPORTED, EXL3_ENOMEM, EXL3_EHIP.
  */
 int exl3_encode_tiles_f16(exl3_ctx *ctx, const uint16_t *x, int64_t n, int K, uint16_t *packed,
