@@ -65,12 +65,8 @@ __device__ __forceinline__ void lane_butterflies(int g, int (&m)[Geo<K>::GPL], i
     }
 }
 
-// The scaled levels v = rn(scale * c) of the lane's 64 states.  K = 2..4 keep
-// them as binary32 registers.  K = 1 needs 32 more registers for the
-// predecessor costs it snapshots (single LDS buffer), so it keeps the binary16
-// code values two per register and forms v in each step with one
-// v_fma_mix_f32 (the binary16 operand converts exactly, the product with the
-// binary32 scale is rounded once: the same v).
+// The scaled levels v = rn(scale * c) of the lane's 64 states, as binary32
+// registers for the whole pass.
 template <int K>
 struct Levels {
     using G = Geo<K>;
@@ -79,31 +75,6 @@ struct Levels {
         v[i][k][bb] = scale * half_bits_to_float(c);
     }
     __device__ __forceinline__ float at(int i, int k, int bb) const { return v[i][k][bb]; }
-};
-
-template <>
-struct Levels<1> {
-    using G = Geo<1>;
-    uint32_t h[G::GPL][G::NB];   // code values of b = 0 (low half) and b = 1 (high half)
-    float scale;
-    __device__ __forceinline__ void set(int i, int k, int bb, uint16_t c, float s) {
-        scale = s;
-        if (bb == 0)
-            h[i][k] = c;
-        else
-            h[i][k] |= (uint32_t)c << 16;
-    }
-    __device__ __forceinline__ float at(int i, int k, int bb) const {
-        // volatile: recomputed where used, never hoisted out of the step loop
-        float r;
-        if (bb == 0)
-            asm volatile("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]"
-                         : "=v"(r) : "v"(h[i][k]), "v"(scale));
-        else
-            asm volatile("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-                         : "=v"(r) : "v"(h[i][k]), "v"(scale));
-        return r;
-    }
 };
 
 // Append one bit per lane to acc: acc = 2 * acc + mask[lane] in one VALU op
@@ -263,10 +234,25 @@ __device__ __forceinline__ uint32_t trellis_step(
     const Levels<K> &lv, const int (&m)[Geo<K>::GPL], int b0) {
     using G = Geo<K>;
     float Mk[G::GPL][G::NB];
+    // K = 1: the lane's 32 reads and 16 writes span 128 KiB, past the 16-bit
+    // LDS immediates; with the lane's index opaque to the compiler they are
+    // addressed from four base registers plus immediates, not one address
+    // register each
+    int lb = m[0];
+    if constexpr (K == 1) asm volatile("" : "+v"(lb));
+    if constexpr (K == 1) {
+        const float *r0 = Mc + lb, *r1 = Mc + (1 << G::MBITS) + lb;
 #pragma unroll
-    for (int i = 0; i < G::GPL; ++i)
+        for (int i = 0; i < G::GPL; ++i) {
+            Mk[i][0] = r0[kLanes * i];
+            Mk[i][1] = r1[kLanes * i];
+        }
+    } else {
 #pragma unroll
-        for (int k = 0; k < G::NB; ++k) Mk[i][k] = Mc[(k << G::MBITS) | m[i]];
+        for (int i = 0; i < G::GPL; ++i)
+#pragma unroll
+            for (int k = 0; k < G::NB; ++k) Mk[i][k] = Mc[(k << G::MBITS) | m[i]];
+    }
     // K = 1 keeps a single buffer of tracked minima (128 KiB): every lane has
     // read its predecessors before any lane overwrites them
     if constexpr (K == 1) __syncthreads();
@@ -331,7 +317,9 @@ __device__ __forceinline__ uint32_t trellis_step(
                 }
                 outv[bb] = BITS ? Acs<K>::run(a, bits) : min_only<G::NB>(a);
             }
-            float *dst = Mn + ((m[i] << K) | b0);
+            float *dst = K == 1 ? Mn + 2 * lb + (i < G::GPL / 2 ? 0 : (1 << (G::Kr - 1))) +
+                                      2 * kLanes * (i % (G::GPL / 2))
+                                : Mn + ((m[i] << K) | b0);
             if constexpr (G::BPL == 2) {
                 *reinterpret_cast<float2 *>(dst) = make_float2(outv[0], outv[1]);
             } else {
