@@ -115,6 +115,30 @@ __device__ __forceinline__ void push_bits<4>(uint32_t &acc, const uint64_t (&kb)
         : "s"(kb[0]), "s"(kb[1]), "s"(kb[2]), "s"(kb[3]));
 }
 
+// Lowest-index minimum as one binary64 minimum.  A candidate is the register
+// pair {low word: its index k, high word: the bits of its binary32 cost}.
+// Costs are non-negative (or +inf) binary32 values, whose bit patterns order
+// like the values, and such a pair read as a binary64 number is non-negative
+// and never a NaN; binary64 order of these pairs is therefore the
+// lexicographic order of (cost, index), and v_min_f64 returns the cheaper
+// candidate, the lower index on equal costs -- exactly, since it returns one
+// of its operands (double-precision denormals are kept).  The winner's high
+// word is the new minimum, its low word the backpointer.
+__device__ __forceinline__ double cost_index(float a, uint32_t k) {
+    return __builtin_bit_cast(double, ((uint64_t)__float_as_uint(a) << 32) | k);
+}
+__device__ __forceinline__ double lex_min(double a, double b) {
+    double r;
+    asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+// acc = (acc << K) | k in one instruction (the compiler would otherwise
+// re-associate the chain of insertions into shifts and three-way ors)
+template <int K>
+__device__ __forceinline__ void push_index(uint32_t &acc, uint32_t k) {
+    asm("v_lshl_or_b32 %0, %0, %2, %1" : "+v"(acc) : "v"(k), "i"(K));
+}
+
 // Minimum of the 2^K candidates and the lowest index reaching it, with the K
 // index bits appended to acc (high bit first).
 //
@@ -134,20 +158,6 @@ struct Acs<1> {
         const float m = __builtin_fminf(a[0], a[1]);
         const uint64_t kb[1] = {__builtin_amdgcn_ballot_w64(a[0] > m)};
         push_bits<1>(acc, kb);
-        return m;
-    }
-};
-
-template <>
-struct Acs<2> {
-    static __device__ __forceinline__ float run(const float (&a)[4], uint32_t &acc) {
-        const float m01 = __builtin_fminf(a[0], a[1]);
-        const float m = __builtin_fminf(__builtin_fminf(m01, a[2]), a[3]);
-        const bool r1 = m01 > m;                      // index in {2, 3}
-        const float l0 = r1 ? a[2] : a[0];            // left leaf of the chosen pair
-        const bool r0 = l0 > m;
-        const uint64_t kb[2] = {__builtin_amdgcn_ballot_w64(r1), __builtin_amdgcn_ballot_w64(r0)};
-        push_bits<2>(acc, kb);
         return m;
     }
 };
@@ -224,10 +234,10 @@ __device__ __forceinline__ float min_only(const float (&a)[NB]) {
 // butterflies from Mc, write the new minima to Mn and return the backpointer
 // word (BITS) -- or only the minima (!BITS, steps whose backpointers are never
 // read).  At K = 2 with bits the lane's 16 updates are software-pipelined so
-// that no compare result is consumed right after it is produced: iteration e
-// issues the branch metrics of update e, the walk of update e-1 (select the
-// left leaf of the chosen pair, compare), the tree of update e (minima and the
-// top compare) and the bit insertion of update e-2.
+// that no binary64 minimum is read right after it is written: iteration e
+// issues the branch metrics of update e and the two pair minima of its
+// candidates, the final minimum (and the store of the new tracked minimum) of
+// update e-1, and the index insertion of update e-2.
 template <int K, bool BITS>
 __device__ __forceinline__ uint32_t trellis_step(
     float xt, const float *__restrict__ Mc, float *__restrict__ Mn,
@@ -259,46 +269,36 @@ __device__ __forceinline__ uint32_t trellis_step(
     uint32_t bits = 0;
     if constexpr (BITS && K == 2) {
         constexpr int NE = G::GPL * G::BPL;
-        float mn[NE], a0[NE], a2[NE];
-        bool r1[NE], r0[NE];
+        double T01[2], T23[2];
+        uint32_t kk[2];
 #pragma unroll
         for (int e = 0; e < NE + 2; ++e) {
             step_priority(e, NE);
-            float a[4];
             if (e < NE) {
                 const int i = e / G::BPL, bb = e % G::BPL;
+                double c[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     float d = xt - lv.at(i, k, bb);
                     float q = d * d;
-                    a[k] = Mk[i][k] + q;
+                    c[k] = cost_index(Mk[i][k] + q, (uint32_t)k);
                 }
+                T01[e & 1] = lex_min(c[0], c[1]);
+                T23[e & 1] = lex_min(c[2], c[3]);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (e >= 1 && e - 1 < NE) {
-                const float l0 = r1[e - 1] ? a2[e - 1] : a0[e - 1];
-                r0[e - 1] = l0 > mn[e - 1];
+                const int f = e - 1, i = f / G::BPL, bb = f % G::BPL;
+                const uint64_t w = __builtin_bit_cast(uint64_t, lex_min(T01[f & 1], T23[f & 1]));
+                kk[f & 1] = (uint32_t)w;
+                // one store per new minimum: the minima are the high halves
+                // of register pairs, so a four-wide store would need moves
+                __hip_atomic_store(Mn + ((m[i] << K) | (b0 + bb)),
+                                   __uint_as_float((uint32_t)(w >> 32)), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (e < NE) {
-                const float m01 = __builtin_fminf(a[0], a[1]);
-                mn[e] = __builtin_fminf(__builtin_fminf(m01, a[2]), a[3]);
-                r1[e] = m01 > mn[e];
-                a0[e] = a[0];
-                a2[e] = a[2];
-                const int i = e / G::BPL, bb = e % G::BPL;
-                if (bb == G::BPL - 1) {
-                    float *dst = Mn + ((m[i] << K) | b0);
-                    *reinterpret_cast<float4 *>(dst) =
-                        make_float4(mn[e - 3], mn[e - 2], mn[e - 1], mn[e]);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if (e >= 2) {
-                const uint64_t kb[2] = {__builtin_amdgcn_ballot_w64(r1[e - 2]),
-                                        __builtin_amdgcn_ballot_w64(r0[e - 2])};
-                push_bits<2>(bits, kb);
-            }
+            if (e >= 2) push_index<2>(bits, kk[e & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
@@ -315,7 +315,8 @@ __device__ __forceinline__ uint32_t trellis_step(
                     float q = d * d;
                     a[k] = Mk[i][k] + q;
                 }
-                outv[bb] = BITS ? Acs<K>::run(a, bits) : min_only<G::NB>(a);
+                if constexpr (BITS) outv[bb] = Acs<K>::run(a, bits);
+                else outv[bb] = min_only<G::NB>(a);
             }
             float *dst = K == 1 ? Mn + 2 * lb + (i < G::GPL / 2 ? 0 : (1 << (G::Kr - 1))) +
                                       2 * kLanes * (i % (G::GPL / 2))
