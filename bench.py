@@ -439,6 +439,8 @@ def main():
         sys.exit(2)
     rank = int(os.environ.get("RANK", "0"))
 
+    import math
+
     import numpy as np
     import torch
     import trellis_coded_weight_amd as T
@@ -545,6 +547,9 @@ def main():
         threads = max(1, min(os.cpu_count() or 1, 16))
         cpu = cpu_baseline(m, K, out["scale"], n_tiles, threads, args.cpu_tiles)
 
+    # ||W - W_hat||_F / ||W||_F: the error is measured in the regularized domain,
+    # whose transform is orthonormal, so its norm is the original domain's
+    rel_frob = math.sqrt(out["mse"] * R * C / float(np.sum(np.square(m.w, dtype=np.float64))))
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -569,6 +574,7 @@ def main():
         "codebooks_k2": codebooks,
         "scale": out["scale"],
         "mse": out["mse"],
+        "rel_frobenius": rel_frob,
         "stages_ms_per_step": stages,
         "roofline": roofline,
         "cpu_baseline": cpu,

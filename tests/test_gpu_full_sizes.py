@@ -148,6 +148,10 @@ def test_workload2_4096x4096_k2(ctx):
     got, rms = _check_matrix(ctx, m, 2, exact_gss=True)
     nmse = got["mse"] / rms ** 2
     assert 2.0 ** -4 < nmse < _lloyd(2)
+    # relative Frobenius error inside the K = 2 band the checkpoint card prints
+    with open(os.path.join(GOLDEN, "pages_figures.json")) as f:
+        lo, hi = json.load(f)["k2_rel_frobenius_band"]
+    assert lo <= math.sqrt(nmse) <= hi
 
 
 def test_workload3_heavy_tailed_k4(ctx):

@@ -60,14 +60,22 @@ def test_encode_tiles_scaled_inputs(ctx, K, scale):
     assert np.array_equal(_bits(sse.cpu().numpy()), _bits(want["sse"]))
 
 
-def test_edge_inputs(ctx):
-    """Zeros, a constant tile, huge outliers, tiny (subnormal-producing) values."""
-    K = 2
-    x = np.zeros((5, 256), np.float32)
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+def test_edge_inputs(ctx, K):
+    """Zeros, a constant tile, huge outliers, tiny (subnormal-producing) values,
+    and squared errors past the binary32 range: from the step of an input of
+    2e19 every cost is +inf, so every later minimum is a tie among infinities
+    and the lowest index decides (at K = 2 the argmin compares {index, cost}
+    register pairs as binary64, whose high word is then 0x7F800000)."""
+    x = np.zeros((7, 256), np.float32)
     x[1] = 0.37
     x[2, ::17] = 1.0e4
     x[3] = np.float32(1e-20) * np.arange(256, dtype=np.float32)
     x[4] = workloads.random_tiles(1, 5)[0] * np.float32(1e-19)
+    x[5] = workloads.random_tiles(1, 6)[0]
+    x[5, 200] = 2.0e19
+    x[6, ::2] = 2.0e19
+    x[6, 1::2] = -2.0e19
     for scale in (1.0, 1e-19):
         want = oracle.encode_tiles(x, K, scale)
         _, states, sse = ctx.encode_tiles(torch.from_numpy(x).to(DEV), K, scale)
