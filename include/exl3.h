@@ -17,6 +17,14 @@
  *   - Every array argument is a DEVICE pointer on the context's device unless
  *     stated otherwise; the caller owns it.  The library never frees it and
  *     never keeps it beyond the work it enqueued on the context's stream.
+ *     Before any launch each array is checked to lie inside one allocation
+ *     the context's GPU can address (device memory of that device, managed
+ *     memory, or pinned host memory) that holds every byte the call touches;
+ *     otherwise (plain host memory, another device's memory, a buffer ending
+ *     too early) the call returns EXL3_EINVAL.  A sub-range of a larger
+ *     allocation, such as a caching allocator's segment, is measured against
+ *     that allocation.  Arrays documented as host arrays must not be device
+ *     memory.
  *   - Calls return EXL3_OK (0) or a negative EXL3_E* code and never throw.
  *     exl3_last_error() gives the message.  Arguments are validated before
  *     anything is enqueued: on a validation error no output has been

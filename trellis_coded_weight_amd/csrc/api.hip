@@ -131,6 +131,54 @@ int set_device(exl3_ctx *ctx) {
 
 bool k_supported(int K) { return K >= 1 && K <= 4; }
 
+// Every array argument must lie inside one allocation that the context's GPU
+// can address (its device memory, managed memory or pinned host memory) and
+// span the bytes the call touches.  Plain host memory, another device's
+// memory or a buffer that ends too early is rejected before any launch, where
+// a kernel would otherwise fault.  A sub-range of a larger allocation (a
+// caching allocator's segment) is measured against that allocation.
+int check_span(exl3_ctx *ctx, const void *p, size_t bytes, const char *name) {
+    if (!p || bytes == 0) return EXL3_OK;
+    hipPointerAttribute_t a;
+    std::memset(&a, 0, sizeof a);
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, EXL3_EINVAL, "%s (%p) is not memory the GPU can address", name, p);
+    }
+    if (a.type == hipMemoryTypeUnregistered)
+        return fail(ctx, EXL3_EINVAL, "%s (%p) is host memory unknown to HIP, not device memory",
+                    name, p);
+    if (a.type == hipMemoryTypeDevice && a.device != ctx->device)
+        return fail(ctx, EXL3_EINVAL, "%s is on device %d, the context on device %d", name,
+                    a.device, ctx->device);
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void *>(p)) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, EXL3_EINVAL, "%s (%p) lies in no allocation", name, p);
+    }
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+    if (q < b || q - b > size || bytes > size - (q - b))
+        return fail(ctx, EXL3_EINVAL,
+                    "%s: %zu bytes from %p run past the end of its allocation (%zu bytes from %p)",
+                    name, bytes, p, size, base);
+    return EXL3_OK;
+}
+
+// Host-side tables (codebooks) must not be device memory.
+int check_host(exl3_ctx *ctx, const void *p, const char *name) {
+    hipPointerAttribute_t a;
+    std::memset(&a, 0, sizeof a);
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return EXL3_OK;
+    }
+    if (a.type == hipMemoryTypeDevice)
+        return fail(ctx, EXL3_EINVAL, "%s (%p) is device memory; a host array is expected", name,
+                    p);
+    return EXL3_OK;
+}
+
 void clear_timing(exl3_ctx *ctx) {
     for (auto &r : ctx->timed) {
         (void)hipEventDestroy(r.start);
@@ -494,6 +542,8 @@ int exl3_ctx_read_timing(exl3_ctx *ctx, int kind, double *total_ms, int64_t *lau
 int exl3_set_codebook(exl3_ctx *ctx, const uint16_t *levels_fp16_host) {
     if (!ctx) return EXL3_EINVAL;
     int rc;
+    if (levels_fp16_host && (rc = check_host(ctx, levels_fp16_host, "levels")) != EXL3_OK)
+        return rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
     std::vector<uint16_t> lv(65536);
     if (levels_fp16_host) {
@@ -531,6 +581,7 @@ int exl3_set_codebook_kind(exl3_ctx *ctx, int kind) {
 int exl3_get_codebook(exl3_ctx *ctx, uint16_t *levels_fp16_host) {
     if (!ctx || !levels_fp16_host) return fail(ctx, EXL3_EINVAL, "null argument");
     int rc;
+    if ((rc = check_host(ctx, levels_fp16_host, "levels")) != EXL3_OK) return rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
     EXL3_HIP(ctx, hipMemcpyAsync(levels_fp16_host, ctx->d_levels, 65536 * sizeof(uint16_t),
                                  hipMemcpyDeviceToHost, ctx->stream));
@@ -548,6 +599,14 @@ int exl3_regularize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int col
     if (!w_reg) return fail(ctx, EXL3_EINVAL, "null output");
     if (out_layout != EXL3_ROW_MAJOR && out_layout != EXL3_TILE_MAJOR)
         return fail(ctx, EXL3_EINVAL, "layout %d", out_layout);
+    const size_t nel = (size_t)rows * cols, ntiles = nel / 256;
+    if ((rc = check_span(ctx, w, nel * (w_dtype == EXL3_BF16 ? 2 : 4), "w")) != EXL3_OK ||
+        (rc = check_span(ctx, su, (size_t)rows * sizeof(float), "su")) != EXL3_OK ||
+        (rc = check_span(ctx, sv, (size_t)cols * sizeof(float), "sv")) != EXL3_OK ||
+        (rc = check_span(ctx, w_reg, nel * sizeof(float), "w_reg")) != EXL3_OK ||
+        (rc = check_span(ctx, tile_sumsq, ntiles * sizeof(float), "tile_sumsq")) != EXL3_OK ||
+        (rc = check_span(ctx, nonfinite, sizeof(int), "nonfinite")) != EXL3_OK)
+        return rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
     EXL3_HIP(ctx, exl3::launch_regularize(w, w_dtype, rows, cols, had_block, su, sv, w_reg,
                                           out_layout, tile_sumsq, nonfinite, ctx->stream));
@@ -569,6 +628,11 @@ int exl3_unregularize(exl3_ctx *ctx, const float *w_reg, int in_layout, int rows
     const char *ib = reinterpret_cast<const char *>(w_reg), *ob = reinterpret_cast<const char *>(out);
     if (ob < ib + bytes && ib < ob + bytes) return fail(ctx, EXL3_EINVAL, "out overlaps w_reg");
     int rc;
+    if ((rc = check_span(ctx, w_reg, bytes, "w_reg")) != EXL3_OK ||
+        (rc = check_span(ctx, su, (size_t)rows * sizeof(float), "su")) != EXL3_OK ||
+        (rc = check_span(ctx, sv, (size_t)cols * sizeof(float), "sv")) != EXL3_OK ||
+        (rc = check_span(ctx, out, bytes, "out")) != EXL3_OK)
+        return rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
     EXL3_HIP(ctx, exl3::launch_unregularize(w_reg, in_layout, rows, cols, had_block, su, sv, out,
                                             ctx->stream));
@@ -591,6 +655,14 @@ int exl3_channel_normalize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, 
     if (ob < wb + in_bytes && wb < ob + (size_t)rows * cols * sizeof(float))
         return fail(ctx, EXL3_EINVAL, "w_norm overlaps w");
     int rc;
+    if ((rc = check_span(ctx, w, in_bytes, "w")) != EXL3_OK ||
+        (rc = check_span(ctx, su, (size_t)rows * sizeof(float), "su")) != EXL3_OK ||
+        (rc = check_span(ctx, w_norm, (size_t)rows * cols * sizeof(float), "w_norm")) !=
+            EXL3_OK ||
+        (rc = check_span(ctx, su_folded, (size_t)rows * sizeof(float), "su_folded")) !=
+            EXL3_OK ||
+        (rc = check_span(ctx, row_rms, (size_t)rows * sizeof(double), "row_rms")) != EXL3_OK)
+        return rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
     if ((rc = check_signs(ctx, su, rows, "su")) != EXL3_OK) return rc;
     EXL3_HIP(ctx, exl3::launch_channel_normalize(w, w_dtype, rows, cols, su, floor, w_norm,
@@ -607,6 +679,12 @@ int exl3_encode_tiles(exl3_ctx *ctx, const float *x, int64_t n, int K, float sca
     if (!std::isfinite(scale)) return fail(ctx, EXL3_EINVAL, "scale is not finite");
     if (n > (int64_t)INT32_MAX) return fail(ctx, EXL3_EINVAL, "too many tiles");
     int rc;
+    const size_t nt = (size_t)n;
+    if ((rc = check_span(ctx, x, nt * 256 * sizeof(float), "x")) != EXL3_OK ||
+        (rc = check_span(ctx, packed, nt * 16 * K * sizeof(uint16_t), "packed")) != EXL3_OK ||
+        (rc = check_span(ctx, states, nt * 256 * sizeof(uint16_t), "states")) != EXL3_OK ||
+        (rc = check_span(ctx, tile_sse, nt * sizeof(float), "tile_sse")) != EXL3_OK)
+        return rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
     return encode_chain(ctx, x, nullptr, n, K, scale, packed, states, tile_sse, nullptr, nullptr);
 }
@@ -619,6 +697,12 @@ int exl3_encode_tiles_f16(exl3_ctx *ctx, const uint16_t *x, int64_t n, int K, ui
     if (n > 0 && (!x || !packed)) return fail(ctx, EXL3_EINVAL, "null input or output");
     if (n > (int64_t)INT32_MAX) return fail(ctx, EXL3_EINVAL, "too many tiles");
     int rc;
+    const size_t nt = (size_t)n;
+    if ((rc = check_span(ctx, x, nt * 256 * sizeof(uint16_t), "x")) != EXL3_OK ||
+        (rc = check_span(ctx, packed, nt * 16 * K * sizeof(uint16_t), "packed")) != EXL3_OK ||
+        (rc = check_span(ctx, states, nt * 256 * sizeof(uint16_t), "states")) != EXL3_OK ||
+        (rc = check_span(ctx, cost, nt * sizeof(uint16_t), "cost")) != EXL3_OK)
+        return rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
     return encode_chain_f16(ctx, x, n, K, packed, states, cost);
 }
@@ -632,6 +716,10 @@ int exl3_decode_tiles(exl3_ctx *ctx, const uint16_t *packed, int64_t n, int K, f
     if (!std::isfinite(scale)) return fail(ctx, EXL3_EINVAL, "scale is not finite");
     if (n > (int64_t)INT32_MAX) return fail(ctx, EXL3_EINVAL, "too many tiles");
     int rc;
+    const size_t nt = (size_t)n;
+    if ((rc = check_span(ctx, packed, nt * 16 * K * sizeof(uint16_t), "packed")) != EXL3_OK ||
+        (rc = check_span(ctx, out, nt * 256 * sizeof(float), "out")) != EXL3_OK)
+        return rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
     EXL3_HIP(ctx, exl3::launch_decode(packed, n, K, scale, ctx->d_levels, out, ctx->stream));
     return EXL3_OK;
@@ -684,6 +772,7 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
                                 int K, int had_block, const float *su, const float *sv,
                                 const exl3_gss *gss, const exl3_grid *grid, float fixed_scale,
                                 uint16_t *packed, float *scale_out, float *scale_chosen,
+                                const float *w_hat, const float *tile_out, const float *L,
                                 bool f16 = false) {
     if (!ctx) return EXL3_EINVAL;
     int rc;
@@ -707,6 +796,19 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
                         gss->lo, gss->hi);
     } else if (!std::isfinite(fixed_scale)) {
         return fail(ctx, EXL3_EINVAL, "fixed scale is not finite");
+    }
+    {
+        const size_t nel = (size_t)rows * cols, nt = nel / 256;
+        if ((rc = check_span(ctx, w, nel * (w_dtype == EXL3_BF16 ? 2 : 4), "w")) != EXL3_OK ||
+            (rc = check_span(ctx, su, (size_t)rows * sizeof(float), "su")) != EXL3_OK ||
+            (rc = check_span(ctx, sv, (size_t)cols * sizeof(float), "sv")) != EXL3_OK ||
+            (rc = check_span(ctx, packed, nt * 16 * K * sizeof(uint16_t), "packed")) !=
+                EXL3_OK ||
+            (rc = check_span(ctx, w_hat, nel * sizeof(float), "w_hat")) != EXL3_OK ||
+            (rc = check_span(ctx, tile_out, nt * sizeof(float), "per-tile output")) !=
+                EXL3_OK ||
+            (rc = check_span(ctx, L, (size_t)cols * cols * sizeof(float), "L")) != EXL3_OK)
+            return rc;
     }
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
     if ((rc = check_signs(ctx, su, rows, "su")) != EXL3_OK) return rc;
@@ -894,7 +996,8 @@ int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, in
                          float *w_hat, float *tile_sse) {
     float scale = 0.0f;
     int rc = regularize_and_choose_scale(ctx, w, w_dtype, rows, cols, K, had_block, su, sv, gss,
-                                         nullptr, fixed_scale, packed, scale_out, &scale);
+                                         nullptr, fixed_scale, packed, scale_out, &scale, w_hat,
+                                         tile_sse, nullptr);
     if (rc != EXL3_OK) return rc;
     return encode_whole_matrix(ctx, rows, cols, K, scale, packed, scale_out, mse_out, w_hat,
                                tile_sse);
@@ -908,7 +1011,8 @@ int exl3_quantize_matrix_grid(exl3_ctx *ctx, const void *w, int w_dtype, int row
     if (!grid) return fail(ctx, EXL3_EINVAL, "null grid");
     float scale = 0.0f;
     int rc = regularize_and_choose_scale(ctx, w, w_dtype, rows, cols, K, had_block, su, sv,
-                                         nullptr, grid, 0.0f, packed, scale_out, &scale);
+                                         nullptr, grid, 0.0f, packed, scale_out, &scale, w_hat,
+                                         tile_sse, nullptr);
     if (rc != EXL3_OK) return rc;
     return encode_whole_matrix(ctx, rows, cols, K, scale, packed, scale_out, mse_out, w_hat,
                                tile_sse);
@@ -921,7 +1025,8 @@ int exl3_quantize_matrix_f16(exl3_ctx *ctx, const void *w, int w_dtype, int rows
     if (!ctx) return EXL3_EINVAL;
     float scale = 0.0f;
     int rc = regularize_and_choose_scale(ctx, w, w_dtype, rows, cols, K, had_block, su, sv, gss,
-                                         nullptr, fixed_scale, packed, scale_out, &scale, true);
+                                         nullptr, fixed_scale, packed, scale_out, &scale, w_hat,
+                                         tile_sse, nullptr, true);
     if (rc != EXL3_OK) return rc;
     const int64_t ntiles = (int64_t)(rows / 16) * (cols / 16);
     const size_t nel = (size_t)rows * cols;
@@ -958,7 +1063,8 @@ int exl3_quantize_matrix_ldlq(exl3_ctx *ctx, const void *w, int w_dtype, int row
     if (!L) return fail(ctx, EXL3_EINVAL, "null factor L");
     float scale = 0.0f;
     int rc = regularize_and_choose_scale(ctx, w, w_dtype, rows, cols, K, had_block, su, sv, gss,
-                                         nullptr, fixed_scale, packed, scale_out, &scale);
+                                         nullptr, fixed_scale, packed, scale_out, &scale, w_hat,
+                                         tile_err, L);
     if (rc != EXL3_OK) return rc;
     const int TR = rows / 16, TC = cols / 16;
     const int64_t ntiles = (int64_t)TR * TC;

@@ -90,13 +90,6 @@ __device__ __forceinline__ void push_bits<1>(uint32_t &acc, const uint64_t (&kb)
     asm("v_addc_co_u32_e64 %0, %1, %0, %0, %2" : "+v"(acc), "=&s"(c0) : "s"(kb[0]));
 }
 template <>
-__device__ __forceinline__ void push_bits<2>(uint32_t &acc, const uint64_t (&kb)[2]) {
-    uint64_t c0, c1;
-    asm("v_addc_co_u32_e64 %0, %1, %0, %0, %3\n\t"
-        "v_addc_co_u32_e64 %0, %2, %0, %0, %4"
-        : "+v"(acc), "=&s"(c0), "=&s"(c1) : "s"(kb[0]), "s"(kb[1]));
-}
-template <>
 __device__ __forceinline__ void push_bits<3>(uint32_t &acc, const uint64_t (&kb)[3]) {
     uint64_t c0, c1, c2;
     asm("v_addc_co_u32_e64 %0, %1, %0, %0, %4\n\t"
