@@ -36,8 +36,11 @@
  *     for any batch size and scratch limit.
  *   - A context is not thread-safe; use one per host thread / stream.  Every
  *     call makes the context's device current on the calling thread.
- *   - Tiles: a 16x16 tile is 256 consecutive floats, element t = 16*row + col;
- *     tile tau = tr * (cols/16) + tc of a rows x cols matrix.
+ *   - Tiles: a 16x16 tile is 256 consecutive values in trellis order: position
+ *     t holds the tile's element order[t] (element 16*row + col), order being
+ *     the context's within-tile order (exl3_set_tile_order; by default the
+ *     identity, position t = element t); tile tau = tr * (cols/16) + tc of a
+ *     rows x cols matrix.
  */
 #ifndef EXL3_H
 #define EXL3_H
@@ -108,6 +111,26 @@ int exl3_set_codebook(exl3_ctx *ctx, const uint16_t *levels_fp16_host);
 
 /* Copy the current level table to a HOST buffer of 65,536 uint16. */
 int exl3_get_codebook(exl3_ctx *ctx, uint16_t *levels_fp16_host);
+
+/*
+ * Within-tile order of every tile-major array of this context [P1 section 5:
+ * a fixed 256-element permutation of the positions within a tile, and its
+ * inverse, for the tensor-core decoder; P1 section 3: LDLQ encodes permuted
+ * tiles and reconstructs in matrix order].  The pages do not print the
+ * table, so the caller supplies it:
+ *   order_host  host uint8 [256], a permutation of 0..255: trellis position t
+ *               of a tile holds the tile's element order[t] = 16*row + col.
+ *               NULL (or the identity) restores the natural order.
+ * It applies where tiles meet matrix order: the tile-major layouts of
+ * exl3_regularize (output and per-tile energies, summed in trellis order)
+ * and exl3_unregularize (input), and the whole-matrix calls (their tiles,
+ * w_hat, per-tile outputs and container, and LDLQ's feedback in matrix
+ * order).  exl3_encode_tiles / exl3_decode_tiles take tiles already in
+ * trellis order and are unaffected.  Work enqueued before the call keeps the
+ * previous order.  Errors: EXL3_EINVAL (not a permutation, device memory),
+ * EXL3_ENOMEM, EXL3_EHIP.
+ */
+int exl3_set_tile_order(exl3_ctx *ctx, const uint8_t *order_host);
 
 /*
  * Select one of the procedural codebooks [P1 section 5: mul1, mcg, 3INST; the

@@ -18,5 +18,5 @@ from .reference import (  # noqa: F401
     default_threads, encode_sequences_f16, encode_tiles_f16, f16_sqadd, f16_sub, forward_f16,
     ldlq, quantize_matrix_ldlq, grid_search, GRID_DEFAULT, channel_normalize, CHANNEL_FLOOR,
     mcg_levels_fp16, inst3_levels_fp16, CODEBOOKS, to_f16_inputs, encode_tiles_f16_scaled,
-    quantize_matrix_f16,
+    quantize_matrix_f16, check_order,
 )

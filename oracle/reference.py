@@ -356,16 +356,37 @@ def channel_normalize(w, su, floor=CHANNEL_FLOOR):
     return np.ascontiguousarray(w_n), su_f, r
 
 
-def to_tiles(m):
-    """[R, C] -> [R/16 * C/16, 256]; tile tr*TC + tc, element 16*r + c."""
+def check_order(order):
+    """A within-tile order: trellis position t of a tile holds the tile's element
+    order[t] (element 16*r + c).  The pages name a fixed 256-entry permutation
+    for tensor-core decoding without printing it (README, Format Primitives);
+    None is the natural row-major order."""
+    if order is None:
+        return None
+    o = np.asarray(order, dtype=np.int64)
+    if o.shape != (256,) or not np.array_equal(np.sort(o), np.arange(256)):
+        raise ValueError("a within-tile order is a permutation of 0..255")
+    return o
+
+
+def to_tiles(m, order=None):
+    """[R, C] -> [R/16 * C/16, 256]; tile tr*TC + tc; position t holds element
+    16*r + c = order[t] (t itself without an order)."""
     R, C = m.shape
-    return np.ascontiguousarray(
-        m.reshape(R // 16, 16, C // 16, 16).transpose(0, 2, 1, 3).reshape(-1, 256))
+    t = m.reshape(R // 16, 16, C // 16, 16).transpose(0, 2, 1, 3).reshape(-1, 256)
+    o = check_order(order)
+    return np.ascontiguousarray(t if o is None else t[:, o])
 
 
-def from_tiles(tiles, R, C):
+def from_tiles(tiles, R, C, order=None):
+    t = np.asarray(tiles).reshape(-1, 256)
+    o = check_order(order)
+    if o is not None:
+        rm = np.empty_like(t)
+        rm[:, o] = t
+        t = rm
     return np.ascontiguousarray(
-        np.asarray(tiles).reshape(R // 16, C // 16, 16, 16).transpose(0, 2, 1, 3).reshape(R, C))
+        t.reshape(R // 16, C // 16, 16, 16).transpose(0, 2, 1, 3).reshape(R, C))
 
 
 # --------------------------------------------------------------------------
@@ -494,21 +515,22 @@ def encode_tiles(tiles, K, scale, levels=None, threads=None):
 
 
 def quantize_matrix(w, su, sv, K, had_block=128, gss=(12, 0.5, 2.0), fixed_scale=1.0,
-                    levels=None, threads=None, tiles_subset=None, grid=None):
+                    levels=None, threads=None, tiles_subset=None, grid=None, order=None):
     """Whole-matrix path: regularize, statistics, scale search, final encode.
 
     gss=None uses fixed_scale; grid (a GRID_DEFAULT-shaped tuple), if given,
     replaces the golden-section search with grid_search, the scale being
     (float)(g * rms).  tiles_subset, if given, restricts the FINAL encode to
     those tile indices (the scale search always uses its full sample), which is
-    how large matrices are checked one sampled tile at a time.
+    how large matrices are checked one sampled tile at a time.  order, if given,
+    is the within-tile order of the tiles (to_tiles).
     """
     w = np.asarray(w, dtype=np.float32)
     R, C = w.shape
     if levels is None:
         levels = mul1_levels_fp16()
     w_reg = regularize(w, su, sv, had_block)
-    tiles = to_tiles(w_reg)
+    tiles = to_tiles(w_reg, order)
     TR, TC = R // 16, C // 16
     sumsq = tile_sumsq(tiles)
     rms = matrix_rms(sumsq, R * C)
@@ -575,7 +597,7 @@ def quantize_matrix(w, su, sv, K, had_block=128, gss=(12, 0.5, 2.0), fixed_scale
 # LDLQ error feedback  [P1 item 3: one-sided block LDLQ, bottom-up span
 # traversal, additive target correction from the strictly lower L blocks]
 # --------------------------------------------------------------------------
-def ldlq(w_reg, L, K, scale, levels=None, threads=None):
+def ldlq(w_reg, L, K, scale, levels=None, threads=None, order=None):
     """Quantize the regularized matrix span by span with LDLQ error feedback.
 
     Readings (listed in the design notes): H = L D L^T over the columns, L unit
@@ -585,7 +607,9 @@ def ldlq(w_reg, L, K, scale, levels=None, threads=None):
         T_j = W_j + sum_{i > j} E_i L_ij,   E_i = W_i - What_i   (binary32),
     accumulated per element in the order i ascending, then row t of the block
     ascending, each product and each sum rounded on its own; span j's tiles are
-    then encoded at the fixed scale and What_j = v[states].
+    then encoded at the fixed scale and What_j = v[states].  Tiles are formed
+    in the within-tile order `order` (to_tiles) for encoding and put back in
+    matrix order for the feedback.
     Returns dict(what [R, C], targets [R, C], states [TR*TC, 256] in tile order,
     packed [TR*TC, 16K], err: per tile sequential binary32 sum of (W - What)^2).
     """
@@ -608,24 +632,24 @@ def ldlq(w_reg, L, K, scale, levels=None, threads=None):
                 col = 16 * i + t
                 T = T + E[:, col:col + 1] * L[col:col + 1, cj]
         targets[:, cj] = T
-        r = encode_tiles(to_tiles(T), K, scale, levels, threads)
+        r = encode_tiles(to_tiles(T, order), K, scale, levels, threads)
         states[:, j, :] = r["states"]
-        what[:, cj] = from_tiles(v[r["states"]], R, 16)
+        what[:, cj] = from_tiles(v[r["states"]], R, 16, order)
         E[:, cj] = W[:, cj] - what[:, cj]
     st = states.reshape(TR * TC, 256)
     return {"what": what, "targets": targets, "states": st,
-            "packed": pack_states(st, K), "err": tile_sse(to_tiles(W), st, v)}
+            "packed": pack_states(st, K), "err": tile_sse(to_tiles(W, order), st, v)}
 
 
 def quantize_matrix_ldlq(w, su, sv, K, L, had_block=128, gss=(12, 0.5, 2.0), fixed_scale=1.0,
-                         levels=None, threads=None):
+                         levels=None, threads=None, order=None):
     """Regularize, choose the scale exactly as quantize_matrix does (on the
     matrix without feedback), then run ldlq at that scale."""
     base = quantize_matrix(w, su, sv, K, had_block, gss, fixed_scale, levels, threads,
-                           tiles_subset=np.zeros(0, np.int64))
+                           tiles_subset=np.zeros(0, np.int64), order=order)
     R, C = np.asarray(w).shape
-    w_reg = from_tiles(base["tiles"], R, C)
-    out = ldlq(w_reg, L, K, base["scale"], levels, threads)
+    w_reg = from_tiles(base["tiles"], R, C, order)
+    out = ldlq(w_reg, L, K, base["scale"], levels, threads, order)
     total = 0.0
     for e in out["err"].tolist():
         total += float(e)
@@ -732,7 +756,7 @@ def encode_tiles_f16_scaled(tiles, K, scale, levels=None, threads=None):
 
 
 def quantize_matrix_f16(w, su, sv, K, had_block=128, gss=(12, 0.5, 2.0), fixed_scale=1.0,
-                        levels=None, threads=None, tiles_subset=None):
+                        levels=None, threads=None, tiles_subset=None, order=None):
     """Whole-matrix path with the binary16 encoder inside the scale search.
 
     Regularization, statistics, tile sample and golden section exactly as in
@@ -743,7 +767,7 @@ def quantize_matrix_f16(w, su, sv, K, had_block=128, gss=(12, 0.5, 2.0), fixed_s
     R, C = w.shape
     if levels is None:
         levels = mul1_levels_fp16()
-    tiles = to_tiles(regularize(w, su, sv, had_block))
+    tiles = to_tiles(regularize(w, su, sv, had_block), order)
     TR, TC = R // 16, C // 16
     sumsq = tile_sumsq(tiles)
     rms = matrix_rms(sumsq, R * C)

@@ -29,6 +29,7 @@ EXL3_TILE_MAJOR = 1
 EXPORTED = [
     "exl3_version", "exl3_ctx_create", "exl3_ctx_destroy", "exl3_last_error",
     "exl3_ctx_set_stream", "exl3_set_codebook", "exl3_get_codebook", "exl3_set_codebook_kind",
+    "exl3_set_tile_order",
     "exl3_regularize", "exl3_unregularize",
     "exl3_channel_normalize", "exl3_encode_tiles", "exl3_encode_tiles_f16", "exl3_decode_tiles", "exl3_quantize_matrix",
     "exl3_quantize_matrix_ldlq", "exl3_quantize_matrix_grid", "exl3_quantize_matrix_f16", "exl3_scratch_per_tile",
@@ -94,6 +95,8 @@ def load_library():
     lib.exl3_set_codebook_kind.restype = i32
     lib.exl3_set_codebook_kind.argtypes = [vp, i32]
     lib.exl3_get_codebook.argtypes = [vp, vp]
+    lib.exl3_set_tile_order.restype = i32
+    lib.exl3_set_tile_order.argtypes = [vp, vp]
     lib.exl3_regularize.restype = i32
     lib.exl3_regularize.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
     lib.exl3_unregularize.restype = i32
@@ -228,6 +231,18 @@ class Context:
         """Select a procedural codebook by name: "mul1", "mcg" or "3inst"."""
         self._sync_stream()
         self._check(self.lib.exl3_set_codebook_kind(self.handle, CODEBOOK_KINDS[name]))
+
+    def set_tile_order(self, order):
+        """Within-tile order of tile-major arrays: position t of a tile holds its
+        element order[t] (16 * row + col); None restores the natural order."""
+        self._sync_stream()
+        if order is None:
+            return self._check(self.lib.exl3_set_tile_order(self.handle, None))
+        o = torch.as_tensor(order, dtype=torch.int64).cpu()
+        if o.numel() != 256 or int(o.min()) < 0 or int(o.max()) > 255:
+            raise ValueError("a within-tile order has 256 entries in 0..255")
+        buf = o.to(torch.uint8).contiguous()
+        self._check(self.lib.exl3_set_tile_order(self.handle, ctypes.c_void_p(buf.data_ptr())))
 
     def get_codebook(self) -> torch.Tensor:
         out = torch.empty(65536, dtype=torch.int16)

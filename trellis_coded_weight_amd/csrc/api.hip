@@ -67,6 +67,11 @@ struct exl3_ctx {
     size_t x16_cap = 0;
     uint16_t *d_pk = nullptr;
     size_t pk_cap = 0;
+    // within-tile order of tile-major arrays: 256 bytes position -> element,
+    // then 256 bytes element -> position; has_order is false for the natural
+    // order (the kernels then take null tables)
+    uint8_t *d_order = nullptr;
+    bool has_order = false;
     std::string err;
     // optional per-launch timing (HIP events on the context's stream)
     struct Timed {
@@ -130,6 +135,11 @@ int set_device(exl3_ctx *ctx) {
 }
 
 bool k_supported(int K) { return K >= 1 && K <= 4; }
+
+const uint8_t *tile_order(const exl3_ctx *ctx) { return ctx->has_order ? ctx->d_order : nullptr; }
+const uint8_t *tile_order_inv(const exl3_ctx *ctx) {
+    return ctx->has_order ? ctx->d_order + 256 : nullptr;
+}
 
 // Every array argument must lie inside one allocation that the context's GPU
 // can address (its device memory, managed memory or pinned host memory) and
@@ -483,7 +493,7 @@ void exl3_ctx_destroy(exl3_ctx *ctx) {
                     ctx->d_cost,        ctx->d_idx,         ctx->d_wreg,        ctx->d_sumsq,
                     ctx->d_sse,         ctx->d_flag,        ctx->d_err_tiles,   ctx->d_span_target,
                     ctx->d_span_what,   ctx->d_span_packed, ctx->d_gs,          ctx->d_x16,
-                    ctx->d_pk};
+                    ctx->d_pk,          ctx->d_order};
     for (void *p : bufs)
         if (p) (void)hipFree(p);
     delete ctx;
@@ -578,6 +588,49 @@ int exl3_set_codebook_kind(exl3_ctx *ctx, int kind) {
     return EXL3_OK;
 }
 
+int exl3_set_tile_order(exl3_ctx *ctx, const uint8_t *order_host) {
+    if (!ctx) return EXL3_EINVAL;
+    int rc;
+    uint8_t tab[512];
+    bool identity = true;
+    if (order_host) {
+        if ((rc = check_host(ctx, order_host, "order")) != EXL3_OK) return rc;
+        bool seen[256] = {};
+        for (int t = 0; t < 256; ++t) {
+            const uint8_t e = order_host[t];
+            if (seen[e])
+                return fail(ctx, EXL3_EINVAL,
+                            "order is not a permutation of 0..255 (element %d appears twice)",
+                            (int)e);
+            seen[e] = true;
+            tab[t] = e;
+            tab[256 + e] = (uint8_t)t;
+            identity = identity && e == t;
+        }
+    }
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    if (identity) {
+        ctx->has_order = false;
+        return EXL3_OK;
+    }
+    if (!ctx->d_order) {
+        void *p = nullptr;
+        hipError_t e = hipMalloc(&p, sizeof tab);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(ctx, EXL3_ENOMEM, "device allocation of the order table failed: %s",
+                        hipGetErrorString(e));
+        }
+        ctx->d_order = static_cast<uint8_t *>(p);
+    }
+    // in stream order: work already enqueued keeps reading the previous table
+    EXL3_HIP(ctx, hipMemcpyAsync(ctx->d_order, tab, sizeof tab, hipMemcpyHostToDevice,
+                                 ctx->stream));
+    EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    ctx->has_order = true;
+    return EXL3_OK;
+}
+
 int exl3_get_codebook(exl3_ctx *ctx, uint16_t *levels_fp16_host) {
     if (!ctx || !levels_fp16_host) return fail(ctx, EXL3_EINVAL, "null argument");
     int rc;
@@ -609,7 +662,8 @@ int exl3_regularize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int col
         return rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
     EXL3_HIP(ctx, exl3::launch_regularize(w, w_dtype, rows, cols, had_block, su, sv, w_reg,
-                                          out_layout, tile_sumsq, nonfinite, ctx->stream));
+                                          out_layout, tile_sumsq, nonfinite, tile_order(ctx),
+                                          ctx->stream));
     return EXL3_OK;
 }
 
@@ -635,7 +689,7 @@ int exl3_unregularize(exl3_ctx *ctx, const float *w_reg, int in_layout, int rows
         return rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
     EXL3_HIP(ctx, exl3::launch_unregularize(w_reg, in_layout, rows, cols, had_block, su, sv, out,
-                                            ctx->stream));
+                                            tile_order(ctx), ctx->stream));
     return EXL3_OK;
 }
 
@@ -825,7 +879,7 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
     int reg_id = open_timed(ctx, EXL3_KERNEL_REGULARIZE, ntiles);
     EXL3_HIP(ctx, exl3::launch_regularize(w, w_dtype, rows, cols, had_block, su, sv, ctx->d_wreg,
                                           EXL3_TILE_MAJOR, ctx->d_sumsq, ctx->d_flag,
-                                          ctx->stream));
+                                          tile_order(ctx), ctx->stream));
     close_timed(ctx, reg_id);
     std::vector<float> sumsq((size_t)ntiles);
     int flag = 0;
@@ -1085,6 +1139,7 @@ int exl3_quantize_matrix_ldlq(exl3_ctx *ctx, const void *w, int w_dtype, int row
     // spans from the last tile column to the first: target, encode, commit
     for (int j = TC - 1; j >= 0; --j) {
         EXL3_HIP(ctx, exl3::launch_ldlq_target(ctx->d_wreg, ctx->d_err_tiles, L, TR, TC, j,
+                                               tile_order_inv(ctx),
                                                ctx->d_span_target, ctx->stream));
         if ((rc = encode_chain(ctx, ctx->d_span_target, nullptr, TR, K, scale, ctx->d_span_packed,
                                nullptr, nullptr, ctx->d_span_what, nullptr)) != EXL3_OK)

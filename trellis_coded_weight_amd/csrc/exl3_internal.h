@@ -151,20 +151,26 @@ hipError_t launch_traceback(int K, int pass, bool f16, const void *bp, int64_t n
                             float scale, uint16_t *packed, uint16_t *states, float *sse,
                             float *w_hat, hipStream_t stream);
 
+// inv: inverse of the within-tile order (element -> position), or null.
 hipError_t launch_ldlq_target(const float *w_tiles, const float *e_tiles, const float *L, int TR,
-                              int TC, int j, float *target, hipStream_t stream);
+                              int TC, int j, const uint8_t *inv, float *target,
+                              hipStream_t stream);
 
 hipError_t launch_ldlq_commit(const float *w_tiles, const float *what_span,
                               const uint16_t *packed_span, int TR, int TC, int j, int K,
                               uint16_t *packed, float *e_tiles, float *w_hat, float *tile_err,
                               hipStream_t stream);
 
+// order: the within-tile order (position -> element) of tile-major arrays, or
+// null for the natural order.
 hipError_t launch_regularize(const void *w, int w_dtype, int rows, int cols, int had_block,
                              const float *su, const float *sv, float *out, int layout,
-                             float *tile_sumsq, int *nonfinite, hipStream_t stream);
+                             float *tile_sumsq, int *nonfinite, const uint8_t *order,
+                             hipStream_t stream);
 
 hipError_t launch_unregularize(const float *in, int in_layout, int rows, int cols, int had_block,
-                               const float *su, const float *sv, float *out, hipStream_t stream);
+                               const float *su, const float *sv, float *out,
+                               const uint8_t *order, hipStream_t stream);
 
 hipError_t launch_channel_normalize(const void *w, int w_dtype, int rows, int cols,
                                     const float *su, double floor_value, float *w_norm,

@@ -5,7 +5,11 @@
 // corrected additively from the strictly lower blocks of L, the residual of
 // the spans already quantized fed back).
 //
-// The matrix lives tile-major ([TR*TC][256], tile tr*TC + tc, element 16r + c).
+// The matrix lives tile-major ([TR*TC][256], tile tr*TC + tc) in the
+// context's within-tile order: element 16r + c of a tile sits at position
+// inv[16r + c], inv being the inverse of the order (at 16r + c without one).
+// The target kernel works in element coordinates and reads and writes tiles
+// through inv; the commit kernel is position-wise and needs no table.
 // Span j is tile column j: the TR tiles (tr, j).  Its target is
 //     T_j = W_j + sum_{i > j} E_i L_ij,      E_i = W_i - What_i,
 // accumulated per element in the order i ascending, then t (row of the 16x16
@@ -31,13 +35,15 @@ constexpr int kLtPad = 20;            // row pitch of the transposed factor bloc
 // column L_ij[0..15][c].
 __global__ void __launch_bounds__(256)
 ldlq_target_kernel(const float *__restrict__ w_tiles, const float *__restrict__ e_tiles,
-                   const float *__restrict__ L, int TC, int j, float *__restrict__ target) {
+                   const float *__restrict__ L, int TC, int j, const uint8_t *__restrict__ inv,
+                   float *__restrict__ target) {
     __shared__ __attribute__((aligned(16))) float Es[2][kBlocksPerChunk][16][16];
     __shared__ __attribute__((aligned(16))) float Lt[2][kBlocksPerChunk][16][kLtPad];
     const int tr = blockIdx.x;
     const int e = threadIdx.x, r = e >> 4, c = e & 15;
+    const int pos = inv ? inv[e] : e;      // position of element (r, c) in a tile
     const size_t C = (size_t)TC * 16;
-    float acc = w_tiles[((size_t)tr * TC + j) * 256 + e];
+    float acc = w_tiles[((size_t)tr * TC + j) * 256 + pos];
     // take the load's wait here, once, not at acc's first use inside the loop
     // (where it would also wait for the next chunk's loads)
     asm volatile("" : "+v"(acc));
@@ -51,7 +57,7 @@ ldlq_target_kernel(const float *__restrict__ w_tiles, const float *__restrict__ 
         for (int q = 0; q < kBlocksPerChunk; ++q) {
             // past the last span: a valid address whose value is never summed
             const int i = (i0 + q) < TC ? (i0 + q) : (TC - 1);
-            pe[q] = e_tiles[((size_t)tr * TC + i) * 256 + e];          // E[16tr + r][16i + c]
+            pe[q] = e_tiles[((size_t)tr * TC + i) * 256 + pos];        // E[16tr + r][16i + c]
             pl[q] = L[(size_t)(16 * i + r) * C + 16 * (size_t)j + c];  // L_ij[r][c]
         }
     };
@@ -86,7 +92,7 @@ ldlq_target_kernel(const float *__restrict__ w_tiles, const float *__restrict__ 
         if (n + 1 < n_chunks) stage(buf ^ 1);
         __syncthreads();
     }
-    target[(size_t)tr * 256 + e] = acc;
+    target[(size_t)tr * 256 + pos] = acc;
 }
 
 // Commit span j: scatter the span's container words, keep its error for the
@@ -119,11 +125,12 @@ ldlq_commit_kernel(const float *__restrict__ w_tiles, const float *__restrict__ 
 }  // namespace
 
 hipError_t launch_ldlq_target(const float *w_tiles, const float *e_tiles, const float *L, int TR,
-                              int TC, int j, float *target, hipStream_t stream) {
+                              int TC, int j, const uint8_t *inv, float *target,
+                              hipStream_t stream) {
     if (TR <= 0) return hipSuccess;
     if (j < 0 || j >= TC) return hipErrorInvalidValue;
     hipLaunchKernelGGL(ldlq_target_kernel, dim3((unsigned)TR), dim3(256), 0, stream, w_tiles,
-                       e_tiles, L, TC, j, target);
+                       e_tiles, L, TC, j, inv, target);
     return hipGetLastError();
 }
 

@@ -16,6 +16,10 @@
 // the block is turned around in LDS, then lane j holds row j for the right
 // transform.  The output is written tile-major (or row-major) and each of the
 // block's (B/16)^2 tiles gets its sequential binary32 sum of squares.
+//
+// Tile-major position t of a tile holds the tile's element order[t]
+// (element 16 r + c), order being the context's within-tile order (the
+// README's tensor-core permutation slot, section 5); without one, element t.
 #include "exl3_internal.h"
 
 #include <math.h>
@@ -50,7 +54,8 @@ template <int B, typename Tin>
 __global__ void __launch_bounds__(B)
 regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__restrict__ su,
                   const float *__restrict__ sv, float *__restrict__ out, int layout,
-                  float *__restrict__ tile_sumsq, int *__restrict__ nonfinite) {
+                  float *__restrict__ tile_sumsq, int *__restrict__ nonfinite,
+                  const uint8_t *__restrict__ order) {
     __shared__ float blk[B][B + 1];
     const int j = threadIdx.x;
     const int br = blockIdx.y, bc = blockIdx.x;
@@ -85,7 +90,8 @@ regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__
         for (int idx = j; idx < B * B; idx += B) {
             int lt = idx >> 8, t = idx & 255;
             int tr = lt / TB, tc = lt % TB;
-            int rr = tr * 16 + (t >> 4), cc = tc * 16 + (t & 15);
+            int el = order ? order[t] : t;
+            int rr = tr * 16 + (el >> 4), cc = tc * 16 + (el & 15);
             size_t tau = (size_t)(r0 / 16 + tr) * TC + (c0 / 16 + tc);
             out[tau * 256 + t] = blk[rr][cc];
         }
@@ -99,7 +105,8 @@ regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__
         int tr = j / TB, tc = j % TB;
         float acc = 0.0f;
         for (int t = 0; t < 256; ++t) {
-            float val = blk[tr * 16 + (t >> 4)][tc * 16 + (t & 15)];
+            const int el = order ? order[t] : t;
+            float val = blk[tr * 16 + (el >> 4)][tc * 16 + (el & 15)];
             float sq = val * val;
             acc = acc + sq;
         }
@@ -116,7 +123,7 @@ template <int B>
 __global__ void __launch_bounds__(B)
 unregularize_kernel(const float *__restrict__ in, int rows, int cols, int in_layout,
                     const float *__restrict__ su, const float *__restrict__ sv,
-                    float *__restrict__ out) {
+                    float *__restrict__ out, const uint8_t *__restrict__ order) {
     __shared__ float blk[B][B + 1];
     const int j = threadIdx.x;
     const int r0 = blockIdx.y * B, c0 = blockIdx.x * B;
@@ -128,8 +135,9 @@ unregularize_kernel(const float *__restrict__ in, int rows, int cols, int in_lay
         size_t src;
         if (in_layout == 1) {
             const int lt = idx >> 8, t = idx & 255, tr = lt / TB, tc = lt % TB;
-            rr = tr * 16 + (t >> 4);
-            cc = tc * 16 + (t & 15);
+            const int el = order ? order[t] : t;
+            rr = tr * 16 + (el >> 4);
+            cc = tc * 16 + (el & 15);
             src = ((size_t)(r0 / 16 + tr) * TC + (c0 / 16 + tc)) * 256 + t;
         } else {
             rr = idx / B;
@@ -161,11 +169,11 @@ unregularize_kernel(const float *__restrict__ in, int rows, int cols, int in_lay
 template <int B, typename Tin>
 hipError_t launch_reg_t(const void *w, int rows, int cols, const float *su, const float *sv,
                         float *out, int layout, float *tile_sumsq, int *nonfinite,
-                        hipStream_t stream) {
+                        const uint8_t *order, hipStream_t stream) {
     dim3 grid(cols / B, rows / B);
     hipLaunchKernelGGL((regularize_kernel<B, Tin>), grid, dim3(B), 0, stream,
                        reinterpret_cast<const Tin *>(w), rows, cols, su, sv, out, layout,
-                       tile_sumsq, nonfinite);
+                       tile_sumsq, nonfinite, order);
     return hipGetLastError();
 }
 
@@ -173,33 +181,34 @@ hipError_t launch_reg_t(const void *w, int rows, int cols, const float *su, cons
 
 hipError_t launch_unregularize(const float *in, int in_layout, int rows, int cols, int had_block,
                                const float *su, const float *sv, float *out,
-                               hipStream_t stream) {
+                               const uint8_t *order, hipStream_t stream) {
     if (rows <= 0 || cols <= 0) return hipSuccess;
     if (had_block != 64 && had_block != 128) return hipErrorInvalidValue;
     dim3 grid(cols / had_block, rows / had_block);
     if (had_block == 64)
         hipLaunchKernelGGL(unregularize_kernel<64>, grid, dim3(64), 0, stream, in, rows, cols,
-                           in_layout, su, sv, out);
+                           in_layout, su, sv, out, order);
     else
         hipLaunchKernelGGL(unregularize_kernel<128>, grid, dim3(128), 0, stream, in, rows, cols,
-                           in_layout, su, sv, out);
+                           in_layout, su, sv, out, order);
     return hipGetLastError();
 }
 
 hipError_t launch_regularize(const void *w, int w_dtype, int rows, int cols, int had_block,
                              const float *su, const float *sv, float *out, int layout,
-                             float *tile_sumsq, int *nonfinite, hipStream_t stream) {
+                             float *tile_sumsq, int *nonfinite, const uint8_t *order,
+                             hipStream_t stream) {
     if (rows <= 0 || cols <= 0) return hipSuccess;
     if (had_block == 64)
         return w_dtype == 1 ? launch_reg_t<64, uint16_t>(w, rows, cols, su, sv, out, layout,
-                                                         tile_sumsq, nonfinite, stream)
+                                                         tile_sumsq, nonfinite, order, stream)
                             : launch_reg_t<64, float>(w, rows, cols, su, sv, out, layout,
-                                                      tile_sumsq, nonfinite, stream);
+                                                      tile_sumsq, nonfinite, order, stream);
     if (had_block == 128)
         return w_dtype == 1 ? launch_reg_t<128, uint16_t>(w, rows, cols, su, sv, out, layout,
-                                                          tile_sumsq, nonfinite, stream)
+                                                          tile_sumsq, nonfinite, order, stream)
                             : launch_reg_t<128, float>(w, rows, cols, su, sv, out, layout,
-                                                       tile_sumsq, nonfinite, stream);
+                                                       tile_sumsq, nonfinite, order, stream);
     return hipErrorInvalidValue;
 }
 
