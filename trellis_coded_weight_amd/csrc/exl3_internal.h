@@ -69,30 +69,32 @@ __host__ __device__ inline void bp_locate(uint32_t e, uint32_t &lane, uint32_t &
 // Binary16 mode of the forward kernel.  Costs, levels and inputs are IEEE
 // binary16; two tracked states share one 32-bit register (low and high half),
 // paired as outputs b and b + 1 of one butterfly, so a packed instruction
-// serves both.  Ownership (1024 lanes per tile, 64 states per lane):
+// serves both.  Ownership (1024 lanes and 64 states per lane at K = 1..3; 512
+// lanes and 128 states per lane at K = 4, so that two tiles share a compute
+// unit):
 //   K=1: lane g owns the butterflies m = 2g + j + 2048 i (i < 8, j < 2)
 //   K=2: lane g owns the butterflies m = 2g + j + 2048 i (i, j < 2)
 //   K=3: m = g
-//   K=4: m = g >> 2 and the outputs b = 4 (g & 3) + 0..3
+//   K=4: m = g >> 1 and the outputs b = 8 (g & 1) + 0..7
 // The lane's output pairs are numbered q in loop order (i, j, pair p).  Index
 // bit r of pair q, half h, comes out as a flag; the step word keeps flags in
 // byte-bit positions:
 //   K=1: bit 16 (q & 1) + 8h + (q >> 1)
 //   K=2: bit 8h + q (r=0), 16 + 8h + q (r=1)
 //   K=3: bit 8h + q (r=0), 16 + 8h + q (r=1), 8h + 16 (q & 1) + 4 + (q >> 1) (r=2)
-//   K=4: (word compacted to 16 bits) 8h + 2q (r=0), 8h + 4 + 2q (r=1),
-//        8h + 2q + 1 (r=2), 8h + 4 + 2q + 1 (r=3)
+//   K=4: 8h + 2q (r=0), 16 + 8h + 2q (r=1), 8h + 2q + 1 (r=2), 16 + 8h + 2q + 1 (r=3)
 template <int K>
 struct GeoH {
     static constexpr int Kr = 16 - K;
     static constexpr int T = 1 << Kr;
     static constexpr int NB = 1 << K;
     static constexpr int MBITS = 16 - 2 * K;
+    static constexpr int LANES = (K == 4) ? 512 : kLanes;     // lanes per tile
     static constexpr int NI = (K == 1) ? 8 : (K == 2) ? 2 : 1;  // butterfly groups per lane
     static constexpr int NJ = (K <= 2) ? 2 : 1;       // adjacent butterflies per group
-    static constexpr int NP = (K == 4) ? 2 : NB / 2;  // output pairs per butterfly and lane
-    using bp_t = typename std::conditional<(K == 4), uint16_t, uint32_t>::type;
-    static_assert(NI * NJ * NP * 2 * NB == 64, "every lane owns 64 states");
+    static constexpr int NP = (K == 4) ? 4 : NB / 2;  // output pairs per butterfly and lane
+    using bp_t = uint32_t;                            // one word per lane and step
+    static_assert(NI * NJ * NP * 2 * NB * LANES == 65536, "the lanes own every state");
 };
 
 // Lane and bit positions (index bit 0 first) of tracked state e's
@@ -117,12 +119,12 @@ __host__ __device__ inline void bp_locate_h(uint32_t e, uint32_t &lane, uint32_t
         bit[1 % K] = 16u + 8u * h + q;
         bit[2 % K] = 8u * h + 16u * (q & 1u) + 4u + (q >> 1);
     } else {
-        uint32_t m = e >> 4, b = e & 15u, bl = b & 3u, h = bl & 1u, q = bl >> 1;
-        lane = (m << 2) | (b >> 2);
+        uint32_t m = e >> 4, b = e & 15u, bl = b & 7u, h = bl & 1u, q = bl >> 1;
+        lane = (m << 1) | (b >> 3);
         bit[0] = 8u * h + 2u * q;
-        bit[1 % K] = 8u * h + 4u + 2u * q;
+        bit[1 % K] = 16u + 8u * h + 2u * q;
         bit[2 % K] = 8u * h + 2u * q + 1u;
-        bit[3 % K] = 8u * h + 4u + 2u * q + 1u;
+        bit[3 % K] = 16u + 8u * h + 2u * q + 1u;
     }
 }
 

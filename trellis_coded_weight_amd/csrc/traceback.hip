@@ -28,9 +28,12 @@ __device__ __forceinline__ uint32_t bp_read(const typename Geo<K>::bp_t *__restr
                                             int slot, uint32_t e) {
     uint32_t lane;
     if (H) {
+        // same bytes per step as the binary32 layout; the binary16 kernel
+        // writes one 32-bit word per lane (512 lanes at K = 4)
         uint32_t bit[K];
         bp_locate_h<K>(e, lane, bit);
-        const uint32_t w = bp_tile[(size_t)slot * kLanes + lane];
+        const uint32_t *bp32 = reinterpret_cast<const uint32_t *>(bp_tile);
+        const uint32_t w = bp32[(size_t)slot * GeoH<K>::LANES + lane];
         uint32_t k = 0;
 #pragma unroll
         for (int r = 0; r < K; ++r) k |= ((w >> bit[r]) & 1u) << r;

@@ -10,8 +10,9 @@
 // Levels are the raw binary16 code values (no scale in this mode).
 //
 // Same work split and two-pass schedule as the binary32 kernel (one 1024-lane
-// workgroup per tile, 64 states per lane with their levels in registers,
-// tracked minima double-buffered in LDS -- half the bytes), but the outputs b
+// workgroup per tile, 64 states per lane with their levels in registers --
+// at K = 4 512 lanes of 128 states, so that two tiles share a compute unit --
+// tracked minima double-buffered in LDS, half the bytes), but the outputs b
 // and b + 1 of a butterfly share one register, so each packed instruction
 // (v_pk_add_f16 with a negated operand, v_pk_fma_f16 with the predecessor
 // cost broadcast to both halves by op_sel, v_pk_min_f16 / v_pk_minimum3_f16)
@@ -190,13 +191,13 @@ __device__ __forceinline__ int read_index(int g, int i, int k) {
     if (K == 1) return (k << 14) | (2 * g + 2048 * i);
     if (K == 2) return (k << 12) | (2 * g + 2048 * i);
     if (K == 3) return (k << 10) | g;
-    return (k << 8) | (g >> 2);
+    return (k << 8) | (g >> 1);
 }
 template <int K>
 __device__ __forceinline__ int write_index(int g, int i) {
     if (K <= 2) return (2 * g + 2048 * i) << K;
     if (K == 3) return g << 3;
-    return 4 * g;
+    return 8 * g;
 }
 // State of (group i, butterfly j, branch k, pair p, half 0).
 template <int K>
@@ -210,8 +211,8 @@ __device__ __forceinline__ uint32_t state_of(int g, int i, int j, int k, int p) 
         m = g;
         b = 2 * p;
     } else {
-        m = g >> 2;
-        b = 4 * (g & 3) + 2 * p;
+        m = g >> 1;
+        b = 8 * (g & 1) + 2 * p;
     }
     return ((uint32_t)k << G::Kr) | (m << K) | b;
 }
@@ -287,21 +288,22 @@ __device__ __forceinline__ uint32_t step_h(
         else
             *reinterpret_cast<uint2 *>(dst) = make_uint2(out[0], out[1]);
     }
-    if (K == 4) acc = (acc & 0x0F0Fu) | ((acc >> 12) & 0xF0F0u);
     return acc;
 }
 
-// At K = 2 and 3 the kernel fits in 64 registers per lane (8 waves per SIMD),
-// so two tiles' workgroups share a compute unit and one computes while the
-// other waits at its step barrier; K = 4 needs more registers, and K = 1's
-// tracked minima (2 x 64 KiB) leave LDS for one workgroup.
+// Two tiles' workgroups share a compute unit, so one computes while the
+// other waits at its step barrier: at K = 2 and 3 the kernel fits in 64
+// registers per lane (two 1024-lane workgroups, 8 waves per SIMD); at K = 4 a
+// tile has 512 lanes of 128 states in up to 128 registers (two workgroups, 4
+// waves per SIMD).  K = 1's tracked minima (2 x 64 KiB) leave LDS for one
+// workgroup.
 template <int K>
 struct WavesPerSimd {
-    static constexpr int v = (K == 2 || K == 3) ? 8 : 1;
+    static constexpr int v = (K == 2 || K == 3) ? 8 : (K == 4) ? 4 : 1;
 };
 
 template <int K, int PASS>
-__global__ void __launch_bounds__(kLanes, WavesPerSimd<K>::v)
+__global__ void __launch_bounds__(GeoH<K>::LANES, WavesPerSimd<K>::v)
 viterbi_fwd_f16_kernel(const uint16_t *__restrict__ x, int64_t tile0,
                        const uint16_t *__restrict__ levels, const uint16_t *__restrict__ X_in,
                        typename GeoH<K>::bp_t *__restrict__ bp, uint16_t *__restrict__ end_state,
@@ -310,7 +312,7 @@ viterbi_fwd_f16_kernel(const uint16_t *__restrict__ x, int64_t tile0,
     using bp_t = typename G::bp_t;
     __shared__ __attribute__((aligned(16))) uint16_t Mbuf[2][G::T];
     __shared__ uint32_t xs[kSteps];
-    __shared__ uint32_t red[kLanes / 64];
+    __shared__ uint32_t red[G::LANES / 64];
 
     const int g = threadIdx.x;
     const int64_t b = blockIdx.x;
@@ -336,11 +338,11 @@ viterbi_fwd_f16_kernel(const uint16_t *__restrict__ x, int64_t tile0,
                     v[i][j][k][p] = as_h2(lv32[state_of<K>(g, i, j, k, p) >> 1]);
 
     const uint32_t xm = (PASS == 1) ? 0u : ((uint32_t)X_in[b] & (uint32_t)(G::T - 1));
-    for (int e = g; e < G::T; e += kLanes)
+    for (int e = g; e < G::T; e += G::LANES)
         Mbuf[0][e] = (PASS == 1 || (uint32_t)e == xm) ? (uint16_t)0 : (uint16_t)0x7C00;
     __syncthreads();
 
-    bp_t *bp_tile = bp + (size_t)b * kSlots * kLanes;
+    bp_t *bp_tile = bp + (size_t)b * kSlots * G::LANES;
     constexpr int t_first = (PASS == 1) ? 127 : 0;
     uint16_t *const B0 = Mbuf[0];
     uint16_t *const B1 = Mbuf[1];
@@ -365,13 +367,13 @@ viterbi_fwd_f16_kernel(const uint16_t *__restrict__ x, int64_t tile0,
         for (; t < kSteps - 1; t += 2) {            // steps 127..254: B1 -> B0 -> B1
             const h2 xn = as_h2(xs[t + 1]);
             uint32_t w = step_h<K, true>(xt, B1, B0, v, g);
-            bp_tile[(size_t)(t - t_first) * kLanes + g] = (bp_t)w;
+            bp_tile[(size_t)(t - t_first) * G::LANES + g] = (bp_t)w;
             __syncthreads();
             xt = xn;
             if (t + 1 < kSteps - 1) {
                 xt = as_h2(xs[t + 2]);
                 w = step_h<K, true>(xn, B0, B1, v, g);
-                bp_tile[(size_t)(t + 1 - t_first) * kLanes + g] = (bp_t)w;
+                bp_tile[(size_t)(t + 1 - t_first) * G::LANES + g] = (bp_t)w;
                 __syncthreads();
             }
         }
@@ -379,13 +381,13 @@ viterbi_fwd_f16_kernel(const uint16_t *__restrict__ x, int64_t tile0,
         for (; t < kSteps - 1; t += 2) {            // steps 0..254: B0 -> B1 -> B0
             const h2 xn = as_h2(xs[t + 1]);
             uint32_t w = step_h<K, true>(xt, B0, B1, v, g);
-            bp_tile[(size_t)t * kLanes + g] = (bp_t)w;
+            bp_tile[(size_t)t * G::LANES + g] = (bp_t)w;
             __syncthreads();
             xt = xn;
             if (t + 1 < kSteps - 1) {
                 xt = as_h2(xs[t + 2]);
                 w = step_h<K, true>(xn, B1, B0, v, g);
-                bp_tile[(size_t)(t + 1) * kLanes + g] = (bp_t)w;
+                bp_tile[(size_t)(t + 1) * G::LANES + g] = (bp_t)w;
                 __syncthreads();
             }
         }
@@ -419,7 +421,7 @@ viterbi_fwd_f16_kernel(const uint16_t *__restrict__ x, int64_t tile0,
         __syncthreads();
         if (g == 0) {
             uint32_t r = red[0];
-            for (int w = 1; w < kLanes / 64; ++w) r = min(r, red[w]);
+            for (int w = 1; w < G::LANES / 64; ++w) r = min(r, red[w]);
             end_state[b] = (uint16_t)(r & 0xFFFFu);
         }
     } else {
@@ -449,7 +451,8 @@ hipError_t launch_t(const uint16_t *x, int64_t tile0, int64_t n, const uint16_t 
                     const uint16_t *X_in, void *bp, uint16_t *end_state, uint16_t *cost_out,
                     hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL((viterbi_fwd_f16_kernel<K, PASS>), dim3((unsigned)n), dim3(kLanes), 0,
+    hipLaunchKernelGGL((viterbi_fwd_f16_kernel<K, PASS>), dim3((unsigned)n),
+                       dim3(GeoH<K>::LANES), 0,
                        stream, x, tile0, levels, X_in,
                        reinterpret_cast<typename GeoH<K>::bp_t *>(bp), end_state, cost_out);
     return hipGetLastError();
