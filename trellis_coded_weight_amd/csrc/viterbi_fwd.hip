@@ -90,14 +90,6 @@ __device__ __forceinline__ void push_bits<1>(uint32_t &acc, const uint64_t (&kb)
     asm("v_addc_co_u32_e64 %0, %1, %0, %0, %2" : "+v"(acc), "=&s"(c0) : "s"(kb[0]));
 }
 template <>
-__device__ __forceinline__ void push_bits<3>(uint32_t &acc, const uint64_t (&kb)[3]) {
-    uint64_t c0, c1, c2;
-    asm("v_addc_co_u32_e64 %0, %1, %0, %0, %4\n\t"
-        "v_addc_co_u32_e64 %0, %2, %0, %0, %5\n\t"
-        "v_addc_co_u32_e64 %0, %3, %0, %0, %6"
-        : "+v"(acc), "=&s"(c0), "=&s"(c1), "=&s"(c2) : "s"(kb[0]), "s"(kb[1]), "s"(kb[2]));
-}
-template <>
 __device__ __forceinline__ void push_bits<4>(uint32_t &acc, const uint64_t (&kb)[4]) {
     uint64_t c0, c1, c2, c3;
     asm("v_addc_co_u32_e64 %0, %1, %0, %0, %5\n\t"
@@ -135,11 +127,11 @@ __device__ __forceinline__ void push_index(uint32_t &acc, uint32_t k) {
 // Minimum of the 2^K candidates and the lowest index reaching it, with the K
 // index bits appended to acc (high bit first).
 //
-// A tournament tree is built bottom-up but only the left child of every node
-// on a root-to-leaf path is ever needed: walking down from the root, the
-// minimum lies in the right subtree exactly when the left child's minimum is
-// larger than the overall minimum (equal values keep the left, i.e. lower,
-// index).  Each step of the walk is one compare, whose lane mask is both the
+// K = 1 and 4, the compare walk: a tournament tree is built bottom-up but only
+// the left child of every node on a root-to-leaf path is ever needed: walking
+// down from the root, the minimum lies in the right subtree exactly when the
+// left child's minimum is larger than the overall minimum (equal values keep
+// the left, i.e. lower, index).  Each step of the walk is one compare, whose lane mask is both the
 // next index bit (inserted with add-with-carry) and the selector that picks
 // the next left child.  No scalar instructions are involved.
 template <int K>
@@ -155,25 +147,20 @@ struct Acs<1> {
     }
 };
 
+// K = 3: the binary64 lexicographic tournament (seven v_min_f64 and one
+// insertion; as many issue slots as the compare walk but no lane-mask
+// latencies: 2 % faster measured).
 template <>
 struct Acs<3> {
     static __device__ __forceinline__ float run(const float (&a)[8], uint32_t &acc) {
-        const float m01 = __builtin_fminf(a[0], a[1]);
-        const float m45 = __builtin_fminf(a[4], a[5]);
-        const float m67 = __builtin_fminf(a[6], a[7]);
-        const float m0123 = __builtin_fminf(__builtin_fminf(m01, a[2]), a[3]);
-        const float m = __builtin_fminf(__builtin_fminf(m0123, m45), m67);
-        const bool r2 = m0123 > m;                    // index in 4..7
-        const float l1 = r2 ? m45 : m01;              // left pair of the chosen half
-        const bool r1 = l1 > m;
-        const float lo = r1 ? a[2] : a[0];
-        const float hi = r1 ? a[6] : a[4];
-        const float l0 = r2 ? hi : lo;                // left leaf of the chosen pair
-        const bool r0 = l0 > m;
-        const uint64_t kb[3] = {__builtin_amdgcn_ballot_w64(r2), __builtin_amdgcn_ballot_w64(r1),
-                                __builtin_amdgcn_ballot_w64(r0)};
-        push_bits<3>(acc, kb);
-        return m;
+        double c[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) c[k] = cost_index(a[k], (uint32_t)k);
+        const double t03 = lex_min(lex_min(c[0], c[1]), lex_min(c[2], c[3]));
+        const double t47 = lex_min(lex_min(c[4], c[5]), lex_min(c[6], c[7]));
+        const uint64_t w = __builtin_bit_cast(uint64_t, lex_min(t03, t47));
+        push_index<3>(acc, (uint32_t)w);
+        return __uint_as_float((uint32_t)(w >> 32));
     }
 };
 
