@@ -22,8 +22,8 @@
 // Backpointers (the winning k of every tracked state, K bits) are packed per
 // lane per step into one word: 32 bits at K=1 and 2, 24 at K=3 (uint32), 16
 // at K=4 (uint16).  The lane appends its tracked states in the order
-// n = i * BPL + bb, high bit first, so state n's k sits at bit
-// K * (GPL * BPL - 1 - n).
+// n = i * BPL + bb, high bit first (at K = 1 with i = 4..7 before 0..3), so
+// state n's k sits at bit K * (GPL * BPL - 1 - n).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -54,8 +54,10 @@ __host__ __device__ inline void bp_locate(uint32_t e, uint32_t &lane, uint32_t &
     if (K <= 2) {
         constexpr uint32_t bpl = 1u << K, n_e = 32u / K;
         uint32_t m = e >> K, bb = e & (bpl - 1u);
+        uint32_t i = m >> 10;
+        if (K == 1 && i < 8u) i ^= 4u;   // K = 1 runs butterflies 4..7 first
         lane = m & 1023u;
-        bit = K * (n_e - 1u - (bpl * (m >> 10) + bb));
+        bit = K * (n_e - 1u - (bpl * i + bb));
     } else if (K == 3) {
         lane = e >> 3;
         bit = 3u * (7u - (e & 7u));

@@ -210,6 +210,16 @@ __device__ __forceinline__ float min_only(const float (&a)[NB]) {
     return r;
 }
 
+// K = 1 keeps one copy of its 2^15 tracked minima (128 KiB) plus one spare
+// 32 KiB slot: quarter Q (entries 8192 Q ..) lives at its own offset, except
+// Q1, which moves between its own slot and the spare every step (steps of
+// parity 0 read it at 8192 and write it at 32768, parity 1 the reverse).  A
+// lane's butterflies 4..7 produce its part of the new Q1, so they run first,
+// before the barrier that lets the others overwrite Q0, Q2, Q3 in place, and
+// their work overlaps the step's reads.
+constexpr int k1_q1_slot(int par) { return par ? 32768 : 8192; }
+constexpr int k1_order(int ii) { return ii < 8 ? (ii ^ 4) : ii; }
+
 // One trellis step for the lane's 64 states: read the tracked minima of its
 // butterflies from Mc, write the new minima to Mn and return the backpointer
 // word (BITS) -- or only the minima (!BITS, steps whose backpointers are never
@@ -218,12 +228,15 @@ __device__ __forceinline__ float min_only(const float (&a)[NB]) {
 // issues the branch metrics of update e and the two pair minima of its
 // candidates, the final minimum (and the store of the new tracked minimum) of
 // update e-1, and the index insertion of update e-2.
-template <int K, bool BITS>
+template <int K, bool BITS, int PAR = 0>
 __device__ __forceinline__ uint32_t trellis_step(
     float xt, const float *__restrict__ Mc, float *__restrict__ Mn,
     const Levels<K> &lv, const int (&m)[Geo<K>::GPL], int b0) {
     using G = Geo<K>;
     float Mk[G::GPL][G::NB];
+    // K = 1: the LDS offsets of quarter Q1 read and written by a step of parity
+    // PAR (see k1_q1_slot)
+    [[maybe_unused]] constexpr int q1r = k1_q1_slot(PAR), q1w = k1_q1_slot(PAR ^ 1);
     // K = 1: the lane's 32 reads and 16 writes span 128 KiB, past the 16-bit
     // LDS immediates; with the lane's index opaque to the compiler they are
     // addressed from four base registers plus immediates, not one address
@@ -231,10 +244,12 @@ __device__ __forceinline__ uint32_t trellis_step(
     int lb = m[0];
     if constexpr (K == 1) asm volatile("" : "+v"(lb));
     if constexpr (K == 1) {
-        const float *r0 = Mc + lb, *r1 = Mc + (1 << G::MBITS) + lb;
+        // butterflies 4..7 (which write Q1 into the free slot) first
+        const float *r0 = Mc + lb, *r0q = Mc + q1r + lb, *r1 = Mc + (1 << G::MBITS) + lb;
 #pragma unroll
-        for (int i = 0; i < G::GPL; ++i) {
-            Mk[i][0] = r0[kLanes * i];
+        for (int ii = 0; ii < G::GPL; ++ii) {
+            const int i = k1_order(ii);
+            Mk[i][0] = i < 8 ? r0[kLanes * i] : r0q[kLanes * (i - 8)];
             Mk[i][1] = r1[kLanes * i];
         }
     } else {
@@ -243,9 +258,6 @@ __device__ __forceinline__ uint32_t trellis_step(
 #pragma unroll
             for (int k = 0; k < G::NB; ++k) Mk[i][k] = Mc[(k << G::MBITS) | m[i]];
     }
-    // K = 1 keeps a single buffer of tracked minima (128 KiB): every lane has
-    // read its predecessors before any lane overwrites them
-    if constexpr (K == 1) __syncthreads();
     uint32_t bits = 0;
     if constexpr (BITS && K == 2) {
         constexpr int NE = G::GPL * G::BPL;
@@ -283,11 +295,16 @@ __device__ __forceinline__ uint32_t trellis_step(
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < G::GPL; ++i) {
+        for (int ii = 0; ii < G::GPL; ++ii) {
+            // K = 1: butterflies 4..7 write quarter Q1 into the free slot; the
+            // others overwrite their quarters in place, once every lane has
+            // read its predecessors (the barrier after the first four)
+            const int i = K == 1 ? k1_order(ii) : ii;
+            if (K == 1 && ii == 4) __syncthreads();
             float outv[G::BPL];
 #pragma unroll
             for (int bb = 0; bb < G::BPL; ++bb) {
-                step_priority(i * G::BPL + bb, G::GPL * G::BPL);
+                step_priority(ii * G::BPL + bb, G::GPL * G::BPL);
                 float a[G::NB];
 #pragma unroll
                 for (int k = 0; k < G::NB; ++k) {
@@ -298,9 +315,12 @@ __device__ __forceinline__ uint32_t trellis_step(
                 if constexpr (BITS) outv[bb] = Acs<K>::run(a, bits);
                 else outv[bb] = min_only<G::NB>(a);
             }
-            float *dst = K == 1 ? Mn + 2 * lb + (i < G::GPL / 2 ? 0 : (1 << (G::Kr - 1))) +
-                                      2 * kLanes * (i % (G::GPL / 2))
-                                : Mn + ((m[i] << K) | b0);
+            // K = 1 outputs 2m, 2m + 1 of butterfly m = lb + 1024 i: quarter i / 4
+            float *dst = Mn + ((m[i] << K) | b0);
+            if constexpr (K == 1)
+                dst = i < 4   ? Mn + 2 * lb + 2 * kLanes * i
+                      : i < 8 ? Mn + q1w + 2 * lb + 2 * kLanes * (i - 4)
+                              : Mn + (1 << (G::Kr - 1)) + 2 * lb + 2 * kLanes * (i - 8);
             if constexpr (G::BPL == 2) {
                 *reinterpret_cast<float2 *>(dst) = make_float2(outv[0], outv[1]);
             } else {
@@ -322,18 +342,41 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
                    uint16_t *__restrict__ end_state, float *__restrict__ cost_out) {
     using G = Geo<K>;
     using bp_t = typename G::bp_t;
-    constexpr int NBUF = (K == 1) ? 1 : 2;          // K = 1: one 128 KiB buffer
-    __shared__ float Mbuf[NBUF][G::T];
-    __shared__ float xs[kSteps];
-    __shared__ float red_cost[kLanes / 64];
-    __shared__ uint32_t red_state[kLanes / 64];
+    constexpr int NBUF = (K == 1) ? 1 : 2;          // K = 1: one 128 KiB copy + a spare
+    // K = 1 takes the whole 160 KiB of LDS: its inputs are read from global
+    // memory each step and the end-of-pass reduction uses the Q1 slot that
+    // the last step does not read
+    float *Mb, *xs, *red_cost;
+    uint32_t *red_state;
+    if constexpr (K == 1) {
+        __shared__ float smem1[5 * 8192];
+        Mb = smem1;
+        xs = nullptr;
+        red_cost = smem1 + k1_q1_slot(0);
+        red_state = reinterpret_cast<uint32_t *>(smem1 + k1_q1_slot(0) + kLanes / 64);
+    } else {
+        __shared__ float Mbuf[NBUF * G::T];
+        __shared__ float xs_s[kSteps];
+        __shared__ float red_cost_s[kLanes / 64];
+        __shared__ uint32_t red_state_s[kLanes / 64];
+        Mb = Mbuf;
+        xs = xs_s;
+        red_cost = red_cost_s;
+        red_state = red_state_s;
+    }
 
     const int g = threadIdx.x;
     const int64_t b = blockIdx.x;
     const int64_t tile = tile_idx ? (int64_t)tile_idx[b] : tile0 + b;
 
     // step t reads the input at position (t + 128) mod 256 in pass 1 (rotated)
-    if (g < kSteps) xs[g] = x[tile * kSteps + ((PASS == 1) ? ((g + 128) & 255) : g)];
+    const float *x_tile = x + tile * kSteps;
+    auto xin = [&](int t) -> float {
+        if constexpr (K == 1) return x_tile[(PASS == 1) ? ((t + 128) & 255) : t];
+        else return xs[t];
+    };
+    if constexpr (K != 1)
+        if (g < kSteps) xs[g] = x_tile[(PASS == 1) ? ((g + 128) & 255) : g];
 
     int m[G::GPL];
     int b0;
@@ -353,7 +396,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
 
     const uint32_t xm = (PASS == 1) ? 0u : ((uint32_t)X_in[b] & (uint32_t)(G::T - 1));
     for (int e = g; e < G::T; e += kLanes)
-        Mbuf[0][e] = (PASS == 1 || (uint32_t)e == xm) ? 0.0f : INFINITY;
+        Mb[e] = (PASS == 1 || (uint32_t)e == xm) ? 0.0f : INFINITY;
     __syncthreads();
 
     bp_t *bp_tile = bp + (size_t)b * kSlots * kLanes;
@@ -368,61 +411,61 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
     // (ds_read2st64 / ds_write_b128), not one address register per access.
     int b1_off = (NBUF - 1) * G::T;
     if constexpr (NBUF == 2 && G::T * sizeof(float) >= 65536) asm volatile("" : "+v"(b1_off));
-    float *const B0 = Mbuf[0];
-    float *const B1 = &Mbuf[0][0] + b1_off;
-    float xt = xs[0];
+    float *const B0 = Mb;
+    float *const B1 = Mb + b1_off;
+    float xt = xin(0);
     int t = 0;
     if constexpr (PASS == 1) {
         for (; t + 1 < t_first; t += 2) {           // steps 0..125 in pairs
-            const float xn = xs[t + 1];
-            trellis_step<K, false>(xt, B0, B1, lv, m, b0);
+            const float xn = xin(t + 1);
+            trellis_step<K, false, 0>(xt, B0, B1, lv, m, b0);
             __syncthreads();
-            xt = xs[t + 2];
-            trellis_step<K, false>(xn, B1, B0, lv, m, b0);
+            xt = xin(t + 2);
+            trellis_step<K, false, 1>(xn, B1, B0, lv, m, b0);
             __syncthreads();
         }
         {                                           // step 126: B0 -> B1
-            const float xn = xs[t + 1];
-            trellis_step<K, false>(xt, B0, B1, lv, m, b0);
+            const float xn = xin(t + 1);
+            trellis_step<K, false, 0>(xt, B0, B1, lv, m, b0);
             __syncthreads();
             xt = xn;
             ++t;
         }
         for (; t < kSteps - 1; t += 2) {            // steps 127..254: B1 -> B0 -> B1
-            const float xn = xs[t + 1];
-            uint32_t w = trellis_step<K, true>(xt, B1, B0, lv, m, b0);
+            const float xn = xin(t + 1);
+            uint32_t w = trellis_step<K, true, 1>(xt, B1, B0, lv, m, b0);
             bp_tile[(size_t)(t - t_first) * kLanes + g] = (bp_t)w;
             __syncthreads();
             xt = xn;
             if (t + 1 < kSteps - 1) {
-                xt = xs[t + 2];
-                w = trellis_step<K, true>(xn, B0, B1, lv, m, b0);
+                xt = xin(t + 2);
+                w = trellis_step<K, true, 0>(xn, B0, B1, lv, m, b0);
                 bp_tile[(size_t)(t + 1 - t_first) * kLanes + g] = (bp_t)w;
                 __syncthreads();
             }
         }
     } else if constexpr (PASS == 3) {
         for (; t < kSteps - 1; t += 2) {            // steps 0..254, no backpointers
-            const float xn = xs[t + 1];
-            trellis_step<K, false>(xt, B0, B1, lv, m, b0);
+            const float xn = xin(t + 1);
+            trellis_step<K, false, 0>(xt, B0, B1, lv, m, b0);
             __syncthreads();
             xt = xn;
             if (t + 1 < kSteps - 1) {
-                xt = xs[t + 2];
-                trellis_step<K, false>(xn, B1, B0, lv, m, b0);
+                xt = xin(t + 2);
+                trellis_step<K, false, 1>(xn, B1, B0, lv, m, b0);
                 __syncthreads();
             }
         }
     } else {
         for (; t < kSteps - 1; t += 2) {            // steps 0..254: B0 -> B1 -> B0
-            const float xn = xs[t + 1];
-            uint32_t w = trellis_step<K, true>(xt, B0, B1, lv, m, b0);
+            const float xn = xin(t + 1);
+            uint32_t w = trellis_step<K, true, 0>(xt, B0, B1, lv, m, b0);
             bp_tile[(size_t)t * kLanes + g] = (bp_t)w;
             __syncthreads();
             xt = xn;
             if (t + 1 < kSteps - 1) {
-                xt = xs[t + 2];
-                w = trellis_step<K, true>(xn, B1, B0, lv, m, b0);
+                xt = xin(t + 2);
+                w = trellis_step<K, true, 1>(xn, B1, B0, lv, m, b0);
                 bp_tile[(size_t)(t + 1) * kLanes + g] = (bp_t)w;
                 __syncthreads();
             }
@@ -430,8 +473,16 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
     }
 
     // last step: costs of all states, no minimum over predecessors
-    xt = xs[kSteps - 1];
-    const float *Mc = Mbuf[((kSteps - 1) & 1) % NBUF];
+    xt = xin(kSteps - 1);
+    const float *Mc = ((kSteps - 1) & 1) && NBUF == 2 ? B1 : B0;
+    // tracked index e of the last step's predecessors -> its LDS word (K = 1:
+    // quarter Q1 sits in the slot of odd steps)
+    auto slot_of = [](uint32_t e) -> uint32_t {
+        if constexpr (K == 1)
+            return (e >> 13) == 1u ? (uint32_t)k1_q1_slot((kSteps - 1) & 1) + (e & 8191u) : e;
+        else
+            return e;
+    };
     if (PASS == 1) {
         float best = 0.0f;
         uint32_t best_s = 0xFFFFFFFFu;
@@ -439,7 +490,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
         for (int i = 0; i < G::GPL; ++i)
 #pragma unroll
             for (int k = 0; k < G::NB; ++k) {
-                float mk = Mc[(k << G::MBITS) | m[i]];
+                float mk = Mc[slot_of(((uint32_t)k << G::MBITS) | (uint32_t)m[i])];
 #pragma unroll
                 for (int bb = 0; bb < G::BPL; ++bb) {
                     float d = xt - lv.at(i, k, bb);
@@ -484,7 +535,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
         for (int i = 0; i < G::GPL; ++i)
 #pragma unroll
             for (int k = 0; k < G::NB; ++k) {
-                float mk = Mc[(k << G::MBITS) | m[i]];
+                float mk = Mc[slot_of(((uint32_t)k << G::MBITS) | (uint32_t)m[i])];
 #pragma unroll
                 for (int bb = 0; bb < G::BPL; ++bb) {
                     uint32_t s = ((uint32_t)k << G::Kr) | ((uint32_t)m[i] << K) | (uint32_t)(b0 + bb);
