@@ -154,6 +154,14 @@ def test_workload2_4096x4096_k2(ctx):
     assert lo <= math.sqrt(nmse) <= hi
 
 
+def test_workload2_at_k1(ctx):
+    """The 4096x4096 matrix at K = 1 (the benchmark's K = 1 figure), in its 8,192-tile
+    launches: sampled tiles bit-exact, the scale in the bracket, the MSE sum."""
+    m = workloads.config(2)[0]
+    got, rms = _check_matrix(ctx, m, 1, exact_gss=False)
+    assert 0.0 < got["mse"] / rms ** 2 < _lloyd(1)
+
+
 def test_workload3_heavy_tailed_k4(ctx):
     m = workloads.config(3)[0]
     got, rms = _check_matrix(ctx, m, 4, exact_gss=True)
