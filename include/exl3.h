@@ -230,6 +230,31 @@ int exl3_channel_normalize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, 
 int exl3_encode_tiles(exl3_ctx *ctx, const float *x, int64_t n, int K, float scale,
                       uint16_t *packed, uint16_t *states, float *tile_sse);
 
+/* Most tiles one exl3_encode_tiles_noalloc call takes (its static scratch). */
+enum { EXL3_NOALLOC_MAX_TILES = 256, EXL3_NOALLOC_MAX_TILES_K4 = 512 };
+
+/*
+ * exl3_encode_tiles without any device allocation, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, outputs and results, bit for bit, as
+ * exl3_encode_tiles; the chain's scratch (backpointers and per-tile
+ * bookkeeping) is a fixed array in the library's device code, 267,390,976 B
+ * (255 MiB) that every GPU the library is loaded on holds until the process
+ * ends, looked up once per device when a context is created there.
+ *   n <= EXL3_NOALLOC_MAX_TILES (K = 1, 2, 3) or EXL3_NOALLOC_MAX_TILES_K4
+ *   (K = 4) per call; larger n is rejected with EXL3_EINVAL before any launch
+ *   (encode the rest in further calls).
+ * The call enqueues four kernels on the context's stream and calls no
+ * hipMalloc / hipFree.  All calls on one GPU share that GPU's array, which
+ * keeps the last call's contents (nothing in it needs to start at zero):
+ * calls that overlap on one GPU -- on different streams or contexts, or from
+ * different threads -- race; order them on one stream.
+ * Errors: EXL3_EINVAL, EXL3_EUNSUPPORTED, EXL3_EHIP (also when the array's
+ * address could not be looked up for this device).
+ */
+int exl3_encode_tiles_noalloc(exl3_ctx *ctx, const float *x, int64_t n, int K, float scale,
+                              uint16_t *packed, uint16_t *states, float *tile_sse);
+
 /*
  * Encode n tiles in binary16 arithmetic [P1 sections 1 and 4: the half-precision
  * add-compare-select]: the same two-pass tail-biting search, with inputs, code

@@ -31,7 +31,8 @@ EXPORTED = [
     "exl3_ctx_set_stream", "exl3_set_codebook", "exl3_get_codebook", "exl3_set_codebook_kind",
     "exl3_set_tile_order",
     "exl3_regularize", "exl3_unregularize",
-    "exl3_channel_normalize", "exl3_encode_tiles", "exl3_encode_tiles_f16", "exl3_decode_tiles", "exl3_quantize_matrix",
+    "exl3_channel_normalize", "exl3_encode_tiles", "exl3_encode_tiles_noalloc",
+    "exl3_encode_tiles_f16", "exl3_decode_tiles", "exl3_quantize_matrix",
     "exl3_quantize_matrix_ldlq", "exl3_quantize_matrix_grid", "exl3_quantize_matrix_f16", "exl3_scratch_per_tile",
     "exl3_ctx_set_timing", "exl3_ctx_read_timing",
 ]
@@ -105,6 +106,8 @@ def load_library():
     lib.exl3_channel_normalize.argtypes = [vp, vp, i32, i32, i32, vp, f64, vp, vp, vp]
     lib.exl3_encode_tiles.restype = i32
     lib.exl3_encode_tiles.argtypes = [vp, vp, i64, i32, f32, vp, vp, vp]
+    lib.exl3_encode_tiles_noalloc.restype = i32
+    lib.exl3_encode_tiles_noalloc.argtypes = [vp, vp, i64, i32, f32, vp, vp, vp]
     lib.exl3_encode_tiles_f16.restype = i32
     lib.exl3_encode_tiles_f16.argtypes = [vp, vp, i64, i32, vp, vp, vp]
     lib.exl3_decode_tiles.restype = i32
@@ -316,6 +319,22 @@ class Context:
         self._check(self.lib.exl3_encode_tiles(self.handle, _ptr(x), n, K, float(scale),
                                                _ptr(packed), _ptr(states), _ptr(sse)))
         return packed, states, sse
+
+    def encode_tiles_noalloc(self, x: torch.Tensor, K: int, scale: float, packed: torch.Tensor,
+                             states: Optional[torch.Tensor] = None,
+                             sse: Optional[torch.Tensor] = None) -> None:
+        """encode_tiles into caller-allocated outputs through the entry point that
+        allocates no device memory (at most 256 tiles per call, 512 at K = 4)."""
+        n = x.shape[0]
+        _need(x, torch.float32, (n, 256), "x")
+        _need(packed, torch.int16, (n, 16 * K), "packed")
+        if states is not None:
+            _need(states, torch.int16, (n, 256), "states")
+        if sse is not None:
+            _need(sse, torch.float32, (n,), "sse")
+        self._sync_stream()
+        self._check(self.lib.exl3_encode_tiles_noalloc(self.handle, _ptr(x), n, K, float(scale),
+                                                       _ptr(packed), _ptr(states), _ptr(sse)))
 
     def encode_tiles_f16(self, x: torch.Tensor, K: int, want_states: bool = True,
                          want_cost: bool = True):

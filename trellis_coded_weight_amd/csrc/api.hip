@@ -18,9 +18,26 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <set>
 #include <string>
 #include <vector>
+
+// ---- Device scratch of exl3_encode_tiles_noalloc ----
+// One batch of the encode chain: the backpointers of up to 256 tiles (K = 1..3,
+// 1,044,480 B each) or 512 tiles (K = 4, 522,240 B each), then the pass-1 end
+// state (uint16), X (uint16) and pass-2 path cost (float) of up to 512 tiles.
+// Each GPU the library is loaded on holds its own copy until the process ends.
+// Host code never passes this name to a kernel: it is a host-side stand-in;
+// the device address comes from hipGetSymbolAddress, looked up once per device
+// when a context is created there (noalloc_setup below).
+constexpr size_t kNoAllocBpBytes =
+    (size_t)EXL3_NOALLOC_MAX_TILES * exl3::kSlots * exl3::kLanes * sizeof(uint32_t);
+static_assert((size_t)EXL3_NOALLOC_MAX_TILES_K4 * exl3::kSlots * exl3::kLanes * sizeof(uint16_t) ==
+                  kNoAllocBpBytes, "K = 4 batches fill the same backpointer bytes");
+constexpr size_t kNoAllocBookTiles = EXL3_NOALLOC_MAX_TILES_K4;
+constexpr size_t kNoAllocBytes = kNoAllocBpBytes + kNoAllocBookTiles * (2 + 2 + 4);
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
 
 struct exl3_ctx {
     int device = 0;
@@ -132,6 +149,45 @@ int ensure(exl3_ctx *ctx, T *&ptr, size_t &cap, size_t count) {
 int set_device(exl3_ctx *ctx) {
     EXL3_HIP(ctx, hipSetDevice(ctx->device));
     return EXL3_OK;
+}
+
+// Per-device address of `scratch` (null until looked up), and the error of a
+// failed lookup.
+std::mutex g_noalloc_mu;
+std::vector<void *> g_noalloc_ptr;
+std::vector<hipError_t> g_noalloc_err;
+
+// Once per device, with that device current: look up the device address of
+// the static scratch.  Runs at context creation (which may allocate host
+// memory for the table); a failure is kept and reported by the entry point.
+void noalloc_setup(int device) {
+    std::lock_guard<std::mutex> lk(g_noalloc_mu);
+    if ((size_t)device < g_noalloc_ptr.size() &&
+        (g_noalloc_ptr[(size_t)device] || g_noalloc_err[(size_t)device] != hipSuccess))
+        return;
+    if ((size_t)device >= g_noalloc_ptr.size()) {
+        g_noalloc_ptr.resize((size_t)device + 1, nullptr);
+        g_noalloc_err.resize((size_t)device + 1, hipSuccess);
+    }
+    void *p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+        (void)hipGetLastError();
+        g_noalloc_err[(size_t)device] = e != hipSuccess ? e : hipErrorInvalidSymbol;
+        return;
+    }
+    g_noalloc_ptr[(size_t)device] = p;
+}
+
+// The looked-up address for this device (no allocation, no HIP call).
+void *noalloc_ptr(int device, hipError_t *err) {
+    std::lock_guard<std::mutex> lk(g_noalloc_mu);
+    if ((size_t)device >= g_noalloc_ptr.size()) {
+        *err = hipErrorNotInitialized;
+        return nullptr;
+    }
+    *err = g_noalloc_err[(size_t)device];
+    return g_noalloc_ptr[(size_t)device];
 }
 
 bool k_supported(int K) { return K >= 1 && K <= 4; }
@@ -465,6 +521,7 @@ int exl3_ctx_create(exl3_ctx **out, int device, void *hip_stream, size_t scratch
     if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess &&
         n_cu > 0)
         ctx->n_cu = n_cu;
+    noalloc_setup(device);
     std::vector<uint16_t> lv(65536);
     exl3::build_mul1_levels(lv.data());
     if (hipMalloc((void **)&ctx->d_levels, 65536 * sizeof(uint16_t)) != hipSuccess ||
@@ -741,6 +798,52 @@ int exl3_encode_tiles(exl3_ctx *ctx, const float *x, int64_t n, int K, float sca
         return rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
     return encode_chain(ctx, x, nullptr, n, K, scale, packed, states, tile_sse, nullptr, nullptr);
+}
+
+int exl3_encode_tiles_noalloc(exl3_ctx *ctx, const float *x, int64_t n, int K, float scale,
+                              uint16_t *packed, uint16_t *states, float *tile_sse) {
+    if (!ctx) return EXL3_EINVAL;
+    if (!k_supported(K)) return fail(ctx, EXL3_EUNSUPPORTED, "K = %d (supported: 1, 2, 3, 4)", K);
+    if (n < 0) return fail(ctx, EXL3_EINVAL, "n = %lld", (long long)n);
+    const int64_t max_n = K == 4 ? EXL3_NOALLOC_MAX_TILES_K4 : EXL3_NOALLOC_MAX_TILES;
+    if (n > max_n)
+        return fail(ctx, EXL3_EINVAL,
+                    "n = %lld tiles exceeds the %lld the static scratch holds at K = %d "
+                    "(call again for the rest)", (long long)n, (long long)max_n, K);
+    if (n > 0 && (!x || !packed)) return fail(ctx, EXL3_EINVAL, "null input or output");
+    if (!std::isfinite(scale)) return fail(ctx, EXL3_EINVAL, "scale is not finite");
+    int rc;
+    const size_t nt = (size_t)n;
+    if ((rc = check_span(ctx, x, nt * 256 * sizeof(float), "x")) != EXL3_OK ||
+        (rc = check_span(ctx, packed, nt * 16 * K * sizeof(uint16_t), "packed")) != EXL3_OK ||
+        (rc = check_span(ctx, states, nt * 256 * sizeof(uint16_t), "states")) != EXL3_OK ||
+        (rc = check_span(ctx, tile_sse, nt * sizeof(float), "tile_sse")) != EXL3_OK)
+        return rc;
+    if (n == 0) return EXL3_OK;
+    if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    hipError_t e = hipSuccess;
+    char *base = static_cast<char *>(noalloc_ptr(ctx->device, &e));
+    if (!base)
+        return fail(ctx, EXL3_EHIP, "the static scratch of device %d is not available: %s",
+                    ctx->device, hipGetErrorString(e));
+    // layout: backpointers, then end states, X and path costs of the batch;
+    // every word the chain reads was written earlier in this call, so nothing
+    // needs clearing
+    void *bp = base;
+    uint16_t *d_end = reinterpret_cast<uint16_t *>(base + kNoAllocBpBytes);
+    uint16_t *d_X = d_end + kNoAllocBookTiles;
+    float *d_cost = reinterpret_cast<float *>(d_X + kNoAllocBookTiles);
+    hipStream_t s = ctx->stream;
+    EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 1, x, nullptr, 0, n, ctx->d_levels, scale, nullptr,
+                                           bp, d_end, nullptr, s));
+    EXL3_HIP(ctx, exl3::launch_traceback(K, 1, false, bp, n, d_end, d_X, nullptr, nullptr, 0,
+                                         nullptr, 0.0f, nullptr, nullptr, nullptr, nullptr, s));
+    EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 2, x, nullptr, 0, n, ctx->d_levels, scale, d_X, bp,
+                                           nullptr, d_cost, s));
+    EXL3_HIP(ctx, exl3::launch_traceback(K, 2, false, bp, n, d_X, nullptr, x, nullptr, 0,
+                                         ctx->d_levels, scale, packed, states, tile_sse, nullptr,
+                                         s));
+    return EXL3_OK;
 }
 
 int exl3_encode_tiles_f16(exl3_ctx *ctx, const uint16_t *x, int64_t n, int K, uint16_t *packed,
