@@ -220,6 +220,33 @@ __device__ __forceinline__ float min_only(const float (&a)[NB]) {
 constexpr int k1_q1_slot(int par) { return par ? 32768 : 8192; }
 constexpr int k1_order(int ii) { return ii < 8 ? (ii ^ 4) : ii; }
 
+// Pass 2 at K = 2 stores tracked minimum e at LDS word (e >> 2) + kSkew2 *
+// (e & 3): four planes by the low two bits, each 4096 words, 8 words apart.  A lane's four
+// new minima (m << 2) | b then go to words m + kSkew2 * b, consecutive across
+// the lanes of a wave for every b, so each one-word store hits 32 distinct
+// banks (in the natural order they are four words apart: an 8-way conflict on
+// the 32 banks); the reads of M[(k << 12) | m] land on words
+// (g >> 2) + kSkew2 * (g & 3) + 1024 k + 256 i, where the skew of 8 words per
+// plane spreads every 32 consecutive lanes over 32 banks as well.  Offsets stay
+// below 64 KiB, so both access kinds use one base register plus immediates.
+// Pass 1 and the cost-only pass keep the natural order: their steps without
+// backpointers store four adjacent minima with one ds_write_b128, and as
+// sixteen one-word stores those steps measured 1 % slower (A/B on one box),
+// while pass 2 gained 0.5 %: the conflicts are not what bounds the step.
+constexpr int kSkew2 = 4104;
+constexpr int kWords2 = 4096 + 3 * kSkew2;   // words per K = 2 buffer (24 unused)
+
+template <int K, int PASS>
+constexpr bool skewed() { return K == 2 && PASS == 2; }
+
+template <int K, bool SKEW>
+__device__ __forceinline__ uint32_t lds_word(uint32_t e) {
+    if constexpr (SKEW) return (e >> 2) + (uint32_t)kSkew2 * (e & 3u);
+    else return e;
+}
+template <int K, bool SKEW>
+constexpr int lds_words() { return SKEW ? kWords2 : Geo<K>::T; }
+
 // One trellis step for the lane's 64 states: read the tracked minima of its
 // butterflies from Mc, write the new minima to Mn and return the backpointer
 // word (BITS) -- or only the minima (!BITS, steps whose backpointers are never
@@ -228,7 +255,7 @@ constexpr int k1_order(int ii) { return ii < 8 ? (ii ^ 4) : ii; }
 // issues the branch metrics of update e and the two pair minima of its
 // candidates, the final minimum (and the store of the new tracked minimum) of
 // update e-1, and the index insertion of update e-2.
-template <int K, bool BITS, int PAR = 0>
+template <int K, bool BITS, int PAR, bool SKEW>
 __device__ __forceinline__ uint32_t trellis_step(
     float xt, const float *__restrict__ Mc, float *__restrict__ Mn,
     const Levels<K> &lv, const int (&m)[Geo<K>::GPL], int b0) {
@@ -252,6 +279,13 @@ __device__ __forceinline__ uint32_t trellis_step(
             Mk[i][0] = i < 8 ? r0[kLanes * i] : r0q[kLanes * (i - 8)];
             Mk[i][1] = r1[kLanes * i];
         }
+    } else if constexpr (SKEW) {
+        // M[(k << 12) | m[i]], m[i] = m[0] + 1024 i: one base plus immediates
+        const float *r = Mc + lds_word<2, true>((uint32_t)m[0]);
+#pragma unroll
+        for (int i = 0; i < G::GPL; ++i)
+#pragma unroll
+            for (int k = 0; k < G::NB; ++k) Mk[i][k] = r[1024 * k + 256 * i];
     } else {
 #pragma unroll
         for (int i = 0; i < G::GPL; ++i)
@@ -285,7 +319,7 @@ __device__ __forceinline__ uint32_t trellis_step(
                 kk[f & 1] = (uint32_t)w;
                 // one store per new minimum: the minima are the high halves
                 // of register pairs, so a four-wide store would need moves
-                __hip_atomic_store(Mn + ((m[i] << K) | (b0 + bb)),
+                __hip_atomic_store(Mn + lds_word<K, SKEW>((uint32_t)((m[i] << K) | (b0 + bb))),
                                    __uint_as_float((uint32_t)(w >> 32)), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
             }
@@ -321,7 +355,11 @@ __device__ __forceinline__ uint32_t trellis_step(
                 dst = i < 4   ? Mn + 2 * lb + 2 * kLanes * i
                       : i < 8 ? Mn + q1w + 2 * lb + 2 * kLanes * (i - 4)
                               : Mn + (1 << (G::Kr - 1)) + 2 * lb + 2 * kLanes * (i - 8);
-            if constexpr (G::BPL == 2) {
+            if constexpr (SKEW) {
+                // one word per new minimum into its plane (see kSkew2)
+#pragma unroll
+                for (int bb = 0; bb < G::BPL; ++bb) Mn[m[i] + kSkew2 * bb] = outv[bb];
+            } else if constexpr (G::BPL == 2) {
                 *reinterpret_cast<float2 *>(dst) = make_float2(outv[0], outv[1]);
             } else {
 #pragma unroll
@@ -342,6 +380,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
                    uint16_t *__restrict__ end_state, float *__restrict__ cost_out) {
     using G = Geo<K>;
     using bp_t = typename G::bp_t;
+    constexpr bool SKEW = skewed<K, PASS>();
     constexpr int NBUF = (K == 1) ? 1 : 2;          // K = 1: one 128 KiB copy + a spare
     // K = 1 takes the whole 160 KiB of LDS: its inputs are read from global
     // memory each step and the end-of-pass reduction uses the Q1 slot that
@@ -355,7 +394,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
         red_cost = smem1 + k1_q1_slot(0);
         red_state = reinterpret_cast<uint32_t *>(smem1 + k1_q1_slot(0) + kLanes / 64);
     } else {
-        __shared__ float Mbuf[NBUF * G::T];
+        __shared__ float Mbuf[NBUF * lds_words<K, SKEW>()];
         __shared__ float xs_s[kSteps];
         __shared__ float red_cost_s[kLanes / 64];
         __shared__ uint32_t red_state_s[kLanes / 64];
@@ -395,8 +434,10 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
             }
 
     const uint32_t xm = (PASS == 1) ? 0u : ((uint32_t)X_in[b] & (uint32_t)(G::T - 1));
-    for (int e = g; e < G::T; e += kLanes)
-        Mb[e] = (PASS == 1 || (uint32_t)e == xm) ? 0.0f : INFINITY;
+    // the first step's buffer, by LDS word (K = 2: unused padding words included)
+    const uint32_t xw = lds_word<K, SKEW>(xm);
+    for (int w = g; w < lds_words<K, SKEW>(); w += kLanes)
+        Mb[w] = (PASS == 1 || (uint32_t)w == xw) ? 0.0f : INFINITY;
     __syncthreads();
 
     bp_t *bp_tile = bp + (size_t)b * kSlots * kLanes;
@@ -409,8 +450,9 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
     // offsets of the LDS instructions; with its offset opaque to the compiler
     // both buffers are addressed as one base register plus immediates
     // (ds_read2st64 / ds_write_b128), not one address register per access.
-    int b1_off = (NBUF - 1) * G::T;
-    if constexpr (NBUF == 2 && G::T * sizeof(float) >= 65536) asm volatile("" : "+v"(b1_off));
+    int b1_off = (NBUF - 1) * lds_words<K, SKEW>();
+    if constexpr (NBUF == 2 && lds_words<K, SKEW>() * sizeof(float) >= 65536)
+        asm volatile("" : "+v"(b1_off));
     float *const B0 = Mb;
     float *const B1 = Mb + b1_off;
     float xt = xin(0);
@@ -418,28 +460,28 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
     if constexpr (PASS == 1) {
         for (; t + 1 < t_first; t += 2) {           // steps 0..125 in pairs
             const float xn = xin(t + 1);
-            trellis_step<K, false, 0>(xt, B0, B1, lv, m, b0);
+            trellis_step<K, false, 0, SKEW>(xt, B0, B1, lv, m, b0);
             __syncthreads();
             xt = xin(t + 2);
-            trellis_step<K, false, 1>(xn, B1, B0, lv, m, b0);
+            trellis_step<K, false, 1, SKEW>(xn, B1, B0, lv, m, b0);
             __syncthreads();
         }
         {                                           // step 126: B0 -> B1
             const float xn = xin(t + 1);
-            trellis_step<K, false, 0>(xt, B0, B1, lv, m, b0);
+            trellis_step<K, false, 0, SKEW>(xt, B0, B1, lv, m, b0);
             __syncthreads();
             xt = xn;
             ++t;
         }
         for (; t < kSteps - 1; t += 2) {            // steps 127..254: B1 -> B0 -> B1
             const float xn = xin(t + 1);
-            uint32_t w = trellis_step<K, true, 1>(xt, B1, B0, lv, m, b0);
+            uint32_t w = trellis_step<K, true, 1, SKEW>(xt, B1, B0, lv, m, b0);
             bp_tile[(size_t)(t - t_first) * kLanes + g] = (bp_t)w;
             __syncthreads();
             xt = xn;
             if (t + 1 < kSteps - 1) {
                 xt = xin(t + 2);
-                w = trellis_step<K, true, 0>(xn, B0, B1, lv, m, b0);
+                w = trellis_step<K, true, 0, SKEW>(xn, B0, B1, lv, m, b0);
                 bp_tile[(size_t)(t + 1 - t_first) * kLanes + g] = (bp_t)w;
                 __syncthreads();
             }
@@ -447,25 +489,25 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
     } else if constexpr (PASS == 3) {
         for (; t < kSteps - 1; t += 2) {            // steps 0..254, no backpointers
             const float xn = xin(t + 1);
-            trellis_step<K, false, 0>(xt, B0, B1, lv, m, b0);
+            trellis_step<K, false, 0, SKEW>(xt, B0, B1, lv, m, b0);
             __syncthreads();
             xt = xn;
             if (t + 1 < kSteps - 1) {
                 xt = xin(t + 2);
-                trellis_step<K, false, 1>(xn, B1, B0, lv, m, b0);
+                trellis_step<K, false, 1, SKEW>(xn, B1, B0, lv, m, b0);
                 __syncthreads();
             }
         }
     } else {
         for (; t < kSteps - 1; t += 2) {            // steps 0..254: B0 -> B1 -> B0
             const float xn = xin(t + 1);
-            uint32_t w = trellis_step<K, true, 0>(xt, B0, B1, lv, m, b0);
+            uint32_t w = trellis_step<K, true, 0, SKEW>(xt, B0, B1, lv, m, b0);
             bp_tile[(size_t)t * kLanes + g] = (bp_t)w;
             __syncthreads();
             xt = xn;
             if (t + 1 < kSteps - 1) {
                 xt = xin(t + 2);
-                w = trellis_step<K, true, 1>(xn, B1, B0, lv, m, b0);
+                w = trellis_step<K, true, 1, SKEW>(xn, B1, B0, lv, m, b0);
                 bp_tile[(size_t)(t + 1) * kLanes + g] = (bp_t)w;
                 __syncthreads();
             }
@@ -481,7 +523,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
         if constexpr (K == 1)
             return (e >> 13) == 1u ? (uint32_t)k1_q1_slot((kSteps - 1) & 1) + (e & 8191u) : e;
         else
-            return e;
+            return lds_word<K, SKEW>(e);
     };
     if (PASS == 1) {
         float best = 0.0f;
