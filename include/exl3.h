@@ -137,7 +137,8 @@ int exl3_set_tile_order(exl3_ctx *ctx, const uint8_t *order_host);
  * pages print their counts of distinct levels, 913, 10,746 and 10,598] as the
  * level table of later calls (binary32 and binary16 modes, encode and decode).
  *   EXL3_CB_MUL1   the default table (see exl3_set_codebook)
- *   EXL3_CB_MCG    w = 0xCBAC1FED * s mod 2^32
+ *   EXL3_CB_MCG    w = 0x9E378FED * s mod 2^32 (the first odd multiplier from
+ *                  0x9E3779B1 up whose table has the printed 10,746 levels)
  *   EXL3_CB_3INST  w = 89226354 * s + 64248484 mod 2^32 (the QTIP three-
  *                  instruction decoder)
  * For mcg and 3INST, w = (w & 0x8FFF8FFF) ^ 0x3B603B60 and the level is the

@@ -129,10 +129,13 @@ def mul1_levels_fp16() -> np.ndarray:
 # is a binary16 number of magnitude in [1/8, 2); the level is the binary16 sum
 # of the two halves.  3INST is the published three-instruction decoder of the
 # QTIP trellis codes (a 32-bit linear congruential step, the mask, the xor);
-# mcg replaces the congruential step by a multiplicative one, with the
-# multiplier chosen here (it reproduces the printed count).
+# mcg replaces the congruential step by a multiplicative one.  The pages give
+# no multiplier: this reading takes the first odd multiplier at or above the
+# golden-ratio constant 0x9E3779B1 (MUL1_MULTIPLIER) whose table has exactly
+# the printed 10,746 distinct levels (mcg_multiplier_scan repeats the search).
 INST3_A, INST3_B = 89226354, 64248484
-MCG_MULTIPLIER = 0xCBAC1FED
+MCG_SCAN_START = 0x9E3779B1
+MCG_MULTIPLIER = 0x9E378FED
 HALVES_MASK, HALVES_XOR = 0x8FFF8FFF, 0x3B603B60
 
 
@@ -146,6 +149,19 @@ def _halves_sum_fp16(words: np.ndarray) -> np.ndarray:
 def inst3_levels_fp16() -> np.ndarray:
     s = np.arange(1 << STATE_BITS, dtype=np.uint64)
     return _halves_sum_fp16((s * np.uint64(INST3_A) + np.uint64(INST3_B)) & np.uint64(0xFFFFFFFF))
+
+
+def mcg_multiplier_scan(target=10746, start=MCG_SCAN_START, limit=1 << 16):
+    """First odd multiplier a >= start (scanning a, a + 2, ...) whose halves
+    table has `target` distinct levels, and the number of odd values scanned."""
+    s = np.arange(1 << STATE_BITS, dtype=np.uint64)
+    a = start | 1
+    for i in range(limit):
+        words = (s * np.uint64(a)) & np.uint64(0xFFFFFFFF)
+        if len(np.unique(_halves_sum_fp16(words))) == target:
+            return a, i + 1
+        a += 2
+    raise ValueError("no multiplier within %d odd values" % limit)
 
 
 def mcg_levels_fp16() -> np.ndarray:

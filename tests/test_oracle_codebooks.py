@@ -44,8 +44,18 @@ def test_neighbouring_constructions_give_other_counts():
     lo = (m & np.uint64(0xFFFF)).astype(np.uint16).view(np.float16).astype(np.float32)
     hi = (m >> np.uint64(16)).astype(np.uint16).view(np.float16).astype(np.float32)
     assert len(np.unique(lo + hi)) != 10746
-    other = oracle.reference._halves_sum_fp16((s * np.uint64(0x83DCD12D)) & np.uint64(0xFFFFFFFF))
+    start = oracle.reference.MCG_SCAN_START
+    other = oracle.reference._halves_sum_fp16((s * np.uint64(start)) & np.uint64(0xFFFFFFFF))
     assert len(np.unique(other)) != 10746
+
+
+def test_mcg_multiplier_is_the_first_hit_of_the_scan():
+    # the pages print the count but no multiplier: the reading takes the first
+    # odd multiplier from the golden-ratio constant up that reproduces it
+    a, scanned = oracle.reference.mcg_multiplier_scan()
+    assert a == oracle.reference.MCG_MULTIPLIER == 0x9E378FED
+    assert scanned == 2847
+    assert oracle.reference.MCG_SCAN_START == oracle.MUL1_MULTIPLIER
 
 
 def _half_value(bits: int) -> Fraction:

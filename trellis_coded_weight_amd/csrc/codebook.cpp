@@ -71,7 +71,10 @@ void build_mul1_levels(uint16_t *out) {
 // levels, 10,746 and 10,598].  A state gives a 32-bit word: 3INST is the
 // published three-instruction decoder of the QTIP trellis codes (linear
 // congruential step w = a*s + b mod 2^32), mcg a multiplicative step
-// w = A*s mod 2^32 (A chosen here; it gives the printed count).  Then
+// w = A*s mod 2^32.  The pages give no multiplier; A = 0x9E378FED is the first
+// odd number at or above the golden-ratio constant 0x9E3779B1 (the mul1
+// reading's multiplier) whose table has exactly the printed 10,746 distinct
+// levels, the 2,847th odd number scanned.  Then
 // w = (w & 0x8FFF8FFF) ^ 0x3B603B60 leaves each 16-bit half a binary16 number
 // of magnitude [1/8, 2) (exponent field 12..15), and the level is the
 // binary16 round-to-nearest-even of the sum of the two halves (the binary64
@@ -79,7 +82,7 @@ void build_mul1_levels(uint16_t *out) {
 namespace {
 
 constexpr uint32_t kInst3A = 89226354u, kInst3B = 64248484u;
-constexpr uint32_t kMcgA = 0xCBAC1FEDu;
+constexpr uint32_t kMcgA = 0x9E378FEDu;
 
 double f16_bits_to_double(uint16_t h) {
     const int e = (h >> 10) & 0x1F;
