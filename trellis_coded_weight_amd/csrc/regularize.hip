@@ -11,11 +11,13 @@
 // levels h = 1, 2, ..., B/2 (pairs (p, p+h), p mod 2h < h, become (a+b, a-b)),
 // x rn(1/sqrt(B)), the same transform along rows, x rn(1/sqrt(B)).
 //
-// One workgroup of B lanes per B x B block (the blocks are independent).  Lane
-// j first holds column j of the block in registers for the left transform,
-// the block is turned around in LDS, then lane j holds row j for the right
-// transform.  The output is written tile-major (or row-major) and each of the
-// block's (B/16)^2 tiles gets its sequential binary32 sum of squares.
+// One workgroup of 2B lanes per B x B block (the blocks are independent):
+// coalesced 16-byte loads into LDS, then each column's left transform split
+// over a lane pair, the block turned around in LDS, each row's right transform
+// split the same way, and a tile-major stage in LDS from which each of the
+// block's (B/16)^2 tiles gets its sequential binary32 sum of squares and the
+// output is written (tile-major or row-major).  HBM-bound: 6 bytes per element
+// for bf16 input (2 in, 4 out).
 //
 // Tile-major position t of a tile holds the tile's element order[t]
 // (element 16 r + c), order being the context's within-tile order (the
@@ -50,67 +52,217 @@ __device__ __forceinline__ float norm_const() {
     return B == 64 ? 0.125f : __uint_as_float(0x3DB504F3u);   // rn(1/sqrt(128))
 }
 
-template <int B, typename Tin>
-__global__ void __launch_bounds__(B)
+// One workgroup of 2B lanes per B x B block.  Lane l works as half h = (l >> 5)
+// & 1 of index i = (l & 31) + 32 (l >> 6): in the left transform it holds rows
+// h B/2 .. h B/2 + B/2 - 1 of column i, in the right transform columns
+// h B/2 .. of row i.  The levels h < B/2 of a transform run in registers; the
+// last level pairs each value with the same position of the other half, held
+// by lane l ^ 32 of the same wave (exchanged with v_permlane32_swap, no LDS).
+//
+//   1. 16-byte loads of the block's rows (coalesced), signs applied, into LDS
+//      (blk_word);
+//   2. left transform along columns, x rn(1/sqrt(B)), back to LDS;
+//   3. right transform along rows, x rn(1/sqrt(B)) (row-major output written
+//      from registers);
+//   4. the block in trellis order into a tile-major LDS stage (tile stride
+//      274 words, 17 words per tile row: conflict-free stores);
+//   5. per-tile sequential sum of squares, one lane per tile;
+//   6. tile-major output from the stage, consecutive lanes on consecutive
+//      positions.
+constexpr int kStageRow = 17;       // LDS words per 16-element tile row in the stage
+constexpr int kStageTile = 274;     // LDS words per tile in the stage
+
+__device__ __forceinline__ int stage_word(int t) { return (t >> 4) * kStageRow + (t & 15); }
+
+
+// The last butterfly level, across the two halves of the wave: one
+// v_permlane32_swap of the value with itself leaves the top half's value
+// (lanes 0..31) in the first result and the bottom half's (lanes 32..63) in
+// the second, in every lane; the lower half keeps top + bottom, the upper half
+// top - bottom, as fma(+-1, bottom, top): the product is exact, so the single
+// rounding is that of the addition or subtraction.
+__device__ __forceinline__ float last_level(float own, float sgn) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(own), __float_as_uint(own),
+                                                    false, false);
+    return __builtin_fmaf(sgn, __uint_as_float(r[1]), __uint_as_float(r[0]));
+}
+
+// LDS word of block element (row, col): rows of B + 1 words, so that the
+// column-wise and the row-wise accesses of the transforms hit 32 distinct
+// banks per half-wave (the first phase's stores, 8 consecutive columns per
+// lane, conflict 4-way; a skew that removes that needs more LDS than two
+// workgroups per compute unit leave).
+template <int B>
+__device__ __forceinline__ int blk_word(int row, int col) { return row * (B + 1) + col; }
+template <int B>
+constexpr int blk_words() { return B * (B + 1); }
+
+template <typename Tin>
+__device__ __forceinline__ void unpack16(const uint4 &u, float (&v)[16 / sizeof(Tin)]);
+template <>
+__device__ __forceinline__ void unpack16<uint16_t>(const uint4 &u, float (&v)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        v[2 * k] = __uint_as_float(w[k] << 16);             // bf16 -> fp32 is exact
+        v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4 &u, float (&v)[4]) {
+    v[0] = __uint_as_float(u.x);
+    v[1] = __uint_as_float(u.y);
+    v[2] = __uint_as_float(u.z);
+    v[3] = __uint_as_float(u.w);
+}
+
+// VEC: the weights start on a 16-byte boundary (else one element per load).
+template <int B, typename Tin, bool VEC, bool ORDERED>
+__global__ void __launch_bounds__(2 * B)
 regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__restrict__ su,
                   const float *__restrict__ sv, float *__restrict__ out, int layout,
                   float *__restrict__ tile_sumsq, int *__restrict__ nonfinite,
                   const uint8_t *__restrict__ order) {
-    __shared__ float blk[B][B + 1];
-    const int j = threadIdx.x;
-    const int br = blockIdx.y, bc = blockIdx.x;
-    const int r0 = br * B, c0 = bc * B;
-    const float c = norm_const<B>();
-
-    float a[B];
-    bool bad = false;
-    const float svj = sv[c0 + j];
-#pragma unroll
-    for (int r = 0; r < B; ++r) {
-        float val = load_w(w, (size_t)(r0 + r) * cols + c0 + j);
-        bad |= !isfinite(val);
-        a[r] = (val * su[r0 + r]) * svj;
-    }
-    if (bad && nonfinite) *nonfinite = 1;
-
-    fwht_regs<B>(a);
-#pragma unroll
-    for (int r = 0; r < B; ++r) blk[r][j] = a[r] * c;
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < B; ++q) a[q] = blk[j][q];
-    fwht_regs<B>(a);
-#pragma unroll
-    for (int q = 0; q < B; ++q) blk[j][q] = a[q] * c;
-    __syncthreads();
-
-    const int TC = cols / 16;
+    constexpr int H = B / 2;          // values per lane in a transform
     constexpr int TB = B / 16;        // tiles per block side
-    if (layout == 1) {
-        for (int idx = j; idx < B * B; idx += B) {
-            int lt = idx >> 8, t = idx & 255;
-            int tr = lt / TB, tc = lt % TB;
-            int el = order ? order[t] : t;
-            int rr = tr * 16 + (el >> 4), cc = tc * 16 + (el & 15);
-            size_t tau = (size_t)(r0 / 16 + tr) * TC + (c0 / 16 + tc);
-            out[tau * 256 + t] = blk[rr][cc];
+    constexpr int kWords = blk_words<B>() > TB * TB * kStageTile ? blk_words<B>()
+                                                                  : TB * TB * kStageTile;
+    __shared__ float smem[kWords];
+    __shared__ float sgn[2 * B];      // the block's column signs, then its row signs
+    __shared__ uint8_t inv[256];      // element -> trellis position (ORDERED)
+    const int l = threadIdx.x;
+    const int r0 = blockIdx.y * B, c0 = blockIdx.x * B;
+    const int TC = cols / 16;
+    const float c = norm_const<B>();
+    const int idx = (l & 31) + 32 * (l >> 6), half = (l >> 5) & 1;
+    const float sgn_half = half ? -1.0f : 1.0f;
+
+    // 1. load, signs (exact), into LDS
+    bool bad = false;
+    if constexpr (VEC) {
+        constexpr int EPC = 16 / sizeof(Tin);       // elements per 16-byte load
+        constexpr int CPR = B / EPC;                // loads per block row
+        constexpr int NL = B * CPR / (2 * B);       // loads per lane
+        uint4 u[NL];
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int q = l + 2 * B * i, rr = q / CPR, cb = (q % CPR) * EPC;
+            u[i] = *reinterpret_cast<const uint4 *>(w + (size_t)(r0 + rr) * cols + c0 + cb);
+        }
+        sgn[l] = l < B ? sv[c0 + l] : su[r0 + l - B];
+        if constexpr (ORDERED)
+            for (int t = l; t < 256; t += 2 * B) inv[order[t]] = (uint8_t)t;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int q = l + 2 * B * i, rr = q / CPR, cb = (q % CPR) * EPC;
+            float v[EPC];
+            unpack16<Tin>(u[i], v);
+            const float sr = sgn[B + rr];
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+                bad |= !isfinite(v[e]);
+                smem[blk_word<B>(rr, cb + e)] = (v[e] * sr) * sgn[cb + e];
+            }
         }
     } else {
-        for (int idx = j; idx < B * B; idx += B) {
-            int rr = idx / B, cc = idx % B;
-            out[(size_t)(r0 + rr) * cols + c0 + cc] = blk[rr][cc];
+        if constexpr (ORDERED)
+            for (int t = l; t < 256; t += 2 * B) inv[order[t]] = (uint8_t)t;
+        for (int q = l; q < B * B; q += 2 * B) {
+            const int rr = q / B, cc = q % B;
+            const float v = load_w(w, (size_t)(r0 + rr) * cols + c0 + cc);
+            bad |= !isfinite(v);
+            smem[blk_word<B>(rr, cc)] = (v * su[r0 + rr]) * sv[c0 + cc];
         }
     }
-    if (tile_sumsq && j < TB * TB) {
-        int tr = j / TB, tc = j % TB;
-        float acc = 0.0f;
-        for (int t = 0; t < 256; ++t) {
-            const int el = order ? order[t] : t;
-            float val = blk[tr * 16 + (el >> 4)][tc * 16 + (el & 15)];
-            float sq = val * val;
-            acc = acc + sq;
+    if (bad && nonfinite) *nonfinite = 1;
+    __syncthreads();
+
+    // 2. left transform: column idx, rows half * H ..
+    float a[H];
+#pragma unroll
+    for (int r = 0; r < H; ++r) a[r] = smem[blk_word<B>(half * H + r, idx)];
+    fwht_regs<H>(a);
+#pragma unroll
+    for (int r = 0; r < H; ++r) a[r] = last_level(a[r], sgn_half);
+#pragma unroll
+    for (int r = 0; r < H; ++r) smem[blk_word<B>(half * H + r, idx)] = a[r] * c;
+    __syncthreads();
+
+    // 3. right transform: row idx, columns half * H ..
+#pragma unroll
+    for (int q = 0; q < H; ++q) a[q] = smem[blk_word<B>(idx, half * H + q)];
+    fwht_regs<H>(a);
+#pragma unroll
+    for (int q = 0; q < H; ++q) a[q] = last_level(a[q], sgn_half) * c;
+    if (layout != 1) {
+        float *dst = out + (size_t)(r0 + idx) * cols + c0 + half * H;
+#pragma unroll
+        for (int q = 0; q < H; q += 4)
+            *reinterpret_cast<float4 *>(dst + q) = make_float4(a[q], a[q + 1], a[q + 2], a[q + 3]);
+    }
+    if (layout != 1 && !tile_sumsq) return;
+    __syncthreads();                  // the block in LDS is read; the stage reuses it
+
+    // 4. trellis order into the tile-major stage
+    {
+        const int tr = idx >> 4, rin = idx & 15;
+#pragma unroll
+        for (int q = 0; q < H; ++q) {
+            const int cc = half * H + q;
+            const int el = 16 * rin + (cc & 15);
+            const int t = ORDERED ? inv[el] : el;
+            smem[(tr * TB + (cc >> 4)) * kStageTile + stage_word(t)] = a[q];
         }
-        tile_sumsq[(size_t)(r0 / 16 + tr) * TC + (c0 / 16 + tc)] = acc;
+    }
+    __syncthreads();
+
+    // 5. per-tile sequential binary32 sum of squares, trellis order: wave 0,
+    // one lane per tile (reads unrolled ahead of the dependent additions)
+    if (tile_sumsq && l < 64) {
+        if (l < TB * TB) {
+            const float *T = smem + l * kStageTile;
+            float acc = 0.0f;
+#pragma unroll 16
+            for (int t = 0; t < 256; ++t) {
+                const float v = T[stage_word(t)];
+                const float sq = v * v;
+                acc = acc + sq;
+            }
+            tile_sumsq[(size_t)(r0 / 16 + l / TB) * TC + (c0 / 16 + l % TB)] = acc;
+        }
+        return;
+    }
+
+    // 6. tile-major output (the other waves, or all of them without energies):
+    // four consecutive positions per lane and store, eight stores' reads issued
+    // ahead
+    if (layout == 1) {
+        const int first = tile_sumsq ? 64 : 0;
+        const int nl = 2 * B - first;
+        constexpr int kQuads = B * B / 4;
+        for (int g0 = l - first; g0 < kQuads; g0 += 8 * nl) {
+            float4 v[8];
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const int g = g0 + b * nl;
+                if (g < kQuads) {
+                    const float *T = smem + (g >> 6) * kStageTile;
+                    const int t = 4 * (g & 63);
+                    v[b] = make_float4(T[stage_word(t)], T[stage_word(t + 1)],
+                                       T[stage_word(t + 2)], T[stage_word(t + 3)]);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const int g = g0 + b * nl;
+                if (g < kQuads) {
+                    const int lt = g >> 6, t = 4 * (g & 63);
+                    const size_t tau = (size_t)(r0 / 16 + lt / TB) * TC + (c0 / 16 + lt % TB);
+                    *reinterpret_cast<float4 *>(out + tau * 256 + t) = v[b];
+                }
+            }
+        }
     }
 }
 
@@ -171,9 +323,16 @@ hipError_t launch_reg_t(const void *w, int rows, int cols, const float *su, cons
                         float *out, int layout, float *tile_sumsq, int *nonfinite,
                         const uint8_t *order, hipStream_t stream) {
     dim3 grid(cols / B, rows / B);
-    hipLaunchKernelGGL((regularize_kernel<B, Tin>), grid, dim3(B), 0, stream,
-                       reinterpret_cast<const Tin *>(w), rows, cols, su, sv, out, layout,
-                       tile_sumsq, nonfinite, order);
+    const Tin *wt = reinterpret_cast<const Tin *>(w);
+    const bool vec = reinterpret_cast<uintptr_t>(w) % 16 == 0;
+#define EXL3_REG_LAUNCH(V, O)                                                                \
+    hipLaunchKernelGGL((regularize_kernel<B, Tin, V, O>), grid, dim3(2 * B), 0, stream, wt,  \
+                       rows, cols, su, sv, out, layout, tile_sumsq, nonfinite, order)
+    if (vec && order) EXL3_REG_LAUNCH(true, true);
+    else if (vec) EXL3_REG_LAUNCH(true, false);
+    else if (order) EXL3_REG_LAUNCH(false, true);
+    else EXL3_REG_LAUNCH(false, false);
+#undef EXL3_REG_LAUNCH
     return hipGetLastError();
 }
 
