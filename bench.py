@@ -25,11 +25,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP32_TFLOPS = 157.3      # 256 CU x 2.4 GHz x 256 FP32 flop/clk (FMA = 2 flops)
-# One-operation (non-FMA) FP32 issue ceiling: each SIMD can issue two VALU
-# instructions per 4-cycle wave64 slot (measured on gfx950 with the
-# SQ_ACTIVE_INST_VALU2 counter and issue probes), i.e. 2 x 64 lanes / 4 cycles
-# per SIMD: 256 CU x 4 SIMD x 32 lane-ops/clk x 2.4 GHz.
-PEAK_ISSUE_TOPS = 78.6
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "viterbi_fwd_traffic.json")
 FWD_SOURCE = os.path.join(ROOT, "trellis_coded_weight_amd", "csrc", "viterbi_fwd.hip")
 METRIC = "encoded 16x16 tiles/sec at K=2/3/4 on 1 MI355X; % of FP32 VALU peak"
@@ -123,6 +118,40 @@ def summarize_traffic(fetch_csv, write_csv, copy_mib, out_path=TRAFFIC_FILE):
     return out
 
 
+def host_threads():
+    """Worker threads for the oracle: the host cores this process may run on,
+    capped by the per-GPU share the host states in OMP_NUM_THREADS (a GPU machine
+    here gives one GPU's jobs 16 cores, whatever nproc shows)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n)
+
+
+def cpu_model_name():
+    """The CPU model as lscpu prints it (else /proc/cpuinfo's first model name)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(m, K, scale, n_tiles, threads, sample_tiles):
     """Oracle on this host: full regularization and statistics, plus the final
     encode of `sample_tiles` tiles; extrapolated to the whole step."""
@@ -144,15 +173,6 @@ def cpu_baseline(m, K, scale, n_tiles, threads, sample_tiles):
     t2 = time.perf_counter()
     oracle.encode_tiles(tiles[idx[:n1]], K, np.float32(scale), levels, threads=1)
     per_tile_1 = (time.perf_counter() - t2) / n1
-    cpu_model = None
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu_model = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
     TR, TC = m.w.shape[0] // 16, m.w.shape[1] // 16
     encodes = n_tiles + (m.gss[0] + 2) * sample_size(TR, TC)
     total = t_reg + per_tile * encodes
@@ -168,7 +188,51 @@ def cpu_baseline(m, K, scale, n_tiles, threads, sample_tiles):
         "measured_s": round(t_reg + t_enc, 2),
         "tile_encodes_per_s": 1.0 / per_tile,
         "single_thread_tile_encodes_per_s": 1.0 / per_tile_1,
-        "cpu_model": cpu_model,
+        "single_thread_tiles_per_s": n_tiles / (t_reg + per_tile_1 * encodes),
+        "nproc": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+        "cpu_model": cpu_model_name(),
+    }
+
+
+def roofline_line(K, kern, encodes_per_s, steps):
+    """The roofline of the dominant kernel: viterbi_fwd_kernel<K, 2>, pass 2 of
+    the final encode (launches of 8,192 tiles), rated by its algorithmic
+    binary32 operations per tile pass over its measured launch durations.
+    Beside it: all forward launches on the library's stream, and the whole
+    step's algorithmic operations over the step time (whole_path_frac)."""
+    f1_ms, f1_n, f1_tiles = kern["fwd1"]
+    f2_ms, f2_n, f2_tiles = kern["fwd2"]
+    f3_ms, f3_n, f3_tiles = kern["fwd_cost"]
+    ops_unit = ops_per_pass(K, False)
+    achieved = f2_tiles * ops_unit / (f2_ms / 1000.0) / 1e12 if f2_ms > 0 else 0.0
+    all_ops = ((f1_tiles * ops_per_pass(K, True)) + (f2_tiles + f3_tiles) * ops_unit)
+    all_ms = f1_ms + f2_ms + f3_ms
+    traffic = None
+    per = load_traffic(K)
+    if per and "pass2" in per and f2_n:
+        traffic = ((per["pass2"]["fetch_bytes_per_tile"] + per["pass2"]["write_bytes_per_tile"])
+                   * f2_tiles / f2_n)
+    return {
+        "bound": "alu",
+        "achieved": round(achieved, 3),
+        "peak": PEAK_FP32_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+        "traffic": traffic,
+        "kernel": "viterbi_fwd_kernel<%d, 2>: forward pass 2 of the final encode" % K,
+        "ops_per_tile_pass": ops_unit,
+        "launches": f2_n,
+        "avg_launch_ms": round(f2_ms / max(f2_n, 1), 4),
+        "avg_tiles_per_launch": round(f2_tiles / max(f2_n, 1), 1),
+        "all_forward_frac": round(all_ops / (all_ms / 1000.0) / 1e12 / PEAK_FP32_TFLOPS, 4)
+                            if all_ms > 0 else None,
+        "whole_path_frac": round(encodes_per_s * ops_per_tile_encode(K) / 1e12
+                                 / PEAK_FP32_TFLOPS, 4),
+        "note": "achieved = ops_per_tile_pass x tiles of the pass-2 launches / the sum of their "
+                "durations (HIP events on the library's stream, in a second run of the same "
+                "steps; the timed steps ran without events); all_forward_frac covers every "
+                "forward launch on that stream (pass 1, pass 2, the probes' cost-only pass)",
     }
 
 
@@ -237,13 +301,14 @@ def ldlq_mode(ctx, m, w, su, sv, steps):
     dt = time.perf_counter() - t0
     f1 = ctx.read_timing("fwd1")
     f2 = ctx.read_timing("fwd2")
+    f3 = ctx.read_timing("fwd_cost")
     ctx.set_timing(False)
     tiles = (R // 16) * (C // 16)
     return {"workload": "the same 4096x4096 matrix, K=2, golden-section scale, LDLQ over 256 "
                         "spans with a synthetic block LDL factor (off-diagonal N(0, 1/4096))",
             "tiles_per_s": round(tiles * n / dt, 1), "ms_per_step": round(1000.0 * dt / n, 3),
             "mse": out["mse"], "scale": out["scale"],
-            "fwd_ms_per_step": round((f1[0] + f2[0]) / n, 3)}
+            "fwd_ms_per_step": round((f1[0] + f2[0] + f3[0]) / n, 3)}
 
 
 def grid_mode(ctx, w, su, sv, n_tiles, steps):
@@ -468,60 +533,31 @@ def main():
         del a, b
 
     out = run_steps(ctx, w, su, sv, K, m.gss, max(args.warmup, 0))
-    ctx.set_timing(True)
+    # the timed region: per-launch timing off
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     out = run_steps(ctx, w, su, sv, K, m.gss, args.steps)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-
-    kern = {k: ctx.read_timing(k) for k in ("fwd1", "fwd2", "tb1", "tb2", "regularize",
-                                             "fwd_side")}
-    ctx.set_timing(False)
     value = n_tiles * args.steps / dt
     ms_step = 1000.0 * dt / args.steps
     TR, TC = R // 16, C // 16
     gss_encodes = (m.gss[0] + 2) * sample_size(TR, TC)
     encodes_per_s = (n_tiles + gss_encodes) * args.steps / dt
 
-    # roofline of the forward kernel (both passes), from its own launch times
-    f1_ms, f1_n, f1_tiles = kern["fwd1"]
-    f2_ms, f2_n, f2_tiles = kern["fwd2"]
-    fwd_ops = f1_tiles * ops_per_pass(K, True) + f2_tiles * ops_per_pass(K, False)
-    fwd_s = (f1_ms + f2_ms) / 1000.0
-    achieved = fwd_ops / fwd_s / 1e12
-    traffic = None
-    per = load_traffic(K)
-    if per and all(p in per for p in ("pass1", "pass2", "pass3")):
-        def tb(p):
-            return per[p]["fetch_bytes_per_tile"] + per[p]["write_bytes_per_tile"]
-        # the pass-2 timing records include the scale-search probes' cost-only form
-        # (less the remainder tiles that ran on the second stream: half the side tiles)
-        probe_tiles = gss_encodes * args.steps - kern["fwd_side"][2] // 2
-        traffic = (tb("pass1") * f1_tiles + tb("pass2") * (f2_tiles - probe_tiles)
-                   + tb("pass3") * probe_tiles) / max(f1_n + f2_n, 1)
-    roofline = {
-        "bound": "alu",
-        "achieved": round(achieved, 3),
-        "peak": PEAK_FP32_TFLOPS,
-        "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
-        "traffic": traffic,
-        "kernel": "viterbi_fwd_kernel<K=2> (pass 1, pass 2, and pass 2's cost-only form in the "
-                  "scale-search probes)",
-        "launches": f1_n + f2_n,
-        "avg_launch_ms": round((f1_ms + f2_ms) / max(f1_n + f2_n, 1), 4),
-        "avg_tiles_per_launch": round((f1_tiles + f2_tiles) / max(f1_n + f2_n, 1), 1),
-        "peak_issue": PEAK_ISSUE_TOPS,
-        "frac_issue": round(achieved / PEAK_ISSUE_TOPS, 4),
-        "whole_path_frac": round(encodes_per_s * ops_per_tile_encode(K) / 1e12
-                                 / PEAK_FP32_TFLOPS, 4),
-        "side_launches": kern["fwd_side"][1],
-        "side_tiles": kern["fwd_side"][2],
-        "note": "achieved = algorithmic ops of the forward launches on the library's stream / "
-                "the sum of their durations; the scale-search probes' last partial round "
-                "(side_tiles tiles) runs on a second stream beside them and is not in it",
-    }
+    # the same steps again with every launch bracketed by HIP events on the
+    # stream it runs on: per-kernel durations for the roofline
+    ctx.set_timing(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    run_steps(ctx, w, su, sv, K, m.gss, args.steps)
+    torch.cuda.synchronize()
+    dt_timed = time.perf_counter() - t1
+    kern = {k: ctx.read_timing(k) for k in ("fwd1", "fwd2", "fwd_cost", "tb1", "tb2",
+                                             "regularize", "fwd_side")}
+    ctx.set_timing(False)
+    roofline = roofline_line(K, kern, encodes_per_s, args.steps)
+    roofline["instrumented_ms_per_step"] = round(1000.0 * dt_timed / args.steps, 3)
     stages = {k: {"ms": round(v[0] / args.steps, 3), "launches": v[1] // max(args.steps, 1)}
               for k, v in kern.items()}
 
@@ -544,7 +580,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline and rank == 0:
-        threads = max(1, min(os.cpu_count() or 1, 16))
+        threads = host_threads()
         cpu = cpu_baseline(m, K, out["scale"], n_tiles, threads, args.cpu_tiles)
 
     # ||W - W_hat||_F / ||W||_F: the error is measured in the regularized domain,

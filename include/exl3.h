@@ -387,14 +387,16 @@ int exl3_quantize_matrix_ldlq(exl3_ctx *ctx, const void *w, int w_dtype, int row
 /* Kernel kinds for exl3_ctx_read_timing. */
 enum {
     EXL3_KERNEL_FWD1 = 0,        /* forward pass 1 (rotated input, free start) */
-    EXL3_KERNEL_FWD2 = 1,        /* forward pass 2 (start pinned to X); in the
-                                    scale search, its cost-only form */
+    EXL3_KERNEL_FWD2 = 1,        /* forward pass 2 (start pinned to X) with
+                                    backpointers */
     EXL3_KERNEL_TB1 = 2,         /* traceback to X */
     EXL3_KERNEL_TB2 = 3,         /* traceback, packing, squared error */
     EXL3_KERNEL_REGULARIZE = 4,
-    EXL3_KERNEL_FWD_SIDE = 5     /* forward passes of a scale-search probe's last
+    EXL3_KERNEL_FWD_SIDE = 5,    /* forward passes of a scale-search probe's last
                                     partial round, run on a second stream beside
                                     the main part (their durations overlap) */
+    EXL3_KERNEL_FWD_COST = 6     /* pass 2's cost-only form (scale-search probes,
+                                    on the context's stream) */
 };
 
 /*

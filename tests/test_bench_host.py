@@ -90,3 +90,19 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_roofline_rates_pass_two_of_the_final_encode(tmp_path, monkeypatch):
+    # 8 pass-2 launches of 8,192 tiles in 80 ms: 8 x 8192 x ops / 0.08 s
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "none.json"))
+    kern = {"fwd1": (70.0, 22, 8 * 8192 + 14 * 256), "fwd2": (80.0, 8, 8 * 8192),
+            "fwd_cost": (5.0, 14, 14 * 256)}
+    r = bench.roofline_line(2, kern, 380000.0, 1)
+    ops = bench.ops_per_pass(2, False)
+    assert ops == 256 * 3 * 65536 + 255 * (65536 - 16384) == 62_865_408
+    assert r["achieved"] == round(8 * 8192 * ops / 0.08 / 1e12, 3)
+    assert r["frac"] == round(r["achieved"] / bench.PEAK_FP32_TFLOPS, 4)
+    assert r["avg_launch_ms"] == 10.0 and r["avg_tiles_per_launch"] == 8192.0
+    assert r["traffic"] is None and "peak_issue" not in r
+    whole = 380000.0 * bench.ops_per_tile_encode(2) / 1e12 / bench.PEAK_FP32_TFLOPS
+    assert r["whole_path_frac"] == round(whole, 4)

@@ -376,7 +376,7 @@ int probe_split(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, in
                                              nullptr, 0, nullptr, 0.0f, nullptr, nullptr,
                                              nullptr, nullptr, p.s));
         close_timed(ctx, id);
-        id = open_timed(ctx, p.s == ctx->stream ? EXL3_KERNEL_FWD2 : EXL3_KERNEL_FWD_SIDE,
+        id = open_timed(ctx, p.s == ctx->stream ? EXL3_KERNEL_FWD_COST : EXL3_KERNEL_FWD_SIDE,
                         p.count, p.s);
         EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 3, x, idx + p.first, 0, p.count, ctx->d_levels,
                                                scale, ctx->d_X + p.first,
@@ -415,7 +415,7 @@ int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, i
                                              nullptr, 0, nullptr, 0.0f, nullptr, nullptr,
                                              nullptr, nullptr, ctx->stream));
         close_timed(ctx, id);
-        id = open_timed(ctx, EXL3_KERNEL_FWD2, nb);
+        id = open_timed(ctx, cost_only ? EXL3_KERNEL_FWD_COST : EXL3_KERNEL_FWD2, nb);
         EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, cost_only ? 3 : 2, x, idx_b, i0, nb,
                                                ctx->d_levels, scale,
                                                ctx->d_X, ctx->d_bp, nullptr,
