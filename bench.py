@@ -132,24 +132,33 @@ def host_threads():
     return max(1, n)
 
 
-def cpu_model_name():
-    """The CPU model as lscpu prints it (else /proc/cpuinfo's first model name)."""
+LSCPU_FIELDS = ("Model name", "Vendor ID", "CPU family", "Model", "Stepping", "CPU max MHz",
+                "BIOS Model name", "Socket(s)", "Core(s) per socket", "Thread(s) per core")
+
+
+def cpu_description():
+    """The host CPU as lscpu describes it (model name plus the identifying
+    fields it prints; /proc/cpuinfo's model name if lscpu is missing)."""
     import subprocess
+    info = {}
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
         for line in out.splitlines():
-            if line.strip().startswith("Model name:"):
-                return line.split(":", 1)[1].strip()
+            k, _, v = line.partition(":")
+            if k.strip() in LSCPU_FIELDS and v.strip():
+                info[k.strip()] = v.strip()
     except (OSError, subprocess.SubprocessError):
         pass
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return None
+    if "Model name" not in info:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        info["Model name"] = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+    return info
 
 
 def cpu_baseline(m, K, scale, n_tiles, threads, sample_tiles):
@@ -191,7 +200,8 @@ def cpu_baseline(m, K, scale, n_tiles, threads, sample_tiles):
         "single_thread_tiles_per_s": n_tiles / (t_reg + per_tile_1 * encodes),
         "nproc": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
-        "cpu_model": cpu_model_name(),
+        "cpu_model": cpu_description().get("Model name"),
+        "lscpu": cpu_description(),
     }
 
 

@@ -81,7 +81,9 @@ const char *exl3_version(void);
  * Create a context on HIP device `device`.  `hip_stream` is a hipStream_t the
  * caller owns (NULL = the null stream); every call enqueues on it.
  * `scratch_bytes` bounds the backpointer scratch the context may allocate
- * (0 = a default of 8 GiB); batches are sized to fit it [P1 section 2].
+ * (0 = a default of 64 GiB, about a fifth of an MI355X's HBM: the final
+ * encode of a 4096 x 4096 matrix in one batch); batches are sized to fit it
+ * and the scratch grows only to what a call needs [P1 section 2].
  * The context uploads the mul1 level table (65,536 fp16 values, 128 KiB).
  * Errors: EXL3_EINVAL (out == NULL), EXL3_EHIP (device unusable).
  */

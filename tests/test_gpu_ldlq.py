@@ -4,9 +4,11 @@ Source: "EXL3 Intel Arc Quantizer" README, Core Implemented Architecture item 3.
 
 Small matrices: scale, container words, dequantized tiles and per-tile errors bit-exact
 against oracle.quantize_matrix_ldlq (synthetic factor from workloads.ldl_factor).
-Properties at any size: an identity factor reproduces exl3_quantize_matrix; the container
-decodes to the dequantized tiles; every sampled span is the tile encoder's output on its
-target recomputed on the host from the regularized matrix and the spans after it.
+At 4096^2: eight whole tile rows of the full run bit-exact against the oracle's LDLQ on
+those rows (rows are independent).  Properties at any size: an identity factor reproduces
+exl3_quantize_matrix; the container decodes to the dequantized tiles; every sampled span
+is the tile encoder's output on its target recomputed on the host from the regularized
+matrix and the spans after it.
 """
 import numpy as np
 import pytest
@@ -129,3 +131,39 @@ def test_ldlq_full_size_properties(ctx):
         p, _, _ = ctx.encode_tiles(tiles, K, float(scale), want_states=False, want_sse=False)
         span = _u16(got["packed"])[:, j, :]
         assert np.array_equal(_u16(p), span), j
+
+
+@pytest.mark.slow
+def test_ldlq_full_size_bands_match_oracle(ctx):
+    """At 4096^2, K = 2: rows of span j's target depend only on the same rows of
+    the spans after it, so the oracle's LDLQ on a band of whole tile rows (its
+    own regularization of the matrix, at the scale its own golden-section search
+    chose, read from the stored workload digests) must reproduce those rows of
+    the GPU's full run bit for bit: container words, dequantized tiles and
+    per-tile errors."""
+    import json
+    import os
+    K = 2
+    m = workloads.config(2)[0]
+    R, C = m.w.shape
+    TC = C // 16
+    digests = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                          "golden", "config_digests.json")))["runs"]
+    scale = np.uint32(int(digests["c2_c2_4096x4096_K2"]["scale_bits"], 16)).view(np.float32)
+    L, _ = workloads.ldl_factor(C, 2102)
+    w, su, sv = _dev(m)
+    print("\nldlq 4096x4096 K=2 against oracle bands", flush=True)
+    got = ctx.quantize_matrix_ldlq(w, K, su, sv, torch.from_numpy(L).to(DEV), gss=m.gss,
+                                   want_w_hat=True, want_tile_err=True)
+    torch.cuda.synchronize()
+    assert np.float32(got["scale"]) == scale
+    tile_rows = [0, 1, 2, 3, 152, 153, 154, 155]
+    rows = np.concatenate([np.arange(16 * t, 16 * t + 16) for t in tile_rows])
+    w_reg = oracle.regularize(m.w, m.su, m.sv, 128)
+    want = oracle.ldlq(w_reg[rows], L, K, scale)
+    packed = _u16(got["packed"]).reshape(R // 16, TC, 16 * K)[tile_rows].reshape(-1, 16 * K)
+    assert np.array_equal(packed, want["packed"])
+    wh = got["w_hat"].cpu().numpy().reshape(R // 16, TC, 256)[tile_rows].reshape(-1, 256)
+    assert np.array_equal(_bits(wh), _bits(oracle.to_tiles(want["what"])))
+    err = got["tile_err"].cpu().numpy().reshape(R // 16, TC)[tile_rows].reshape(-1)
+    assert np.array_equal(_bits(err), _bits(want["err"]))

@@ -124,3 +124,20 @@ def test_feedback_lowers_proxy_loss_on_correlated_hessian():
     with_fb = _proxy(W - out["what"], H)
     without = _proxy(W - what_ind, H)
     assert with_fb < 0.8 * without
+
+
+def test_rows_are_independent():
+    # the band property the full-size GPU check relies on: LDLQ on a subset of
+    # whole tile rows reproduces those rows of the full run, bit for bit
+    W = _w(96, 64, 31)
+    L, _ = workloads.ldl_factor(64, 32, off_std=1.5)
+    full = oracle.ldlq(W, L, 2, _scale(2))
+    tile_rows = [1, 4]
+    rows = np.concatenate([np.arange(16 * t, 16 * t + 16) for t in tile_rows])
+    band = oracle.ldlq(W[rows], L, 2, _scale(2))
+    TC = 64 // 16
+    pk = full["packed"].reshape(6, TC, -1)[tile_rows].reshape(-1, full["packed"].shape[1])
+    assert np.array_equal(band["packed"], pk)
+    assert np.array_equal(band["what"], full["what"][rows])
+    assert np.array_equal(band["err"].view(np.uint32),
+                          full["err"].reshape(6, TC)[tile_rows].reshape(-1).view(np.uint32))
