@@ -255,7 +255,17 @@ constexpr int lds_words() { return SKEW ? kWords2 : Geo<K>::T; }
 // issues the branch metrics of update e and the two pair minima of its
 // candidates, the final minimum (and the store of the new tracked minimum) of
 // update e-1, and the index insertion of update e-2.
-template <int K, bool BITS, int PAR, bool SKEW>
+// Passes 2 and 3 start with one tracked minimum finite (the one X admits), and
+// after t steps only 2^(K (t + 1)) of them are: until they fill the tracked set
+// most waves read nothing but +inf.  When every candidate of a wave is +inf,
+// every new minimum is +inf and the lowest index reaching it is 0 -- exactly
+// what the full step would compute -- so such a wave stores those and skips
+// the step (a wave-uniform test, SKIP steps only: the first 6 / 4 / 2 at
+// K = 2 / 3 / 4; at K = 1 none).
+template <int K>
+constexpr int skip_steps() { return K == 2 ? 6 : K == 3 ? 4 : K == 4 ? 2 : 0; }
+
+template <int K, bool BITS, int PAR, bool SKEW, bool SKIP = false>
 __device__ __forceinline__ uint32_t trellis_step(
     float xt, const float *__restrict__ Mc, float *__restrict__ Mn,
     const Levels<K> &lv, const int (&m)[Geo<K>::GPL], int b0) {
@@ -291,6 +301,22 @@ __device__ __forceinline__ uint32_t trellis_step(
         for (int i = 0; i < G::GPL; ++i)
 #pragma unroll
             for (int k = 0; k < G::NB; ++k) Mk[i][k] = Mc[(k << G::MBITS) | m[i]];
+    }
+    if constexpr (SKIP) {
+        static_assert(K != 1, "K = 1 steps hold a barrier");
+        bool finite = false;
+#pragma unroll
+        for (int i = 0; i < G::GPL; ++i)
+#pragma unroll
+            for (int k = 0; k < G::NB; ++k) finite = finite || Mk[i][k] != INFINITY;
+        if (__builtin_amdgcn_ballot_w64(finite) == 0) {
+#pragma unroll
+            for (int i = 0; i < G::GPL; ++i)
+#pragma unroll
+                for (int bb = 0; bb < G::BPL; ++bb)
+                    Mn[lds_word<K, SKEW>((uint32_t)((m[i] << K) | (b0 + bb)))] = INFINITY;
+            return 0u;
+        }
     }
     uint32_t bits = 0;
     if constexpr (BITS && K == 2) {
@@ -487,6 +513,15 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
             }
         }
     } else if constexpr (PASS == 3) {
+        if constexpr (skip_steps<K>() > 0)
+            for (; t < skip_steps<K>(); t += 2) {   // the first steps, unreachable waves skip
+                const float xn = xin(t + 1);
+                trellis_step<K, false, 0, SKEW, true>(xt, B0, B1, lv, m, b0);
+                __syncthreads();
+                xt = xin(t + 2);
+                trellis_step<K, false, 1, SKEW, true>(xn, B1, B0, lv, m, b0);
+                __syncthreads();
+            }
         for (; t < kSteps - 1; t += 2) {            // steps 0..254, no backpointers
             const float xn = xin(t + 1);
             trellis_step<K, false, 0, SKEW>(xt, B0, B1, lv, m, b0);
@@ -499,6 +534,17 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
             }
         }
     } else {
+        if constexpr (skip_steps<K>() > 0)
+            for (; t < skip_steps<K>(); t += 2) {   // the first steps, unreachable waves skip
+                const float xn = xin(t + 1);
+                uint32_t w = trellis_step<K, true, 0, SKEW, true>(xt, B0, B1, lv, m, b0);
+                bp_tile[(size_t)t * kLanes + g] = (bp_t)w;
+                __syncthreads();
+                xt = xin(t + 2);
+                w = trellis_step<K, true, 1, SKEW, true>(xn, B1, B0, lv, m, b0);
+                bp_tile[(size_t)(t + 1) * kLanes + g] = (bp_t)w;
+                __syncthreads();
+            }
         for (; t < kSteps - 1; t += 2) {            // steps 0..254: B0 -> B1 -> B0
             const float xn = xin(t + 1);
             uint32_t w = trellis_step<K, true, 0, SKEW>(xt, B0, B1, lv, m, b0);
