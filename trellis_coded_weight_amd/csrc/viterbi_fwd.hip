@@ -310,11 +310,22 @@ __device__ __forceinline__ uint32_t trellis_step(
 #pragma unroll
             for (int k = 0; k < G::NB; ++k) finite = finite || Mk[i][k] != INFINITY;
         if (__builtin_amdgcn_ballot_w64(finite) == 0) {
+            // the same stores as the full step's (see its end)
 #pragma unroll
-            for (int i = 0; i < G::GPL; ++i)
+            for (int i = 0; i < G::GPL; ++i) {
+                float *dst = Mn + ((m[i] << K) | b0);
+                if constexpr (SKEW) {
 #pragma unroll
-                for (int bb = 0; bb < G::BPL; ++bb)
-                    Mn[lds_word<K, SKEW>((uint32_t)((m[i] << K) | (b0 + bb)))] = INFINITY;
+                    for (int bb = 0; bb < G::BPL; ++bb) Mn[m[i] + kSkew2 * bb] = INFINITY;
+                } else if constexpr (G::BPL == 2) {
+                    *reinterpret_cast<float2 *>(dst) = make_float2(INFINITY, INFINITY);
+                } else {
+#pragma unroll
+                    for (int q4 = 0; q4 < G::BPL; q4 += 4)
+                        *reinterpret_cast<float4 *>(dst + q4) =
+                            make_float4(INFINITY, INFINITY, INFINITY, INFINITY);
+                }
+            }
             return 0u;
         }
     }
