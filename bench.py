@@ -362,7 +362,7 @@ def codebook_mode(ctx, w, su, sv, n_tiles):
 def channel_mode(ctx, n_tiles, steps):
     """Out-channel RMS normalization on a 4096x4096 bf16 matrix whose rows have
     unequal scale (log-normal spread, 0.2% all-zero rows): the normalization
-    kernel alone (median of 20 calls; HBM-bound: 2 B read and 4 B written per
+    kernel alone (mean of 20 launches; HBM-bound: 2 B read and 4 B written per
     element), then normalization + K = 2 quantization with the golden section."""
     import torch
     import workloads
@@ -371,15 +371,14 @@ def channel_mode(ctx, n_tiles, steps):
     w = torch.from_numpy(m.w).to(torch.bfloat16).to(dev)
     su, sv = torch.from_numpy(m.su).to(dev), torch.from_numpy(m.sv).to(dev)
     ctx.channel_normalize(w, su)
-    ts = []
+    # the kernel's own duration: HIP events around each launch on the library's
+    # stream (events around the Python call would add the host's call overhead)
+    ctx.set_timing(True)
     for _ in range(20):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
         ctx.channel_normalize(w, su)
-        e1.record()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    ms = sorted(ts)[10]
+    total, launches, _ = ctx.read_timing("channel")
+    ctx.set_timing(False)
+    ms = total / launches
     nbytes = 4096 * 4096 * (2 + 4)
     n = max(1, steps // 2)
     torch.cuda.synchronize()

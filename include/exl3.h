@@ -397,8 +397,9 @@ enum {
     EXL3_KERNEL_FWD_SIDE = 5,    /* forward passes of a scale-search probe's last
                                     partial round, run on a second stream beside
                                     the main part (their durations overlap) */
-    EXL3_KERNEL_FWD_COST = 6     /* pass 2's cost-only form (scale-search probes,
+    EXL3_KERNEL_FWD_COST = 6,    /* pass 2's cost-only form (scale-search probes,
                                     on the context's stream) */
+    EXL3_KERNEL_CHANNEL = 7      /* out-channel normalization (tile count 0) */
 };
 
 /*

@@ -5,8 +5,11 @@ Source: "EXL3 Intel Arc Quantizer" README, Core Implemented Architecture item 8.
 Normalized matrix, folded signs and binary64 row rms bit-exact against
 oracle.channel_normalize, for bf16 and fp32 inputs, ragged bands (rows not a
 multiple of 16) and ragged column chunks (cols not a multiple of 256), all-zero
-rows, and the 4096x4096 size of the projection workload; the normalized matrix
-then quantizes bit-exactly like any other input; malformed arguments are rejected.
+rows, and the 4096x4096 size of the projection workload; rows whose sums round at
+most additions (values spread over many binades, subnormals, a few tiny values
+among large ones), so that the kernel's exact block shortcut is refused and its
+one-square-at-a-time path runs; the normalized matrix then quantizes
+bit-exactly like any other input; malformed arguments are rejected.
 """
 import ctypes
 
@@ -54,6 +57,35 @@ def test_channel_normalize_bit_exact(ctx, rows, cols, bf16, dead):
     print("\nchannel_normalize %dx%d bf16=%s dead=%g" % (rows, cols, bf16, dead), flush=True)
     m = workloads.channel_spread(rows, cols, 300 + rows, 400 + cols, bf16=bf16, dead=dead)
     _check(ctx, m)
+
+
+def _spread_rows(rows, cols, seed, bf16):
+    """Rows whose binary64 sums round often: |values| 2^U(-149, 40) (fp32) or
+    2^U(-133, 40) (bf16), random signs; one row of subnormals with every 64th
+    value normal of standard deviation 1e-3; one row of N(0, 1) with every 97th value 2^-30."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lo = -149.0 if not bf16 else -133.0
+    w = (rng.choice([-1.0, 1.0], (rows, cols)) * np.exp2(rng.uniform(lo, 40.0, (rows, cols))))
+    w = w.astype(np.float32)
+    w[0] = (rng.standard_normal(cols) * 1e-40).astype(np.float32)
+    w[0, ::64] = (rng.standard_normal(len(w[0, ::64])) * 1e-3).astype(np.float32)
+    w[1] = rng.standard_normal(cols).astype(np.float32)
+    w[1, ::97] = np.float32(2.0 ** -30)
+    if bf16:
+        w = workloads.to_bf16_values(w)
+    su = np.where(rng.random(rows) < 0.5, -1.0, 1.0).astype(np.float32)
+    return workloads.Matrix("spread", w, "bf16" if bf16 else "f32", su, np.ones(cols, np.float32),
+                            128, 2, None)
+
+
+@pytest.mark.parametrize("rows,cols,bf16", [
+    (48, 1024, False),          # three whole bands, whole chunks
+    (33, 2056, True),           # ragged band, a last chunk of one block
+    (17, 4100, False),          # ragged band and chunk
+])
+def test_channel_normalize_rounding_rows(ctx, rows, cols, bf16):
+    print("\nchannel_normalize rounding rows %dx%d bf16=%s" % (rows, cols, bf16), flush=True)
+    _check(ctx, _spread_rows(rows, cols, 500 + rows, bf16))
 
 
 def test_all_zero_matrix(ctx):

@@ -721,9 +721,11 @@ int exl3_regularize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int col
         (rc = check_span(ctx, nonfinite, sizeof(int), "nonfinite")) != EXL3_OK)
         return rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
+    const int id = open_timed(ctx, EXL3_KERNEL_REGULARIZE, (int64_t)ntiles);
     EXL3_HIP(ctx, exl3::launch_regularize(w, w_dtype, rows, cols, had_block, su, sv, w_reg,
                                           out_layout, tile_sumsq, nonfinite, tile_order(ctx),
                                           ctx->stream));
+    close_timed(ctx, id);
     return EXL3_OK;
 }
 
@@ -779,8 +781,10 @@ int exl3_channel_normalize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, 
         return rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
     if ((rc = check_signs(ctx, su, rows, "su")) != EXL3_OK) return rc;
+    const int id = open_timed(ctx, EXL3_KERNEL_CHANNEL, 0);
     EXL3_HIP(ctx, exl3::launch_channel_normalize(w, w_dtype, rows, cols, su, floor, w_norm,
                                                  su_folded, row_rms, ctx->stream));
+    close_timed(ctx, id);
     return EXL3_OK;
 }
 

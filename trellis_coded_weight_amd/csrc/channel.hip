@@ -11,10 +11,11 @@
 // The binary64 square of a binary32 value is exact, so only the additions
 // round, in column order.
 //
-// Both kernels below use one workgroup of 256 lanes per band of 16 rows, in
-// which one lane per row adds its row's squares in column order: the chain of
-// `cols` dependent binary64 additions per row (all rows in parallel) is the
-// kernel's latency.  A second sweep writes the scaled rows.
+// Both kernels below use one workgroup per band of rows (16 in the general
+// form, 4 in the fast one), in which one lane per row adds its row's squares in
+// column order (the general form one at a time: a chain of `cols` dependent
+// binary64 additions; the fast form a group of squares at a time where that is
+// provably exact, see below).  A second sweep writes the scaled rows.
 #include "exl3.h"
 #include "exl3_internal.h"
 
@@ -76,148 +77,252 @@ channel_normalize_any_kernel(const Tin *__restrict__ w, int rows, int cols,
 }
 
 
+// Exact shortcut for the row sums.  The squares are exact binary64 values and
+// the running sum a is non-negative, so when a and the squares of a block are
+// all integer multiples of one power of two u and the exact total
+// A = a + s_1 + ... + s_n is below 2^53 u, every partial sum is a multiple of u
+// below 2^53 u, hence representable: none of the n additions rounds, and
+// a + (s_1 + ... + s_n), with the block's squares summed in any order, is the
+// sequential result bit for bit.  Rounding is monotone and 2^53 u is
+// representable, so a computed total below 2^53 u implies the exact one is too
+// (if some partial sum reached 2^53 u, so would every later computed sum).
+// For u the row's lane keeps a lower bound g on the lowest set bit of a: the
+// minimum of the lowest set bits of the squares taken since the last block
+// that was added one square at a time (a is an exact sum from there on), and
+// that block's result's unit in the last place (every binary64 value is a
+// multiple of it).  The test is then A < 2^53 min(g, lowest set bit of the
+// block's squares).  It is taken for groups of eight blocks at once, with the
+// group's squares summed in a tree: every computed partial sum of non-negative
+// values is at most the computed total (rounding is monotone), so a total below
+// 2^53 u, u now the smallest of the group's and g, again makes every addition
+// of the tree exact.  A group that fails is taken again block by block in
+// column order; blocks that fail, and blocks with a NaN or infinity (bound 0),
+// are added one square at a time.
+constexpr int kBig = 1 << 20;          // "no set bit" (a zero)
+
+// 2^(53 + 2 m): the shortcut's bound for squares of values whose lowest set
+// bit is at least 2^m; m = kBig (all zero) gives +inf, m = -kBig (a NaN or
+// infinity) 0
+__device__ __forceinline__ double square_bound(int m) {
+    return m == kBig ? (double)INFINITY : m == -kBig ? 0.0 : ldexp(1.0, 53 + 2 * m);
+}
+
+// 2^(floor(log2(a)) + 1) for a > 0 (binary64): 2^53 times the unit in the last
+// place of a normal a; for a subnormal one at most 2^53 times 2^-1074 (a
+// smaller bound than needed, so only stricter)
+__device__ __forceinline__ double next_binade(double a) {
+    const uint64_t bits = (uint64_t)__double_as_longlong(a);
+    const int ex = (int)((bits >> 52) & 0x7FFu);
+    const uint64_t mant = bits & 0xFFFFFFFFFFFFFull;
+    const int lg = ex ? ex - 1023 : 63 - (int)__builtin_clzll(mant | 1ull) - 1074;
+    return ldexp(1.0, lg + 1);
+}
+
 // The fast form for rows of whole 16-byte groups (cols * sizeof(Tin) and the
 // output row a multiple of 16 bytes, both arrays 16-byte aligned).  Workgroup
-// of 320 lanes per band of 16 rows.  Wave 0's lanes 0..15 own the band's rows
-// and run the sequential binary64 sums; waves 1..4 load the band in chunks of
-// kFastCols columns, each lane keeping kFifo chunks of loads in flight in
-// registers, and store chunk k into a two-slot LDS ring as binary64 squares
-// (the square of a binary32 value is exact in binary64) just before the
-// barrier after which wave 0 adds them, one dependent v_add_f64 per element in
-// column order.  Then all lanes read the band again with 16-byte loads and
-// write the scaled rows with 16-byte stores.  The time is that of the longest
-// dependent chain: `cols` additions, each group of 16 waiting for its LDS
-// reads, and one barrier per chunk (4096 columns: ~0.07 ms, against 0.013 ms
-// for the 100 MB of traffic at the HBM peak).
-constexpr int kFastCols = 128;                 // columns per chunk
-constexpr int kFifo = 8;                       // chunks of loads in flight per loader lane
-constexpr int kLoaders = 256;                  // loader lanes (waves 1..4)
-constexpr int kRingStride = kFastCols + 2;     // binary64 words per ring row
+// of 256 lanes per band of 4 rows (four workgroups share a compute unit, which
+// hides each one's latencies).  All lanes load the band in chunks of
+// kChunkBlocks 16-byte blocks per row, one block per lane, keeping kFifo
+// chunks of loads in flight in registers (every lane issues every load, from a
+// clamped address where it has none, so that the compiler's waits for them
+// count exactly); for each block they store into a two-slot LDS ring the sum
+// of its squares, the bound of the shortcut above and its raw bits, and per
+// group of eight blocks (eight neighbouring lanes, reduced with lane shuffles)
+// the sum of their sums and the smallest of their bounds.  The lowest set bit
+// of a value is bounded below from its exponent alone (2^(E - p + 1) for p
+// significant bits), looser than the bit itself but one comparison per value.
+// The kernel's time (4096 x 4096 bf16: 33 us against 49 us for one addition
+// per square) is now the VALU work of these summaries and the per-chunk
+// barriers, not the additions.  Wave 0's lanes 0..3 also own the band's rows and take
+// the groups in column order: one dependent addition and one test per group
+// when it passes, block by block (and a failing block's squares one by one)
+// when not.  Then all lanes read the band again with 16-byte loads and write
+// the scaled rows with 16-byte stores.
+constexpr int kFastRows = 4;                   // rows per band of the fast form
+constexpr int kChunkBlocks = 64;               // 16-byte blocks per row per chunk
+constexpr int kFifo = 4;                       // chunks of loads in flight per lane
+constexpr int kFastLanes = 256;                // lanes of the workgroup
+constexpr int kRingStride = kChunkBlocks + 1;
+constexpr int kGroup = 8;                      // blocks per shortcut group
+constexpr int kGroupStride = kChunkBlocks / kGroup + 1;
+static_assert(kFastRows * kChunkBlocks == kFastLanes, "one block per lane per chunk");
 
 template <typename Tin>
-__global__ void __launch_bounds__(64 + kLoaders)
+__device__ __forceinline__ void unpack_block(const uint4 &u, float (&v)[16 / sizeof(Tin)]) {
+    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+    if constexpr (sizeof(Tin) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = __uint_as_float(wd[e] << 16);             // bf16 -> fp32 is exact
+            v[2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(wd[e]);
+    }
+}
+
+template <typename Tin>
+__global__ void __launch_bounds__(kFastLanes)
 channel_normalize_kernel(const Tin *__restrict__ w, int rows, int cols,
                          const float *__restrict__ su, double floor_value,
                          float *__restrict__ w_norm, float *__restrict__ su_folded,
                          double *__restrict__ row_rms) {
-    constexpr int EPL = 16 / sizeof(Tin);                  // elements per 16-byte load
-    constexpr int LPR = kFastCols / EPL;                   // loads per chunk row
-    constexpr int NLD = kBandRows * LPR / kLoaders;        // loads per loader lane per chunk
-    static_assert(NLD * kLoaders == kBandRows * LPR, "loads divide over the loader lanes");
-    __shared__ double ring[2][kBandRows][kRingStride];
-    __shared__ float factor[kBandRows];
+    constexpr int EPL = 16 / sizeof(Tin);                  // elements per 16-byte block
+    constexpr int kSig = sizeof(Tin) == 2 ? 8 : 24;        // significant bits of the input
+    __shared__ double ring_sum[2][kFastRows][kRingStride];
+    __shared__ double ring_bound[2][kFastRows][kRingStride];
+    __shared__ uint4 ring_raw[2][kFastRows][kRingStride];
+    __shared__ double2 ring_group[2][kFastRows][kGroupStride];   // group sum, group bound
+    __shared__ float factor[kFastRows];
     const int t = threadIdx.x;
-    const bool loader = t >= 64;
-    const int lt = t - 64;
-    const int row0 = blockIdx.x * kBandRows;
-    const int nr = min(kBandRows, rows - row0);
-    const int nchunk = (cols + kFastCols - 1) / kFastCols;
+    const int row0 = blockIdx.x * kFastRows;
+    const int nr = min(kFastRows, rows - row0);
+    const int nblk = cols / EPL;                           // blocks per row
+    const int nchunk = (nblk + kChunkBlocks - 1) / kChunkBlocks;
+    // the lane's block of each chunk: row r, block b; eight consecutive lanes
+    // hold the blocks of a group
+    const int r = t / kChunkBlocks, b = t % kChunkBlocks;
+    const int rc = min(r, nr - 1);
 
-    uint4 fifo[kFifo][NLD];
-    auto issue = [&](int k, uint4 (&dst)[NLD]) {
+    uint4 fifo[kFifo];
+    auto issue = [&](int k, uint4 &dst) {
+        // past the band or the row: a load of the row's last block, unused
+        const int bl = min(k * kChunkBlocks + b, nblk - 1);
+        dst = *reinterpret_cast<const uint4 *>(w + (size_t)(row0 + rc) * cols + (size_t)bl * EPL);
+    };
+    auto store = [&](int k, const uint4 &src) {
+        const bool valid = r < nr && k < nchunk && k * kChunkBlocks + b < nblk;
+        float v[EPL];
+        unpack_block<Tin>(src, v);
+        uint32_t emin = 0x1FFu;                            // smallest exponent field of a nonzero value
+        bool bad = false;
+        double sq[EPL];
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int q = lt + kLoaders * i, r = q / LPR, cb = (q % LPR) * EPL;
-            if (k < nchunk && r < nr && k * kFastCols + cb < cols)
-                dst[i] = *reinterpret_cast<const uint4 *>(w + (size_t)(row0 + r) * cols +
-                                                          k * kFastCols + cb);
+        for (int e = 0; e < EPL; ++e) {
+            const uint32_t bits = __float_as_uint(v[e]);
+            const uint32_t ex = (bits >> 23) & 0xFFu;
+            bad = bad | (ex == 0xFFu);
+            emin = min(emin, (bits & 0x7FFFFFFFu) ? max(ex, 1u) : 0x1FFu);
+            const double d = (double)v[e];
+            sq[e] = d * d;                                 // exact in binary64
+        }
+#pragma unroll
+        for (int h = 1; h < EPL; h <<= 1)
+#pragma unroll
+            for (int e = 0; e < EPL; e += 2 * h) sq[e] = sq[e] + sq[e + h];
+        int m = bad ? -kBig : emin == 0x1FFu ? kBig : (int)emin - 127 - (kSig - 1);
+        if (!valid) m = kBig;
+        const double s0 = valid ? sq[0] : 0.0;
+        int mg = m;
+        double sg = s0;
+#pragma unroll
+        for (int x = 1; x < kGroup; x <<= 1) {
+            mg = min(mg, __shfl_xor(mg, x));
+            sg = sg + __shfl_xor(sg, x);
+        }
+        if (valid) {
+            ring_sum[k & 1][r][b] = s0;
+            ring_bound[k & 1][r][b] = square_bound(m);
+            ring_raw[k & 1][r][b] = src;
+            if (b % kGroup == 0)
+                ring_group[k & 1][r][b / kGroup] = make_double2(sg, square_bound(mg));
         }
     };
-    auto store = [&](int k, const uint4 (&src)[NLD]) {
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int q = lt + kLoaders * i, r = q / LPR, cb = (q % LPR) * EPL;
-            if (r >= nr || k * kFastCols + cb >= cols) continue;
-            const uint32_t wd[4] = {src[i].x, src[i].y, src[i].z, src[i].w};
-            double v[EPL];
-            if constexpr (EPL == 8) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[2 * e] = (double)__uint_as_float(wd[e] << 16);     // bf16 -> fp32 exact
-                    v[2 * e + 1] = (double)__uint_as_float(wd[e] & 0xFFFF0000u);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (double)__uint_as_float(wd[e]);
-            }
-            double *dst = &ring[k & 1][r][cb];
-            // the squares (exact in binary64): the row sums only add
-#pragma unroll
-            for (int e = 0; e < EPL; e += 2)
-                *reinterpret_cast<double2 *>(dst + e) =
-                    make_double2(v[e] * v[e], v[e + 1] * v[e + 1]);
-        }
-    };
 
-    if (loader) {
-#pragma unroll
-        for (int j = 0; j < kFifo; ++j) issue(j, fifo[j]);
-    }
     double acc = 0.0;
-    for (int k0 = 0; k0 < nchunk; k0 += kFifo) {
+    double gbound = INFINITY;                      // 2^53 x the lower bound g on acc's lowest set bit
+    // the first pass of the loop only issues the first kFifo chunks' loads, so
+    // that every load is issued by the same instructions into the same
+    // registers (the compiler's waits then keep kFifo - 1 chunks in flight)
+    for (int k0 = -kFifo; k0 < nchunk; k0 += kFifo) {
 #pragma unroll
         for (int j = 0; j < kFifo; ++j) {
             const int k = k0 + j;
-            if (loader && k < nchunk) {
-                store(k, fifo[j]);
-                issue(k + kFifo, fifo[j]);
-            }
+            if (k >= 0) store(k, fifo[j]);
+            issue(k + kFifo, fifo[j]);
+            if (k < 0) continue;
             __syncthreads();                           // chunk k is in ring slot k & 1
             if (t < nr && k < nchunk) {
-                const double *src = ring[k & 1][t];
-                const int nc = min(kFastCols, cols - k * kFastCols);
-#pragma unroll 16
-                for (int c = 0; c < nc; ++c) acc = acc + src[c];
+                const double *S = ring_sum[k & 1][t];
+                const double *B = ring_bound[k & 1][t];
+                const double2 *G = ring_group[k & 1][t];
+                const int nb = min(kChunkBlocks, nblk - k * kChunkBlocks);
+                const int ngr = (nb + kGroup - 1) / kGroup;
+                double2 gn = G[0];
+                for (int gi = 0; gi < ngr; ++gi) {
+                    // the group on the shortcut: its blocks' sums summed in a
+                    // tree by the loaders, one dependent addition, one test
+                    const double2 gc = gn;
+                    gn = G[min(gi + 1, kChunkBlocks / kGroup - 1)];
+                    const double a = acc + gc.x;
+                    if ((a < gbound) & (a < gc.y)) {
+                        acc = a;
+                        gbound = gc.y < gbound ? gc.y : gbound;
+                    } else {
+                        // again from the group's start, a block at a time
+                        double x = acc, g = gbound;
+                        const int b0 = gi * kGroup, ng = min(kGroup, nb - b0);
+                        for (int i = 0; i < ng; ++i) {
+                            const double A = x + S[b0 + i];
+                            const double bb = B[b0 + i];
+                            g = bb < g ? bb : g;
+                            if (A < g) {
+                                x = A;
+                            } else {
+                                float v[EPL];
+                                unpack_block<Tin>(ring_raw[k & 1][t][b0 + i], v);
+#pragma unroll
+                                for (int e = 0; e < EPL; ++e) {
+                                    const double d = (double)v[e];
+                                    x = x + d * d;
+                                }
+                                // x is now a multiple of its unit in the last
+                                // place: that alone bounds its lowest set bit
+                                g = x > 0.0 ? next_binade(x) : g;
+                            }
+                        }
+                        acc = x;
+                        gbound = g;
+                    }
+                }
             }
         }
     }
     if (t < nr) {
         const int i = row0 + t;
-        const double r = sqrt(acc / (double)cols);
-        const double r_eff = r == 0.0 ? floor_value : r;
+        const double rr = sqrt(acc / (double)cols);
+        const double r_eff = rr == 0.0 ? floor_value : rr;
         factor[t] = (float)(1.0 / r_eff);
-        su_folded[i] = r == 0.0 ? 0.0f : su[i] * (float)r;
-        if (row_rms) row_rms[i] = r;
+        su_folded[i] = rr == 0.0 ? 0.0f : su[i] * (float)rr;
+        if (row_rms) row_rms[i] = rr;
     }
     __syncthreads();
 
     // scaled rows: 16-byte loads (kBatch in flight per lane), 16-byte stores
     constexpr int kBatch = 8;
-    constexpr int kLanes = 64 + kLoaders;
-    const int gpr = cols / EPL;                        // load groups per row
-    const int ng = nr * gpr;
-    for (int q0 = t; q0 < ng; q0 += kBatch * kLanes) {
+    const int ng = nr * nblk;
+    for (int q0 = t; q0 < ng; q0 += kBatch * kFastLanes) {
         uint4 ub[kBatch];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int q = q0 + b * kLanes;
-            if (q < ng)
-                ub[b] = *reinterpret_cast<const uint4 *>(
-                    w + (size_t)(row0 + q / gpr) * cols + (q % gpr) * EPL);
+        for (int bt = 0; bt < kBatch; ++bt) {
+            const int q = min(q0 + bt * kFastLanes, ng - 1);
+            ub[bt] = *reinterpret_cast<const uint4 *>(
+                w + (size_t)(row0 + q / nblk) * cols + (size_t)(q % nblk) * EPL);
         }
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-        const int q = q0 + b * kLanes;
-        if (q >= ng) break;
-        const int r = q / gpr, cb = (q % gpr) * EPL;
-        const size_t base = (size_t)(row0 + r) * cols + cb;
-        const uint4 u = ub[b];
-        const float f = factor[r];
-        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-        if constexpr (EPL == 8) {
-            float v[8];
+        for (int bt = 0; bt < kBatch; ++bt) {
+            const int q = q0 + bt * kFastLanes;
+            if (q >= ng) break;
+            const int rq = q / nblk;
+            const size_t base = (size_t)(row0 + rq) * cols + (size_t)(q % nblk) * EPL;
+            const float f = factor[rq];
+            float v[EPL];
+            unpack_block<Tin>(ub[bt], v);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[2 * e] = __uint_as_float(wd[e] << 16) * f;
-                v[2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u) * f;
-            }
-            *reinterpret_cast<float4 *>(w_norm + base) = make_float4(v[0], v[1], v[2], v[3]);
-            *reinterpret_cast<float4 *>(w_norm + base + 4) = make_float4(v[4], v[5], v[6], v[7]);
-        } else {
-            *reinterpret_cast<float4 *>(w_norm + base) =
-                make_float4(__uint_as_float(wd[0]) * f, __uint_as_float(wd[1]) * f,
-                            __uint_as_float(wd[2]) * f, __uint_as_float(wd[3]) * f);
-        }
+            for (int e = 0; e < EPL; e += 4)
+                *reinterpret_cast<float4 *>(w_norm + base + e) =
+                    make_float4(v[e] * f, v[e + 1] * f, v[e + 2] * f, v[e + 3] * f);
         }
     }
 }
@@ -229,6 +334,7 @@ hipError_t launch_channel_normalize(const void *w, int w_dtype, int rows, int co
                                     float *su_folded, double *row_rms, hipStream_t stream) {
     if (rows <= 0 || cols <= 0) return hipErrorInvalidValue;
     const unsigned blocks = (unsigned)((rows + kBandRows - 1) / kBandRows);
+    const unsigned fast_blocks = (unsigned)((rows + kFastRows - 1) / kFastRows);
     const size_t in_bytes = w_dtype == EXL3_BF16 ? 2 : 4;
     const bool fast = reinterpret_cast<uintptr_t>(w) % 16 == 0 &&
                       reinterpret_cast<uintptr_t>(w_norm) % 16 == 0 &&
@@ -236,7 +342,7 @@ hipError_t launch_channel_normalize(const void *w, int w_dtype, int rows, int co
     if (w_dtype == EXL3_BF16) {
         const uint16_t *wb = static_cast<const uint16_t *>(w);
         if (fast)
-            hipLaunchKernelGGL(channel_normalize_kernel<uint16_t>, dim3(blocks), dim3(64 + kLoaders), 0,
+            hipLaunchKernelGGL(channel_normalize_kernel<uint16_t>, dim3(fast_blocks), dim3(kFastLanes), 0,
                                stream, wb, rows, cols, su, floor_value, w_norm, su_folded,
                                row_rms);
         else
@@ -246,7 +352,7 @@ hipError_t launch_channel_normalize(const void *w, int w_dtype, int rows, int co
     } else {
         const float *wf = static_cast<const float *>(w);
         if (fast)
-            hipLaunchKernelGGL(channel_normalize_kernel<float>, dim3(blocks), dim3(64 + kLoaders), 0,
+            hipLaunchKernelGGL(channel_normalize_kernel<float>, dim3(fast_blocks), dim3(kFastLanes), 0,
                                stream, wf, rows, cols, su, floor_value, w_norm, su_folded,
                                row_rms);
         else
