@@ -161,6 +161,13 @@ def cpu_description():
     return info
 
 
+def gss_probes(iters: int) -> int:
+    """Sample encodes of a golden-section search with `iters` reductions: the two
+    starting points and one new point per reduction except the last, whose
+    score the result (the last bracket's midpoint) never reads."""
+    return iters + 1
+
+
 def cpu_baseline(m, K, scale, n_tiles, threads, sample_tiles):
     """Oracle on this host: full regularization and statistics, plus the final
     encode of `sample_tiles` tiles; extrapolated to the whole step."""
@@ -183,7 +190,7 @@ def cpu_baseline(m, K, scale, n_tiles, threads, sample_tiles):
     oracle.encode_tiles(tiles[idx[:n1]], K, np.float32(scale), levels, threads=1)
     per_tile_1 = (time.perf_counter() - t2) / n1
     TR, TC = m.w.shape[0] // 16, m.w.shape[1] // 16
-    encodes = n_tiles + (m.gss[0] + 2) * sample_size(TR, TC)
+    encodes = n_tiles + gss_probes(m.gss[0]) * sample_size(TR, TC)
     total = t_reg + per_tile * encodes
     return {
         "value": n_tiles / total,
@@ -551,7 +558,7 @@ def main():
     value = n_tiles * args.steps / dt
     ms_step = 1000.0 * dt / args.steps
     TR, TC = R // 16, C // 16
-    gss_encodes = (m.gss[0] + 2) * sample_size(TR, TC)
+    gss_encodes = gss_probes(m.gss[0]) * sample_size(TR, TC)
     encodes_per_s = (n_tiles + gss_encodes) * args.steps / dt
 
     # the same steps again with every launch bracketed by HIP events on the

@@ -296,8 +296,10 @@ int exl3_decode_tiles(exl3_ctx *ctx, const uint16_t *packed, int64_t n, int K, f
  * scale on the tile sample (wrapped diagonal plus the highest- and
  * lowest-energy tiles), whose objective is the binary64 sum, in ascending tile
  * order, of the sample tiles' squared errors; the result is the midpoint of the
- * final bracket rounded to binary32 (0 when rms is 0).  Then every tile is
- * encoded at that scale.
+ * final bracket rounded to binary32 (0 when rms is 0).  The sample is encoded
+ * iters + 1 times: the last reduction's new point is never scored, since the
+ * bracket it narrows already fixes the result.  Then every tile is encoded at
+ * that scale.
  *   w, w_dtype, rows, cols, had_block, su, sv : as exl3_regularize
  *   packed    uint16 [rows/16][cols/16][16*K]
  *   scale_out HOST float [1]: the scale used

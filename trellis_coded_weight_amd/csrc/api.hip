@@ -1095,20 +1095,24 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
             const double g = (std::sqrt(5.0) - 1.0) / 2.0;
             double a = gss->lo * rms, b = gss->hi * rms;
             double p = b - (b - a) * g, q = a + (b - a) * g;
+            // The result is the midpoint of the last bracket, which the last
+            // reduction sets before its new point is scored: that score can
+            // never be read, so it is not computed (iters + 1 probes in all).
             double fp = objective(p), fq = objective(q);
             for (int it = 0; it < gss->iters && err == EXL3_OK; ++it) {
+                const bool last = it + 1 == gss->iters;
                 if (fp < fq) {
                     b = q;
                     q = p;
                     fq = fp;
                     p = b - (b - a) * g;
-                    fp = objective(p);
+                    if (!last) fp = objective(p);
                 } else {
                     a = p;
                     p = q;
                     fp = fq;
                     q = a + (b - a) * g;
-                    fq = objective(q);
+                    if (!last) fq = objective(q);
                 }
             }
             if (err != EXL3_OK) return err;
