@@ -182,6 +182,20 @@ def test_small_matrix_with_scale_search(ctx, K):
     assert got["mse"] == want["mse"]
 
 
+def test_module_level_quantize_matrix_tuple():
+    """trellis_coded_weight_amd.quantize_matrix returns (packed, scale, mse) of the
+    same search as the oracle's (a context per device kept for the process)."""
+    import trellis_coded_weight_amd as T
+    m = workloads.gaussian(256, 256, 0.02, 71, 72, K=2)
+    want = oracle.quantize_matrix(m.w, m.su, m.sv, 2, had_block=128, gss=m.gss)
+    packed, scale, mse = T.quantize_matrix(torch.from_numpy(m.w).to(torch.bfloat16).to(DEV), 2,
+                                           torch.from_numpy(m.su).to(DEV),
+                                           torch.from_numpy(m.sv).to(DEV))
+    assert np.float32(scale) == want["scale"]
+    assert np.array_equal(_u16(packed).reshape(-1, 32), want["packed"])
+    assert mse == want["mse"]
+
+
 @pytest.mark.parametrize("K", [2, 3])
 def test_small_matrix_with_grid_search(ctx, K):
     import trellis_coded_weight_amd as T

@@ -7,5 +7,5 @@ tensors into it.  There is no CPU fallback.
 from .binding import (  # noqa: F401
     CODEBOOK_KINDS, EXPORTED, GRID_PAGES, Context, Exl3Error, EXL3_BF16, EXL3_EHIP, EXL3_EINVAL, EXL3_ENOMEM,
     EXL3_ENONFINITE, EXL3_EUNSUPPORTED, EXL3_F32, EXL3_OK, EXL3_ROW_MAJOR, EXL3_TILE_MAJOR, library_path, load_library,
-    scratch_per_tile, version,
+    quantize_matrix, scratch_per_tile, version,
 )

@@ -482,3 +482,22 @@ def scratch_per_tile(K: int) -> int:
 
 def version() -> str:
     return load_library().exl3_version().decode()
+
+
+_DEFAULT_CTX = {}
+
+
+def quantize_matrix(w: torch.Tensor, K: int, su: torch.Tensor, sv: torch.Tensor,
+                    had_block: int = 128,
+                    gss: Optional[Tuple[int, float, float]] = (12, 0.5, 2.0),
+                    scale: float = 1.0):
+    """The whole-matrix path as a tuple: (packed int16 [R/16, C/16, 16K], scale,
+    mse), on a context per device kept for the process (its scratch is the
+    library's default bound).  Context.quantize_matrix takes the same arguments
+    and also returns the optional outputs."""
+    dev = w.device.index if w.device.index is not None else torch.cuda.current_device()
+    ctx = _DEFAULT_CTX.get(dev)
+    if ctx is None:
+        ctx = _DEFAULT_CTX[dev] = Context(dev)
+    out = ctx.quantize_matrix(w, K, su, sv, had_block=had_block, gss=gss, scale=scale)
+    return out["packed"], out["scale"], out["mse"]
