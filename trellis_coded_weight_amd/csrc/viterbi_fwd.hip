@@ -409,6 +409,81 @@ __device__ __forceinline__ uint32_t trellis_step(
     return bits;
 }
 
+// K = 2, passes 2 and 3: a quarter of a step, where the rest of it provably
+// does not matter.  Both ends of these passes are pinned by X:
+//  * in step t <= 5 the finite tracked minima all come from X's low bits and
+//    t + 1 new symbols, so the butterflies with finite inputs all have the same
+//    index i_t = (X >> (10 - 2t)) & 3 among each lane's four (FIX = 0, V = i_t):
+//    the lane runs that butterfly's four updates and stores +inf, the exact
+//    result, for the other twelve (every minimum is written, so the two buffers
+//    hold exactly what the full steps would leave there);
+//  * in step 254 - j, j <= 6, only minima that can lead to the state X read at
+//    the end matter, and those all end in the same symbol b = (X >> (2 + 2j))
+//    & 3 (FIX = 1, V = b): the lane runs its four updates at position b and
+//    leaves the other minima as they were (no later update that matters reads
+//    them); the traceback from X reads only these backpointer fields.
+// The updates that run are the full step's, operation for operation.
+template <bool BITS, bool SKEW, int FIX, int V>
+__device__ __forceinline__ uint32_t part_step2_v(float xt, const float *__restrict__ Mc,
+                                                 float *__restrict__ Mn, const Levels<2> &lv,
+                                                 const int (&m)[4]) {
+    float Mk[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (FIX == 1 || i == V)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                Mk[i][k] = Mc[lds_word<2, SKEW>(((uint32_t)k << 12) | (uint32_t)m[i])];
+    if constexpr (FIX == 0) {
+        bool finite = false;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) finite = finite || Mk[V][k] != INFINITY;
+        const bool live = __builtin_amdgcn_ballot_w64(finite) != 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (i != V || !live)
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+                    Mn[lds_word<2, SKEW>(((uint32_t)m[i] << 2) | (uint32_t)bb)] = INFINITY;
+        if (!live) return 0u;
+    }
+    uint32_t bits = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            if ((FIX == 0 && i != V) || (FIX == 1 && bb != V)) continue;
+            double c[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float d = xt - lv.at(i, k, bb);
+                float q = d * d;
+                c[k] = cost_index(Mk[i][k] + q, (uint32_t)k);
+            }
+            const uint64_t w =
+                __builtin_bit_cast(uint64_t, lex_min(lex_min(c[0], c[1]), lex_min(c[2], c[3])));
+            Mn[lds_word<2, SKEW>(((uint32_t)m[i] << 2) | (uint32_t)bb)] =
+                __uint_as_float((uint32_t)(w >> 32));
+            if constexpr (BITS) bits |= ((uint32_t)w & 3u) << (2 * (15 - (4 * i + bb)));
+        }
+    return bits;
+}
+
+template <bool BITS, bool SKEW, int FIX>
+__device__ __forceinline__ uint32_t part_step2(int v, float xt, const float *__restrict__ Mc,
+                                               float *__restrict__ Mn, const Levels<2> &lv,
+                                               const int (&m)[4]) {
+    switch (v) {
+        case 0: return part_step2_v<BITS, SKEW, FIX, 0>(xt, Mc, Mn, lv, m);
+        case 1: return part_step2_v<BITS, SKEW, FIX, 1>(xt, Mc, Mn, lv, m);
+        case 2: return part_step2_v<BITS, SKEW, FIX, 2>(xt, Mc, Mn, lv, m);
+        default: return part_step2_v<BITS, SKEW, FIX, 3>(xt, Mc, Mn, lv, m);
+    }
+}
+
+constexpr int kPartHead = 6;                   // K = 2: steps 0..5 on one butterfly
+constexpr int kPartTail = 7;                   // K = 2: steps 248..254 on one position
+
 template <int K, int PASS>
 __global__ void __launch_bounds__(kLanes, 1)
 viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile_idx,
@@ -523,6 +598,32 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
                 __syncthreads();
             }
         }
+    } else if constexpr (PASS == 3 && K == 2) {
+        const uint32_t Xf = X_in[b];
+        for (; t < kPartHead; t += 2) {             // steps 0..5: one butterfly
+            const float xn = xin(t + 1);
+            part_step2<false, SKEW, 0>((xm >> (10 - 2 * t)) & 3u, xt, B0, B1, lv, m);
+            __syncthreads();
+            xt = xin(t + 2);
+            part_step2<false, SKEW, 0>((xm >> (8 - 2 * t)) & 3u, xn, B1, B0, lv, m);
+            __syncthreads();
+        }
+        for (; t < kSteps - 1 - kPartTail; t += 2) {   // steps 6..247
+            const float xn = xin(t + 1);
+            trellis_step<K, false, 0, SKEW>(xt, B0, B1, lv, m, b0);
+            __syncthreads();
+            xt = xin(t + 2);
+            trellis_step<K, false, 1, SKEW>(xn, B1, B0, lv, m, b0);
+            __syncthreads();
+        }
+        for (; t < kSteps - 1; ++t) {               // steps 248..254: one position
+            const int j = kSteps - 2 - t;
+            const float xn = xin(t + 1);
+            part_step2<false, SKEW, 1>((Xf >> (2 + 2 * j)) & 3u, xt, (t & 1) ? B1 : B0,
+                                       (t & 1) ? B0 : B1, lv, m);
+            __syncthreads();
+            xt = xn;
+        }
     } else if constexpr (PASS == 3) {
         if constexpr (skip_steps<K>() > 0)
             for (; t < skip_steps<K>(); t += 2) {   // the first steps, unreachable waves skip
@@ -543,6 +644,38 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
                 trellis_step<K, false, 1, SKEW>(xn, B1, B0, lv, m, b0);
                 __syncthreads();
             }
+        }
+    } else if constexpr (K == 2) {
+        const uint32_t Xf = X_in[b];
+        for (; t < kPartHead; t += 2) {             // steps 0..5: one butterfly
+            const float xn = xin(t + 1);
+            uint32_t w = part_step2<true, SKEW, 0>((xm >> (10 - 2 * t)) & 3u, xt, B0, B1, lv, m);
+            bp_tile[(size_t)t * kLanes + g] = (bp_t)w;
+            __syncthreads();
+            xt = xin(t + 2);
+            w = part_step2<true, SKEW, 0>((xm >> (8 - 2 * t)) & 3u, xn, B1, B0, lv, m);
+            bp_tile[(size_t)(t + 1) * kLanes + g] = (bp_t)w;
+            __syncthreads();
+        }
+        for (; t < kSteps - 1 - kPartTail; t += 2) {   // steps 6..247: B0 -> B1 -> B0
+            const float xn = xin(t + 1);
+            uint32_t w = trellis_step<K, true, 0, SKEW>(xt, B0, B1, lv, m, b0);
+            bp_tile[(size_t)t * kLanes + g] = (bp_t)w;
+            __syncthreads();
+            xt = xin(t + 2);
+            w = trellis_step<K, true, 1, SKEW>(xn, B1, B0, lv, m, b0);
+            bp_tile[(size_t)(t + 1) * kLanes + g] = (bp_t)w;
+            __syncthreads();
+        }
+        for (; t < kSteps - 1; ++t) {               // steps 248..254: one position
+            const int j = kSteps - 2 - t;
+            const float xn = xin(t + 1);
+            const uint32_t w = part_step2<true, SKEW, 1>((Xf >> (2 + 2 * j)) & 3u, xt,
+                                                         (t & 1) ? B1 : B0, (t & 1) ? B0 : B1,
+                                                         lv, m);
+            bp_tile[(size_t)t * kLanes + g] = (bp_t)w;
+            __syncthreads();
+            xt = xn;
         }
     } else {
         if constexpr (skip_steps<K>() > 0)
