@@ -599,7 +599,6 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
             }
         }
     } else if constexpr (PASS == 3 && K == 2) {
-        const uint32_t Xf = X_in[b];
         for (; t < kPartHead; t += 2) {             // steps 0..5: one butterfly
             const float xn = xin(t + 1);
             part_step2<false, SKEW, 0>((xm >> (10 - 2 * t)) & 3u, xt, B0, B1, lv, m);
@@ -616,6 +615,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
             trellis_step<K, false, 1, SKEW>(xn, B1, B0, lv, m, b0);
             __syncthreads();
         }
+        const uint32_t Xf = X_in[b];
         for (; t < kSteps - 1; ++t) {               // steps 248..254: one position
             const int j = kSteps - 2 - t;
             const float xn = xin(t + 1);
@@ -646,7 +646,6 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
             }
         }
     } else if constexpr (K == 2) {
-        const uint32_t Xf = X_in[b];
         for (; t < kPartHead; t += 2) {             // steps 0..5: one butterfly
             const float xn = xin(t + 1);
             uint32_t w = part_step2<true, SKEW, 0>((xm >> (10 - 2 * t)) & 3u, xt, B0, B1, lv, m);
@@ -667,13 +666,19 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
             bp_tile[(size_t)(t + 1) * kLanes + g] = (bp_t)w;
             __syncthreads();
         }
+        const uint32_t Xf = X_in[b];
+        // the backpointer address afresh (kept from before the loop it would
+        // hold two registers through it)
+        int gl = g;
+        asm volatile("" : "+v"(gl));
+        bp_t *const bp_last = bp + (size_t)b * kSlots * kLanes + gl;
         for (; t < kSteps - 1; ++t) {               // steps 248..254: one position
             const int j = kSteps - 2 - t;
             const float xn = xin(t + 1);
             const uint32_t w = part_step2<true, SKEW, 1>((Xf >> (2 + 2 * j)) & 3u, xt,
                                                          (t & 1) ? B1 : B0, (t & 1) ? B0 : B1,
                                                          lv, m);
-            bp_tile[(size_t)t * kLanes + g] = (bp_t)w;
+            bp_last[(size_t)t * kLanes] = (bp_t)w;
             __syncthreads();
             xt = xn;
         }
