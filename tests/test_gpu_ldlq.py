@@ -43,16 +43,18 @@ def _dev(m):
     return w, torch.from_numpy(m.su).to(DEV), torch.from_numpy(m.sv).to(DEV)
 
 
-@pytest.mark.parametrize("K,gss", [(2, (12, 0.5, 2.0)), (1, None), (4, None)])
-def test_ldlq_bit_exact_small(ctx, K, gss):
-    m = workloads.gaussian(128, 256, 0.02, 60 + K, 70 + K, K=K, gss=gss)
+# 192 rows with 64-blocks: twelve tile rows, six per stream
+@pytest.mark.parametrize("R,hb,K,gss", [(128, 128, 2, (12, 0.5, 2.0)), (128, 128, 1, None),
+                                        (128, 128, 4, None), (192, 64, 3, None)])
+def test_ldlq_bit_exact_small(ctx, R, hb, K, gss):
+    m = workloads.gaussian(R, 256, 0.02, 60 + K, 70 + K, had_block=hb, K=K, gss=gss)
     L, _ = workloads.ldl_factor(256, 80 + K, off_std=1.5)
-    scale = {1: 0.022, 2: 0.017, 4: 0.012}[K]
-    print("\nldlq 128x256 K=%d gss=%s" % (K, gss), flush=True)
-    want = oracle.quantize_matrix_ldlq(m.w, m.su, m.sv, K, L, had_block=128, gss=gss,
+    scale = {1: 0.022, 2: 0.017, 3: 0.014, 4: 0.012}[K]
+    print("\nldlq %dx256 hb=%d K=%d gss=%s" % (R, hb, K, gss), flush=True)
+    want = oracle.quantize_matrix_ldlq(m.w, m.su, m.sv, K, L, had_block=hb, gss=gss,
                                        fixed_scale=scale)
     w, su, sv = _dev(m)
-    got = ctx.quantize_matrix_ldlq(w, K, su, sv, torch.from_numpy(L).to(DEV), had_block=128,
+    got = ctx.quantize_matrix_ldlq(w, K, su, sv, torch.from_numpy(L).to(DEV), had_block=hb,
                                    gss=gss, scale=scale, want_w_hat=True, want_tile_err=True)
     assert np.float32(got["scale"]) == want["scale"]
     assert np.array_equal(_u16(got["packed"]).reshape(-1, 16 * K), want["packed"])
