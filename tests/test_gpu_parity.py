@@ -130,9 +130,12 @@ def test_decode_matches_oracle(ctx, K):
     assert np.array_equal(_bits(out.cpu().numpy()), _bits(v[states]))
 
 
-@pytest.mark.parametrize("B,dtype", [(64, torch.float32), (128, torch.bfloat16),
-                                     (128, torch.float32)])
-def test_regularize_bit_exact(ctx, B, dtype):
+# misaligned: the weights start one element past a 16-byte boundary (the
+# kernel then loads one element at a time)
+@pytest.mark.parametrize("B,dtype,misaligned", [
+    (64, torch.float32, False), (64, torch.bfloat16, False), (128, torch.bfloat16, False),
+    (128, torch.float32, False), (64, torch.float32, True), (128, torch.bfloat16, True)])
+def test_regularize_bit_exact(ctx, B, dtype, misaligned):
     R, C = 2 * B, 3 * B
     rng = np.random.default_rng(B)
     w = (rng.standard_normal((R, C)) * 0.02).astype(np.float32)
@@ -141,13 +144,19 @@ def test_regularize_bit_exact(ctx, B, dtype):
     su = (2 * rng.integers(0, 2, R) - 1).astype(np.float32)
     sv = (2 * rng.integers(0, 2, C) - 1).astype(np.float32)
     want = oracle.regularize(w32, su, sv, B)
-    out, sums, flag = ctx.regularize(wt.to(DEV), torch.from_numpy(su).to(DEV),
+    wd = wt.to(DEV)
+    if misaligned:
+        buf = torch.zeros(R * C + 1, dtype=dtype, device=DEV)
+        buf[1:] = wd.reshape(-1)
+        wd = buf[1:].view(R, C)
+        assert wd.data_ptr() % 16 != 0
+    out, sums, flag = ctx.regularize(wd, torch.from_numpy(su).to(DEV),
                                      torch.from_numpy(sv).to(DEV), B)
     tiles = oracle.to_tiles(want)
     assert np.array_equal(_bits(out.cpu().numpy()), _bits(tiles))
     assert np.array_equal(_bits(sums.cpu().numpy()), _bits(oracle.tile_sumsq(tiles)))
     assert int(flag.item()) == 0
-    rm, _, _ = ctx.regularize(wt.to(DEV), torch.from_numpy(su).to(DEV),
+    rm, _, _ = ctx.regularize(wd, torch.from_numpy(su).to(DEV),
                               torch.from_numpy(sv).to(DEV), B, tile_major=False)
     assert np.array_equal(_bits(rm.cpu().numpy()), _bits(want))
 
