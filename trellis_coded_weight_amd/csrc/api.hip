@@ -39,6 +39,16 @@ constexpr size_t kNoAllocBookTiles = EXL3_NOALLOC_MAX_TILES_K4;
 constexpr size_t kNoAllocBytes = kNoAllocBpBytes + kNoAllocBookTiles * (2 + 2 + 4);
 static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
 
+// State of a golden-section scale search run on the device: the bracket
+// [a, b], its two points and their scores, the reductions done, which point
+// the next score belongs to (0: p, 1: q), and the scale of the next probe
+// (after the last reduction: the result).
+struct GssDev {
+    double a, b, p, q, fp, fq;
+    int it, pending;
+    float scale;
+};
+
 struct exl3_ctx {
     int device = 0;
     int n_cu = 256;
@@ -66,6 +76,7 @@ struct exl3_ctx {
     float *d_sse = nullptr;
     size_t sse_cap = 0;
     int *d_flag = nullptr;
+    GssDev *d_gss = nullptr;
     // LDLQ: error of the quantized spans (tile-major), one span's target,
     // dequantized values and container words
     float *d_err_tiles = nullptr;
@@ -350,7 +361,7 @@ int ensure_aux(exl3_ctx *ctx) {
 // chain runs on the second stream, so its pass 1 shares a round with the main
 // part's pass 2 instead of leaving the chip idle for a round of its own.
 int probe_split(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, int K, float scale,
-                float *cost_out) {
+                const float *scale_dev, float *cost_out) {
     const int64_t rem = n % ctx->n_cu, a = n - rem;
     const size_t per_tile = exl3::bp_bytes_per_tile(K);
     char *bp = static_cast<char *>(ctx->d_bp);
@@ -368,7 +379,7 @@ int probe_split(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, in
         int id = open_timed(ctx, p.s == ctx->stream ? EXL3_KERNEL_FWD1 : EXL3_KERNEL_FWD_SIDE,
                             p.count, p.s);
         EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 1, x, idx + p.first, 0, p.count, ctx->d_levels,
-                                               scale, nullptr, bp + p.first * per_tile,
+                                               scale, scale_dev, nullptr, bp + p.first * per_tile,
                                                ctx->d_end + p.first, nullptr, p.s));
         close_timed(ctx, id);
     }
@@ -382,7 +393,7 @@ int probe_split(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, in
         id = open_timed(ctx, p.s == ctx->stream ? EXL3_KERNEL_FWD_COST : EXL3_KERNEL_FWD_SIDE,
                         p.count, p.s);
         EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 3, x, idx + p.first, 0, p.count, ctx->d_levels,
-                                               scale, ctx->d_X + p.first,
+                                               scale, scale_dev, ctx->d_X + p.first,
                                                bp + p.first * per_tile, nullptr,
                                                cost_out + p.first, p.s));
         close_timed(ctx, id);
@@ -392,25 +403,75 @@ int probe_split(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, in
     return EXL3_OK;
 }
 
+// One step of the golden-section scale search on the device, after probe k,
+// with the operations of the host form in the same order (so the same scale,
+// bit for bit): the probe's score is the binary64 sum of the sample's path
+// costs in ascending tile order.  Probe 0 scores p0 and probe 1 q0; every
+// later probe scores the point the previous reduction set.  From probe 1 on,
+// one reduction follows; the binary32 value of its new point is the next
+// probe's scale, and after the last reduction the scale is the midpoint of
+// the bracket (the result).  One lane: the sum is a chain of dependent
+// additions anyway.
+__global__ void __launch_bounds__(64)
+gss_step_kernel(GssDev *__restrict__ st, const float *__restrict__ costs, int64_t cnt, double a0,
+                double b0, double p0, double q0, double g, int iters, int k) {
+    if (threadIdx.x != 0) return;
+    double f = 0.0;
+    for (int64_t i = 0; i < cnt; ++i) f += (double)costs[i];
+    GssDev s;
+    if (k == 0) {
+        s = GssDev{a0, b0, p0, q0, f, 0.0, 0, 0, (float)q0};
+        *st = s;
+        return;
+    }
+    s = *st;
+    if (k == 1 || s.pending == 1) s.fq = f;
+    else s.fp = f;
+    if (s.it < iters) {
+        if (s.fp < s.fq) {
+            s.b = s.q;
+            s.q = s.p;
+            s.fq = s.fp;
+            s.p = s.b - (s.b - s.a) * g;
+            s.pending = 0;
+            s.scale = (float)s.p;
+        } else {
+            s.a = s.p;
+            s.p = s.q;
+            s.fp = s.fq;
+            s.q = s.a + (s.b - s.a) * g;
+            s.pending = 1;
+            s.scale = (float)s.q;
+        }
+        ++s.it;
+    }
+    if (s.it == iters) s.scale = (float)((s.a + s.b) / 2.0);
+    *st = s;
+}
+
 // The pass-1 / traceback / pass-2 (/ traceback) chain over n tiles, batched so
 // that the backpointers of one batch fit the scratch bound.  With cost_only,
-// only the pass-2 path costs are produced (scale-search probes).
+// only the pass-2 path costs are produced (scale-search probes); with
+// scale_dev, the forward passes read the scale from device memory.
 int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, int K,
                  float scale, uint16_t *packed, uint16_t *states, float *sse, float *w_hat,
-                 float *cost_only) {
+                 float *cost_only, const float *scale_dev = nullptr) {
     if (n == 0) return EXL3_OK;
+    // the traceback dequantizes at the host's scale: a device scale is for
+    // path costs only
+    if (scale_dev && !cost_only) return fail(ctx, EXL3_EINVAL, "device scale without cost_only");
     int64_t batch = 0;
     int rc;
     if ((rc = admit_batch(ctx, n, K, &batch)) != EXL3_OK) return rc;
     if (cost_only && idx && batch == n && n > ctx->n_cu && n % ctx->n_cu != 0 &&
         n % ctx->n_cu <= ctx->n_cu / 8)
-        return probe_split(ctx, x, idx, n, K, scale, cost_only);
+        return probe_split(ctx, x, idx, n, K, scale, scale_dev, cost_only);
     for (int64_t i0 = 0; i0 < n; i0 += batch) {
         const int64_t nb = std::min<int64_t>(batch, n - i0);
         const int32_t *idx_b = idx ? idx + i0 : nullptr;
         int id = open_timed(ctx, EXL3_KERNEL_FWD1, nb);
         EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 1, x, idx_b, i0, nb, ctx->d_levels, scale,
-                                               nullptr, ctx->d_bp, ctx->d_end, nullptr,
+                                               scale_dev, nullptr, ctx->d_bp, ctx->d_end, nullptr,
                                                ctx->stream));
         close_timed(ctx, id);
         id = open_timed(ctx, EXL3_KERNEL_TB1, nb);
@@ -420,7 +481,7 @@ int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, i
         close_timed(ctx, id);
         id = open_timed(ctx, cost_only ? EXL3_KERNEL_FWD_COST : EXL3_KERNEL_FWD2, nb);
         EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, cost_only ? 3 : 2, x, idx_b, i0, nb,
-                                               ctx->d_levels, scale,
+                                               ctx->d_levels, scale, scale_dev,
                                                ctx->d_X, ctx->d_bp, nullptr,
                                                cost_only ? cost_only + i0 : ctx->d_cost,
                                                ctx->stream));
@@ -529,6 +590,7 @@ int exl3_ctx_create(exl3_ctx **out, int device, void *hip_stream, size_t scratch
     exl3::build_mul1_levels(lv.data());
     if (hipMalloc((void **)&ctx->d_levels, 65536 * sizeof(uint16_t)) != hipSuccess ||
         hipMalloc((void **)&ctx->d_flag, sizeof(int)) != hipSuccess ||
+        hipMalloc((void **)&ctx->d_gss, sizeof(GssDev)) != hipSuccess ||
         hipMemcpy(ctx->d_levels, lv.data(), 65536 * sizeof(uint16_t), hipMemcpyHostToDevice) !=
             hipSuccess) {
         (void)hipGetLastError();
@@ -553,7 +615,7 @@ void exl3_ctx_destroy(exl3_ctx *ctx) {
                     ctx->d_cost,        ctx->d_idx,         ctx->d_wreg,        ctx->d_sumsq,
                     ctx->d_sse,         ctx->d_flag,        ctx->d_err_tiles,   ctx->d_span_target,
                     ctx->d_span_what,   ctx->d_span_packed, ctx->d_gs,          ctx->d_x16,
-                    ctx->d_pk,          ctx->d_order};
+                    ctx->d_pk,          ctx->d_order,       ctx->d_gss};
     for (void *p : bufs)
         if (p) (void)hipFree(p);
     delete ctx;
@@ -842,11 +904,11 @@ int exl3_encode_tiles_noalloc(exl3_ctx *ctx, const float *x, int64_t n, int K, f
     float *d_cost = reinterpret_cast<float *>(d_X + kNoAllocBookTiles);
     hipStream_t s = ctx->stream;
     EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 1, x, nullptr, 0, n, ctx->d_levels, scale, nullptr,
-                                           bp, d_end, nullptr, s));
+                                           nullptr, bp, d_end, nullptr, s));
     EXL3_HIP(ctx, exl3::launch_traceback(K, 1, false, bp, n, d_end, d_X, nullptr, nullptr, 0,
                                          nullptr, 0.0f, nullptr, nullptr, nullptr, nullptr, s));
-    EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 2, x, nullptr, 0, n, ctx->d_levels, scale, d_X, bp,
-                                           nullptr, d_cost, s));
+    EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 2, x, nullptr, 0, n, ctx->d_levels, scale, nullptr,
+                                           d_X, bp, nullptr, d_cost, s));
     EXL3_HIP(ctx, exl3::launch_traceback(K, 2, false, bp, n, d_X, nullptr, x, nullptr, 0,
                                          ctx->d_levels, scale, packed, states, tile_sse, nullptr,
                                          s));
@@ -1091,10 +1153,34 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
                 *scale_chosen = (float)(mult * rms);
                 return EXL3_OK;
             }
-            auto objective = [&](double s) { return objective_on(s, 0, ns); };
             const double g = (std::sqrt(5.0) - 1.0) / 2.0;
             double a = gss->lo * rms, b = gss->hi * rms;
             double p = b - (b - a) * g, q = a + (b - a) * g;
+            if (!f16) {
+                // The whole search enqueued at once, no host round trip between
+                // probes: each probe after the first reads its scale from device
+                // memory, written by the search step before it (the result is
+                // read back once, at the end).  The last reduction's point is
+                // not scored (the result never reads it): iters + 1 probes.
+                const int probes = gss->iters >= 1 ? gss->iters + 1 : 2;
+                const float *scale_dev = &ctx->d_gss->scale;
+                for (int k = 0; k < probes; ++k) {
+                    if ((rc = encode_chain(ctx, ctx->d_wreg, ctx->d_idx, ns, K, (float)p, nullptr,
+                                           nullptr, nullptr, nullptr, ctx->d_sse,
+                                           k == 0 ? nullptr : scale_dev)) != EXL3_OK)
+                        return rc;
+                    hipLaunchKernelGGL(gss_step_kernel, dim3(1), dim3(64), 0, ctx->stream,
+                                       ctx->d_gss, ctx->d_sse, ns, a, b, p, q, g, gss->iters, k);
+                    EXL3_HIP(ctx, hipGetLastError());
+                }
+                float chosen = 0.0f;
+                EXL3_HIP(ctx, hipMemcpyAsync(&chosen, scale_dev, sizeof(float),
+                                             hipMemcpyDeviceToHost, ctx->stream));
+                EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+                *scale_chosen = chosen;
+                return EXL3_OK;
+            }
+            auto objective = [&](double s) { return objective_on(s, 0, ns); };
             // The result is the midpoint of the last bracket, which the last
             // reduction sets before its new point is scored: that score can
             // never be read, so it is not computed (iters + 1 probes in all).

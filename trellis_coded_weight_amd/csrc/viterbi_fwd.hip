@@ -488,8 +488,9 @@ template <int K, int PASS>
 __global__ void __launch_bounds__(kLanes, 1)
 viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile_idx,
                    int64_t tile0, const uint16_t *__restrict__ levels, float scale,
-                   const uint16_t *__restrict__ X_in, typename Geo<K>::bp_t *__restrict__ bp,
-                   uint16_t *__restrict__ end_state, float *__restrict__ cost_out) {
+                   const float *__restrict__ scale_dev, const uint16_t *__restrict__ X_in,
+                   typename Geo<K>::bp_t *__restrict__ bp, uint16_t *__restrict__ end_state,
+                   float *__restrict__ cost_out) {
     using G = Geo<K>;
     using bp_t = typename G::bp_t;
     constexpr bool SKEW = skewed<K, PASS>();
@@ -533,7 +534,9 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
     int b0;
     lane_butterflies<K>(g, m, b0);
 
-    // levels of the lane's 64 states, scaled once per pass
+    // levels of the lane's 64 states, scaled once per pass (the scale from
+    // device memory when given: a search that chooses it on the device)
+    if (scale_dev) scale = *scale_dev;
     Levels<K> lv;
 #pragma unroll
     for (int i = 0; i < G::GPL; ++i)
@@ -788,11 +791,12 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
 
 template <int K, int PASS>
 hipError_t launch_fwd_t(const float *x, const int32_t *tile_idx, int64_t tile0, int64_t n,
-                        const uint16_t *levels, float scale, const uint16_t *X_in, void *bp,
-                        uint16_t *end_state, float *cost_out, hipStream_t stream) {
+                        const uint16_t *levels, float scale, const float *scale_dev,
+                        const uint16_t *X_in, void *bp, uint16_t *end_state, float *cost_out,
+                        hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL((viterbi_fwd_kernel<K, PASS>), dim3((unsigned)n), dim3(kLanes), 0, stream,
-                       x, tile_idx, tile0, levels, scale, X_in,
+                       x, tile_idx, tile0, levels, scale, scale_dev, X_in,
                        reinterpret_cast<typename Geo<K>::bp_t *>(bp), end_state, cost_out);
     return hipGetLastError();
 }
@@ -801,16 +805,19 @@ hipError_t launch_fwd_t(const float *x, const int32_t *tile_idx, int64_t tile0, 
 
 hipError_t launch_viterbi_fwd(int K, int pass, const float *x, const int32_t *tile_idx,
                               int64_t tile0, int64_t n, const uint16_t *levels, float scale,
-                              const uint16_t *X_in, void *bp, uint16_t *end_state,
-                              float *cost_out, hipStream_t stream) {
+                              const float *scale_dev, const uint16_t *X_in, void *bp,
+                              uint16_t *end_state, float *cost_out, hipStream_t stream) {
 #define EXL3_FWD_CASE(KK)                                                                    \
     case KK:                                                                                 \
-        return pass == 1   ? launch_fwd_t<KK, 1>(x, tile_idx, tile0, n, levels, scale, X_in, bp, \
-                                                  end_state, cost_out, stream)                 \
-               : pass == 2 ? launch_fwd_t<KK, 2>(x, tile_idx, tile0, n, levels, scale, X_in, bp, \
-                                                  end_state, cost_out, stream)                 \
-                           : launch_fwd_t<KK, 3>(x, tile_idx, tile0, n, levels, scale, X_in, bp, \
-                                                  end_state, cost_out, stream);
+        return pass == 1   ? launch_fwd_t<KK, 1>(x, tile_idx, tile0, n, levels, scale,       \
+                                                  scale_dev, X_in, bp, end_state, cost_out,  \
+                                                  stream)                                    \
+               : pass == 2 ? launch_fwd_t<KK, 2>(x, tile_idx, tile0, n, levels, scale,       \
+                                                  scale_dev, X_in, bp, end_state, cost_out,  \
+                                                  stream)                                    \
+                           : launch_fwd_t<KK, 3>(x, tile_idx, tile0, n, levels, scale,       \
+                                                  scale_dev, X_in, bp, end_state, cost_out,  \
+                                                  stream);
     switch (K) {
         EXL3_FWD_CASE(1)
         EXL3_FWD_CASE(2)
