@@ -78,10 +78,15 @@ def _spread_rows(rows, cols, seed, bf16):
                             128, 2, None)
 
 
+# bf16 rows of up to 16 chunks of 64 blocks take the resident-band kernel (up
+# to 8 chunks, or up to 16), longer ones and binary32 rows the chunked one
 @pytest.mark.parametrize("rows,cols,bf16", [
     (48, 1024, False),          # three whole bands, whole chunks
-    (33, 2056, True),           # ragged band, a last chunk of one block
+    (33, 2056, True),           # ragged band, a last chunk of one block (band, 8 chunks)
     (17, 4100, False),          # ragged band and chunk
+    (12, 8192, True),           # band kernel, 16 whole chunks
+    (9, 6000, True),            # band kernel, 16-chunk form, ragged last chunk and band
+    (5, 8200, True),            # 17 chunks: the chunked kernel
 ])
 def test_channel_normalize_rounding_rows(ctx, rows, cols, bf16):
     print("\nchannel_normalize rounding rows %dx%d bf16=%s" % (rows, cols, bf16), flush=True)

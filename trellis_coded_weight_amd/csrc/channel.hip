@@ -11,11 +11,13 @@
 // The binary64 square of a binary32 value is exact, so only the additions
 // round, in column order.
 //
-// Both kernels below use one workgroup per band of rows (16 in the general
-// form, 4 in the fast one), in which one lane per row adds its row's squares in
-// column order (the general form one at a time: a chain of `cols` dependent
-// binary64 additions; the fast form a group of squares at a time where that is
-// provably exact, see below).  A second sweep writes the scaled rows.
+// Three forms, one workgroup per band of rows each: the general one (16 rows,
+// any shape) adds a row's squares one at a time in column order, a chain of
+// `cols` dependent binary64 additions; the chunked one (4 rows, rows of whole
+// 16-byte blocks) adds a group of squares at a time where that is provably
+// exact (see below); both then sweep the band again for the scaled rows.  The
+// resident-row one (bf16 rows of up to 16 chunks) keeps each row in its wave's
+// registers, so it reads the input once, and tests a row's groups in parallel.
 #include "exl3.h"
 #include "exl3_internal.h"
 
@@ -162,6 +164,35 @@ __device__ __forceinline__ void unpack_block(const uint4 &u, float (&v)[16 / siz
     }
 }
 
+// The shortcut's inputs for one 16-byte block: the sum of its squares (exact
+// binary64 squares, added in a tree) and, in m, the exponent of a lower bound on
+// the lowest set bit of its values (kBig: all zero; -kBig: a NaN or infinity).
+template <typename Tin>
+__device__ __forceinline__ double block_summary(const uint4 &u, int &m) {
+    constexpr int EPL = 16 / sizeof(Tin);                  // elements per 16-byte block
+    constexpr int kSig = sizeof(Tin) == 2 ? 8 : 24;        // significant bits of the input
+    float v[EPL];
+    unpack_block<Tin>(u, v);
+    uint32_t emin = 0x1FFu;                                // smallest exponent field of a nonzero value
+    bool bad = false;
+    double sq[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const uint32_t bits = __float_as_uint(v[e]);
+        const uint32_t ex = (bits >> 23) & 0xFFu;
+        bad = bad | (ex == 0xFFu);
+        emin = min(emin, (bits & 0x7FFFFFFFu) ? max(ex, 1u) : 0x1FFu);
+        const double d = (double)v[e];
+        sq[e] = d * d;                                     // exact in binary64
+    }
+#pragma unroll
+    for (int h = 1; h < EPL; h <<= 1)
+#pragma unroll
+        for (int e = 0; e < EPL; e += 2 * h) sq[e] = sq[e] + sq[e + h];
+    m = bad ? -kBig : emin == 0x1FFu ? kBig : (int)emin - 127 - (kSig - 1);
+    return sq[0];
+}
+
 template <typename Tin>
 __global__ void __launch_bounds__(kFastLanes)
 channel_normalize_kernel(const Tin *__restrict__ w, int rows, int cols,
@@ -169,7 +200,6 @@ channel_normalize_kernel(const Tin *__restrict__ w, int rows, int cols,
                          float *__restrict__ w_norm, float *__restrict__ su_folded,
                          double *__restrict__ row_rms) {
     constexpr int EPL = 16 / sizeof(Tin);                  // elements per 16-byte block
-    constexpr int kSig = sizeof(Tin) == 2 ? 8 : 24;        // significant bits of the input
     __shared__ double ring_sum[2][kFastRows][kRingStride];
     __shared__ double ring_bound[2][kFastRows][kRingStride];
     __shared__ uint4 ring_raw[2][kFastRows][kRingStride];
@@ -193,27 +223,10 @@ channel_normalize_kernel(const Tin *__restrict__ w, int rows, int cols,
     };
     auto store = [&](int k, const uint4 &src) {
         const bool valid = r < nr && k < nchunk && k * kChunkBlocks + b < nblk;
-        float v[EPL];
-        unpack_block<Tin>(src, v);
-        uint32_t emin = 0x1FFu;                            // smallest exponent field of a nonzero value
-        bool bad = false;
-        double sq[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const uint32_t bits = __float_as_uint(v[e]);
-            const uint32_t ex = (bits >> 23) & 0xFFu;
-            bad = bad | (ex == 0xFFu);
-            emin = min(emin, (bits & 0x7FFFFFFFu) ? max(ex, 1u) : 0x1FFu);
-            const double d = (double)v[e];
-            sq[e] = d * d;                                 // exact in binary64
-        }
-#pragma unroll
-        for (int h = 1; h < EPL; h <<= 1)
-#pragma unroll
-            for (int e = 0; e < EPL; e += 2 * h) sq[e] = sq[e] + sq[e + h];
-        int m = bad ? -kBig : emin == 0x1FFu ? kBig : (int)emin - 127 - (kSig - 1);
+        int m;
+        const double s_blk = block_summary<Tin>(src, m);
         if (!valid) m = kBig;
-        const double s0 = valid ? sq[0] : 0.0;
+        const double s0 = valid ? s_blk : 0.0;
         int mg = m;
         double sg = s0;
 #pragma unroll
@@ -327,6 +340,207 @@ channel_normalize_kernel(const Tin *__restrict__ w, int rows, int cols,
     }
 }
 
+// The resident-row form, for bf16 rows of at most NCH chunks of 64 blocks
+// (the rows whose shortcut groups nearly always pass; binary32 rows, whose
+// groups fail, keep the form above).  Wave r of the workgroup owns row r of
+// the band from start to end: its lanes load all of the row's blocks at once
+// and keep them in registers for the scaled row, so the input is read once,
+// and store them with the groups' summaries in LDS; the wave then tests the
+// row's groups in parallel (see there) and writes the scaled row.  The waves
+// share nothing, so a row is written as soon as its own sum is known.  A group
+// that fails is taken block by block, each block's summary recomputed from LDS
+// by the same code as the loaders', a failing block one square at a time.
+template <typename Tin, int NCH>
+__global__ void __launch_bounds__(kFastLanes)
+channel_normalize_band_kernel(const Tin *__restrict__ w, int rows, int cols,
+                              const float *__restrict__ su, double floor_value,
+                              float *__restrict__ w_norm, float *__restrict__ su_folded,
+                              double *__restrict__ row_rms) {
+    constexpr int EPL = 16 / sizeof(Tin);                  // elements per 16-byte block
+    constexpr int NB = NCH * kChunkBlocks;                 // blocks per row at most
+    __shared__ uint4 raw[kFastRows][NB];
+    __shared__ double2 grp[kFastRows][NB / kGroup];        // group sum, group bound
+    const int t = threadIdx.x;
+    const int row0 = blockIdx.x * kFastRows;
+    const int nr = min(kFastRows, rows - row0);
+    const int nblk = cols / EPL;                           // blocks per row (<= NB)
+    // wave r, lane b: blocks k * 64 + b of row r; eight consecutive lanes hold
+    // the blocks of a group
+    const int r = t / kChunkBlocks, b = t % kChunkBlocks;
+    if (r >= nr) return;                                   // past the last row (whole waves)
+    const Tin *wr = w + (size_t)(row0 + r) * cols;
+
+    // every load of the lane at once (past the row: its last block, unused)
+    uint4 u[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int bl = min(k * kChunkBlocks + b, nblk - 1);
+        u[k] = *reinterpret_cast<const uint4 *>(wr + (size_t)bl * EPL);
+    }
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int kb = k * kChunkBlocks + b;
+        const bool valid = kb < nblk;
+        int m;
+        const double s_blk = block_summary<Tin>(u[k], m);
+        if (!valid) m = kBig;
+        const double s0 = valid ? s_blk : 0.0;
+        int mg = m;
+        double sg = s0;
+#pragma unroll
+        for (int x = 1; x < kGroup; x <<= 1) {
+            mg = min(mg, __shfl_xor(mg, x));
+            sg = sg + __shfl_xor(sg, x);
+        }
+        if (valid) {
+            raw[r][kb] = u[k];
+            if (b % kGroup == 0) grp[r][kb / kGroup] = make_double2(sg, square_bound(mg));
+        }
+    }
+    // the row's LDS entries are the wave's own: its stores are done before its
+    // reads (no other wave is waited for)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+    // the rows' sums: wave r takes row r.  A run of groups s..j that all pass
+    // the shortcut is exact whatever the order of its additions (the argument
+    // above, for the run as one group), so the wave scans the run at once: lane
+    // l holds groups l + 64 q, prefix sums P_j = x + sum and prefix bounds
+    // min(g, bounds) over 64 lanes, and a ballot of the tests finds the first
+    // group the column-order chain would fail (the test's outcome does not
+    // depend on the order of the additions either).  Everything before it is
+    // added, the failing group is taken block by block, and the scan resumes
+    // after it.  The state (x, g) is the column-order chain's, bit for bit.
+    float f_row;
+    {
+        constexpr int GQ = NB / kGroup / 64;               // groups per lane
+        const int lane = t & 63;
+        const int ngr = (nblk + kGroup - 1) / kGroup;
+        double2 gq[GQ];
+#pragma unroll
+        for (int q = 0; q < GQ; ++q) gq[q] = grp[r][lane + 64 * q];
+        double x = 0.0;
+        double g = INFINITY;                       // 2^53 x the lower bound on x's lowest set bit
+        int s0 = 0;                                // first group not yet added
+        while (s0 < ngr) {
+            double carry = x, mcarry = g;
+            int f = ngr;                           // first failing group (ngr: none)
+            double x_f = x, g_f = g;               // the state just before it
+#pragma unroll
+            for (int q = 0; q < GQ; ++q) {
+                const int j = lane + 64 * q;
+                const bool in = j >= s0 && j < ngr;
+                double v = in ? gq[q].x : 0.0;
+                double m = in ? gq[q].y : (double)INFINITY;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const double vu = __shfl_up(v, d), mu = __shfl_up(m, d);
+                    if (lane >= d) {
+                        v = vu + v;
+                        m = mu < m ? mu : m;
+                    }
+                }
+                const double P = carry + v;
+                const double M = mcarry < m ? mcarry : m;
+                const uint64_t fails = __ballot(in && !(P < M));
+                if (f == ngr && fails) {
+                    const int lf = __builtin_ctzll(fails);
+                    f = lf + 64 * q;
+                    // the state after group f - 1 (or the run's start)
+                    const double Pp = __shfl(P, lf > 0 ? lf - 1 : 0);
+                    const double Mp = __shfl(M, lf > 0 ? lf - 1 : 0);
+                    x_f = f > s0 ? (lf > 0 ? Pp : carry) : x;
+                    g_f = f > s0 ? (lf > 0 ? Mp : mcarry) : g;
+                }
+                carry = __shfl(P, 63);
+                mcarry = __shfl(M, 63);
+            }
+            if (f == ngr) {                        // every remaining group passed
+                x = carry;
+                g = mcarry;
+                break;
+            }
+            // group f again from its start, a block at a time, by the same rule
+            // one level down: lanes 0..7 (and their copies in every eight
+            // lanes) recompute the group's block summaries from LDS, a scan
+            // adds each run of passing blocks and finds the first failing one,
+            // which is added one square at a time (all lanes alike)
+            x = x_f;
+            g = g_f;
+            const int b0 = f * kGroup, ng = min(kGroup, nblk - b0);
+            const int li = lane & (kGroup - 1);
+            int mb;
+            const double S = block_summary<Tin>(raw[r][b0 + min(li, ng - 1)], mb);
+            const double B = square_bound(mb);
+            int i0 = 0;
+            while (i0 < ng) {
+                const bool in = li >= i0 && li < ng;
+                double v = in ? S : 0.0;
+                double m = in ? B : (double)INFINITY;
+#pragma unroll
+                for (int d = 1; d < kGroup; d <<= 1) {
+                    const double vu = __shfl_up(v, d, kGroup), mu = __shfl_up(m, d, kGroup);
+                    if (li >= d) {
+                        v = vu + v;
+                        m = mu < m ? mu : m;
+                    }
+                }
+                const double P = x + v;
+                const double M = g < m ? g : m;
+                const uint64_t fails = __ballot(in && !(P < M)) & ((1ull << kGroup) - 1);
+                if (!fails) {                      // the rest of the group passed
+                    x = __shfl(P, ng - 1);
+                    g = __shfl(M, ng - 1);
+                    break;
+                }
+                const int lf = __builtin_ctzll(fails);
+                // the failing block's bound joins g first, as in the column-order
+                // chain; then its squares one at a time
+                const double Pp = __shfl(P, lf > 0 ? lf - 1 : 0);
+                x = lf > i0 ? Pp : x;
+                g = __shfl(M, lf);
+                float vv[EPL];
+                unpack_block<Tin>(raw[r][b0 + lf], vv);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    const double d = (double)vv[e];
+                    x = x + d * d;
+                }
+                // x is now a multiple of its unit in the last place: that alone
+                // bounds its lowest set bit
+                g = x > 0.0 ? next_binade(x) : g;
+                i0 = lf + 1;
+            }
+            s0 = f + 1;
+        }
+        const double rr = sqrt(x / (double)cols);
+        const double r_eff = rr == 0.0 ? floor_value : rr;
+        f_row = (float)(1.0 / r_eff);
+        if (lane == 0) {
+            const int i = row0 + r;
+            su_folded[i] = rr == 0.0 ? 0.0f : su[i] * (float)rr;
+            if (row_rms) row_rms[i] = rr;
+        }
+    }
+
+    // the scaled row from the registers, 16-byte stores
+    {
+        const float f = f_row;
+        float *dst = w_norm + (size_t)(row0 + r) * cols;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int kb = k * kChunkBlocks + b;
+            if (kb < nblk) {
+                float v[EPL];
+                unpack_block<Tin>(u[k], v);
+#pragma unroll
+                for (int e = 0; e < EPL; e += 4)
+                    *reinterpret_cast<float4 *>(dst + (size_t)kb * EPL + e) =
+                        make_float4(v[e] * f, v[e + 1] * f, v[e + 2] * f, v[e + 3] * f);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_channel_normalize(const void *w, int w_dtype, int rows, int cols,
@@ -341,7 +555,17 @@ hipError_t launch_channel_normalize(const void *w, int w_dtype, int rows, int co
                       ((size_t)cols * in_bytes) % 16 == 0 && ((size_t)cols * 4) % 16 == 0;
     if (w_dtype == EXL3_BF16) {
         const uint16_t *wb = static_cast<const uint16_t *>(w);
-        if (fast)
+        const int nchunk = (cols / 8 + kChunkBlocks - 1) / kChunkBlocks;
+        if (fast && nchunk <= 16) {
+            if (nchunk <= 8)
+                hipLaunchKernelGGL((channel_normalize_band_kernel<uint16_t, 8>), dim3(fast_blocks),
+                                   dim3(kFastLanes), 0, stream, wb, rows, cols, su, floor_value,
+                                   w_norm, su_folded, row_rms);
+            else
+                hipLaunchKernelGGL((channel_normalize_band_kernel<uint16_t, 16>),
+                                   dim3(fast_blocks), dim3(kFastLanes), 0, stream, wb, rows, cols,
+                                   su, floor_value, w_norm, su_folded, row_rms);
+        } else if (fast)
             hipLaunchKernelGGL(channel_normalize_kernel<uint16_t>, dim3(fast_blocks), dim3(kFastLanes), 0,
                                stream, wb, rows, cols, su, floor_value, w_norm, su_folded,
                                row_rms);
