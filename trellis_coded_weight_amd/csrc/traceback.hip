@@ -145,16 +145,28 @@ traceback2_kernel(const typename Geo<K>::bp_t *__restrict__ bp, int64_t n,
 // that holds the true hypothesis.  Under h the state at step t-d is
 //     (h << (16 - K d)) | (S_t >> (K d)),
 // since each step shifts K bits out at the bottom and the backpointer in at
-// the top.  Look-ahead depth D: the largest with 1 + 2^K + ... + 2^(K(D-1))
-// <= 64 lanes.
-template <int K>
+// the top.  In the binary32 layout at K = 1 and 2 the top W bits of a state
+// (W = 4 and 2: its butterfly's index among the lane's) only choose the field
+// within the word, not the word, so hypotheses that differ only there share
+// one load: depth d needs 2^max(0, K d - W) words, and the lanes load whole
+// words, the resolution taking the field of the true state.  Look-ahead depth
+// D: the largest whose words fit in 64 lanes (K = 1 / 2 / 3 / 4: 9 / 4 / 2 / 2
+// in the binary32 layout, 6 / 3 / 2 / 2 in the binary16 one).
+template <int K, bool H>
 struct Look {
-    static constexpr int D = (K == 1) ? 6 : (K == 2) ? 3 : 2;
+    static constexpr int W = H ? 0 : K == 1 ? 4 : K == 2 ? 2 : 0;
+    static constexpr int bits(int d) { return K * d - W > 0 ? K * d - W : 0; }
     static constexpr int offset(int d) {   // first lane of depth d
         int off = 0;
-        for (int i = 0; i < d; ++i) off += 1 << (K * i);
+        for (int i = 0; i < d; ++i) off += 1 << bits(i);
         return off;
     }
+    static constexpr int depth() {
+        int d = 0;
+        while (offset(d + 1) <= 64) ++d;
+        return d;
+    }
+    static constexpr int D = depth();
 };
 
 // Walk `count` transitions back from state s: the first reads slot `slot0`,
@@ -165,16 +177,17 @@ template <int K, bool H>
 __device__ uint32_t walk_wave(const typename Geo<K>::bp_t *__restrict__ bp_tile, uint32_t s,
                               int slot0, int count, uint16_t *S, int pos0) {
     using G = Geo<K>;
-    using L = Look<K>;
+    using L = Look<K, H>;
     constexpr int D = L::D;
     const int lane = threadIdx.x & 63;
-    // this lane's depth and hypothesis bits (lanes past the last depth stay idle)
+    // this lane's depth and the hypothesis bits that choose its word (lanes
+    // past the last depth stay idle)
     int d = -1;
     uint32_t hs = 0;
 #pragma unroll
     for (int i = 0; i < D; ++i) {
         const int off = L::offset(i);
-        if (lane >= off && lane < off + (1 << (K * i))) {
+        if (lane >= off && lane < off + (1 << L::bits(i))) {
             d = i;
             hs = i == 0 ? 0u : (uint32_t)(lane - off) << (16 - K * i);
         }
@@ -186,14 +199,27 @@ __device__ uint32_t walk_wave(const typename Geo<K>::bp_t *__restrict__ bp_tile,
         uint32_t val = 0;
         if (d >= 0 && d < r) {
             const uint32_t st = hs | (s >> shift);              // state at step t - d
-            val = bp_read<K, H>(bp_tile, slot0 - done - d, st >> K);
+            if constexpr (L::W > 0) {
+                // the whole word (the binary32 layout)
+                uint32_t wl, wb;
+                bp_locate<K>(st >> K, wl, wb);
+                val = bp_tile[(size_t)(slot0 - done - d) * kLanes + wl];
+            } else {
+                val = bp_read<K, H>(bp_tile, slot0 - done - d, st >> K);
+            }
         }
         uint32_t hyp = 0;
 #pragma unroll
         for (int i = 0; i < D; ++i) {
             if (i < r) {
-                const uint32_t k =
-                    (uint32_t)__builtin_amdgcn_readlane((int)val, L::offset(i) + (int)hyp);
+                const int src = L::offset(i) + (int)(hyp & ((1u << L::bits(i)) - 1u));
+                uint32_t k = (uint32_t)__builtin_amdgcn_readlane((int)val, src);
+                if constexpr (L::W > 0) {
+                    // the field of the true state at step t - i (s, by now)
+                    uint32_t wl, wb;
+                    bp_locate<K>(s >> K, wl, wb);
+                    k = (k >> wb) & ((1u << K) - 1u);
+                }
                 s = (k << G::Kr) | (s >> K);
                 if (S && lane == 0) S[pos0 - 1 - done - i] = (uint16_t)s;
                 hyp |= k << (K * i);
