@@ -191,6 +191,23 @@ def test_small_matrix_with_scale_search(ctx, K):
     assert got["mse"] == want["mse"]
 
 
+# the scale search runs on the device (one search step per probe): other
+# reduction counts and brackets, down to a single reduction, against the
+# oracle's golden section
+@pytest.mark.parametrize("gss", [(1, 0.5, 2.0), (2, 0.5, 2.0), (3, 0.25, 4.0), (7, 0.9, 1.1)])
+def test_scale_search_reductions_and_brackets(ctx, gss):
+    m = workloads.gaussian(128, 256, 0.02, 81, 82, K=2)
+    print("\nscale search gss=%s" % (gss,), flush=True)
+    want = oracle.quantize_matrix(m.w, m.su, m.sv, 2, had_block=128, gss=gss)
+    got = ctx.quantize_matrix(torch.from_numpy(m.w).to(torch.bfloat16).to(DEV), 2,
+                              torch.from_numpy(m.su).to(DEV), torch.from_numpy(m.sv).to(DEV),
+                              had_block=128, gss=gss, want_tile_sse=True)
+    assert np.float32(got["scale"]) == want["scale"]
+    assert np.array_equal(_u16(got["packed"]).reshape(-1, 32), want["packed"])
+    assert np.array_equal(_bits(got["tile_sse"].cpu().numpy()), _bits(want["sse"]))
+    assert got["mse"] == want["mse"]
+
+
 def test_module_level_quantize_matrix_tuple():
     """trellis_coded_weight_amd.quantize_matrix returns (packed, scale, mse) of the
     same search as the oracle's (a context per device kept for the process)."""
