@@ -77,6 +77,12 @@ struct exl3_ctx {
     size_t sse_cap = 0;
     int *d_flag = nullptr;
     GssDev *d_gss = nullptr;
+    // pinned host staging for the read-backs (sign checks, tile energies, the
+    // chosen scale, per-tile errors): a copy into it is a DMA queued behind the
+    // work on the stream, where a pageable destination is staged by the
+    // runtime only once the stream has drained
+    void *h_pin = nullptr;
+    size_t pin_cap = 0;
     // LDLQ: error of the quantized spans (tile-major), one span's target,
     // dequantized values and container words
     float *d_err_tiles = nullptr;
@@ -533,15 +539,57 @@ int encode_chain_f16(exl3_ctx *ctx, const uint16_t *x, int64_t n, int K, uint16_
     return EXL3_OK;
 }
 
-// Sign vectors must hold exactly +1 or -1 (copied to the host to check).
-int check_signs(exl3_ctx *ctx, const float *d, int n, const char *name) {
-    std::vector<float> h((size_t)n);
-    EXL3_HIP(ctx, hipMemcpyAsync(h.data(), d, (size_t)n * sizeof(float), hipMemcpyDeviceToHost,
-                                 ctx->stream));
+// The pinned staging buffer, at least `bytes` long (the stream is idle when
+// it is replaced: every use synchronizes before reading it).
+int pinned(exl3_ctx *ctx, size_t bytes, void **out) {
+    if (bytes > ctx->pin_cap) {
+        if (ctx->h_pin) {
+            EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+            (void)hipHostFree(ctx->h_pin);
+            ctx->h_pin = nullptr;
+            ctx->pin_cap = 0;
+        }
+        const size_t cap = std::max<size_t>(bytes, 1 << 20);
+        EXL3_HIP(ctx, hipHostMalloc(&ctx->h_pin, cap, hipHostMallocDefault));
+        ctx->pin_cap = cap;
+    }
+    *out = ctx->h_pin;
+    return EXL3_OK;
+}
+
+// Device-to-host read-backs of up to two arrays through the pinned buffer, one
+// synchronization; returns the host copies (valid until the next read-back).
+int read_back(exl3_ctx *ctx, const void *d0, size_t b0, const void *d1, size_t b1,
+              const void **h0, const void **h1 = nullptr) {
+    const size_t off1 = (b0 + 255) / 256 * 256;
+    void *h;
+    int rc;
+    if ((rc = pinned(ctx, off1 + b1, &h)) != EXL3_OK) return rc;
+    char *hc = static_cast<char *>(h);
+    if (b0) EXL3_HIP(ctx, hipMemcpyAsync(hc, d0, b0, hipMemcpyDeviceToHost, ctx->stream));
+    if (b1) EXL3_HIP(ctx, hipMemcpyAsync(hc + off1, d1, b1, hipMemcpyDeviceToHost, ctx->stream));
     EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
-    for (int i = 0; i < n; ++i)
-        if (h[i] != 1.0f && h[i] != -1.0f)
-            return fail(ctx, EXL3_EINVAL, "%s[%d] = %g is not +1 or -1", name, i, (double)h[i]);
+    *h0 = hc;
+    if (h1) *h1 = hc + off1;
+    return EXL3_OK;
+}
+
+// Sign vectors must hold exactly +1 or -1 (copied to the host to check, both
+// with one synchronization; d1 may be null).
+int check_signs(exl3_ctx *ctx, const float *d0, int n0, const char *name0,
+                const float *d1 = nullptr, int n1 = 0, const char *name1 = nullptr) {
+    const void *p0, *p1;
+    int rc;
+    if ((rc = read_back(ctx, d0, (size_t)n0 * sizeof(float), d1,
+                        d1 ? (size_t)n1 * sizeof(float) : 0, &p0, &p1)) != EXL3_OK)
+        return rc;
+    const float *h0 = static_cast<const float *>(p0), *h1 = static_cast<const float *>(p1);
+    for (int i = 0; i < n0; ++i)
+        if (h0[i] != 1.0f && h0[i] != -1.0f)
+            return fail(ctx, EXL3_EINVAL, "%s[%d] = %g is not +1 or -1", name0, i, (double)h0[i]);
+    for (int i = 0; d1 && i < n1; ++i)
+        if (h1[i] != 1.0f && h1[i] != -1.0f)
+            return fail(ctx, EXL3_EINVAL, "%s[%d] = %g is not +1 or -1", name1, i, (double)h1[i]);
     return EXL3_OK;
 }
 
@@ -611,6 +659,7 @@ void exl3_ctx_destroy(exl3_ctx *ctx) {
     if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
     if (ctx->ev_switch) (void)hipEventDestroy(ctx->ev_switch);
     if (ctx->aux) (void)hipStreamDestroy(ctx->aux);
+    if (ctx->h_pin) (void)hipHostFree(ctx->h_pin);
     void *bufs[] = {ctx->d_levels,      ctx->d_bp,          ctx->d_end,         ctx->d_X,
                     ctx->d_cost,        ctx->d_idx,         ctx->d_wreg,        ctx->d_sumsq,
                     ctx->d_sse,         ctx->d_flag,        ctx->d_err_tiles,   ctx->d_span_target,
@@ -1037,8 +1086,7 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
             return rc;
     }
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
-    if ((rc = check_signs(ctx, su, rows, "su")) != EXL3_OK) return rc;
-    if ((rc = check_signs(ctx, sv, cols, "sv")) != EXL3_OK) return rc;
+    if ((rc = check_signs(ctx, su, rows, "su", sv, cols, "sv")) != EXL3_OK) return rc;
 
     const int TR = rows / 16, TC = cols / 16;
     const int64_t ntiles = (int64_t)TR * TC;
@@ -1053,18 +1101,18 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
                                           EXL3_TILE_MAJOR, ctx->d_sumsq, ctx->d_flag,
                                           tile_order(ctx), ctx->stream));
     close_timed(ctx, reg_id);
-    std::vector<float> sumsq((size_t)ntiles);
-    int flag = 0;
-    EXL3_HIP(ctx, hipMemcpyAsync(sumsq.data(), ctx->d_sumsq, (size_t)ntiles * sizeof(float),
-                                 hipMemcpyDeviceToHost, ctx->stream));
-    EXL3_HIP(ctx, hipMemcpyAsync(&flag, ctx->d_flag, sizeof(int), hipMemcpyDeviceToHost,
-                                 ctx->stream));
-    EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
-    if (flag) return fail(ctx, EXL3_ENONFINITE, "weight matrix holds NaN or Inf");
+    const void *p_sumsq, *p_flag;
+    if ((rc = read_back(ctx, ctx->d_sumsq, (size_t)ntiles * sizeof(float), ctx->d_flag,
+                        sizeof(int), &p_sumsq, &p_flag)) != EXL3_OK)
+        return rc;
+    if (*static_cast<const int *>(p_flag))
+        return fail(ctx, EXL3_ENONFINITE, "weight matrix holds NaN or Inf");
+    // read in place: the next read-back (the chosen scale) comes after its last use
+    const float *sumsq = static_cast<const float *>(p_sumsq);
 
     // 2. rms in binary64, ascending tile order
     double total = 0.0;
-    for (int64_t i = 0; i < ntiles; ++i) total += (double)sumsq[(size_t)i];
+    for (int64_t i = 0; i < ntiles; ++i) total += (double)sumsq[i];
     const double rms = std::sqrt(total / (double)nel);
 
     // 3. scale
@@ -1079,8 +1127,8 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
                 pick.insert((int64_t)(i % TR) * TC + (i % TC));
             int64_t imax = 0, imin = 0;
             for (int64_t i = 1; i < ntiles; ++i) {
-                if (sumsq[(size_t)i] > sumsq[(size_t)imax]) imax = i;
-                if (sumsq[(size_t)i] < sumsq[(size_t)imin]) imin = i;
+                if (sumsq[i] > sumsq[imax]) imax = i;
+                if (sumsq[i] < sumsq[imin]) imin = i;
             }
             pick.insert(imax);
             pick.insert(imin);
@@ -1173,11 +1221,11 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
                                        ctx->d_gss, ctx->d_sse, ns, a, b, p, q, g, gss->iters, k);
                     EXL3_HIP(ctx, hipGetLastError());
                 }
-                float chosen = 0.0f;
-                EXL3_HIP(ctx, hipMemcpyAsync(&chosen, scale_dev, sizeof(float),
-                                             hipMemcpyDeviceToHost, ctx->stream));
-                EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
-                *scale_chosen = chosen;
+                const void *p_scale;
+                if ((rc = read_back(ctx, scale_dev, sizeof(float), nullptr, 0, &p_scale)) !=
+                    EXL3_OK)
+                    return rc;
+                *scale_chosen = *static_cast<const float *>(p_scale);
                 return EXL3_OK;
             }
             auto objective = [&](double s) { return objective_on(s, 0, ns); };
@@ -1227,12 +1275,13 @@ int encode_whole_matrix(exl3_ctx *ctx, int rows, int cols, int K, float scale, u
                            w_hat, nullptr)) != EXL3_OK)
         return rc;
     if (mse_out) {
-        std::vector<float> sse((size_t)ntiles);
-        EXL3_HIP(ctx, hipMemcpyAsync(sse.data(), sse_dev, (size_t)ntiles * sizeof(float),
-                                     hipMemcpyDeviceToHost, ctx->stream));
-        EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+        const void *p;
+        if ((rc = read_back(ctx, sse_dev, (size_t)ntiles * sizeof(float), nullptr, 0, &p)) !=
+            EXL3_OK)
+            return rc;
+        const float *sse = static_cast<const float *>(p);
         double tot = 0.0;
-        for (int64_t i = 0; i < ntiles; ++i) tot += (double)sse[(size_t)i];
+        for (int64_t i = 0; i < ntiles; ++i) tot += (double)sse[i];
         *mse_out = tot / (double)nel;
     }
     EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
@@ -1295,13 +1344,14 @@ int exl3_quantize_matrix_f16(exl3_ctx *ctx, const void *w, int w_dtype, int rows
     if ((rc = encode_chain_f16(ctx, ctx->d_x16, ntiles, K, packed, nullptr, nullptr, ctx->d_wreg,
                                scale, sse_dev, w_hat)) != EXL3_OK)
         return rc;
-    std::vector<float> sse((size_t)ntiles);
-    EXL3_HIP(ctx, hipMemcpyAsync(sse.data(), sse_dev, (size_t)ntiles * sizeof(float),
-                                 hipMemcpyDeviceToHost, ctx->stream));
-    EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    const void *p_sse;
+    if ((rc = read_back(ctx, sse_dev, (size_t)ntiles * sizeof(float), nullptr, 0, &p_sse)) !=
+        EXL3_OK)
+        return rc;
+    const float *sse = static_cast<const float *>(p_sse);
     if (mse_out) {
         double tot = 0.0;
-        for (int64_t i = 0; i < ntiles; ++i) tot += (double)sse[(size_t)i];
+        for (int64_t i = 0; i < ntiles; ++i) tot += (double)sse[i];
         *mse_out = tot / (double)nel;
     }
     *scale_out = scale;
@@ -1349,12 +1399,13 @@ int exl3_quantize_matrix_ldlq(exl3_ctx *ctx, const void *w, int w_dtype, int row
                                                err_dev, ctx->stream));
     }
     if (mse_out) {
-        std::vector<float> err((size_t)ntiles);
-        EXL3_HIP(ctx, hipMemcpyAsync(err.data(), err_dev, (size_t)ntiles * sizeof(float),
-                                     hipMemcpyDeviceToHost, ctx->stream));
-        EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
+        const void *p_err;
+        if ((rc = read_back(ctx, err_dev, (size_t)ntiles * sizeof(float), nullptr, 0, &p_err)) !=
+            EXL3_OK)
+            return rc;
+        const float *err = static_cast<const float *>(p_err);
         double tot = 0.0;
-        for (int64_t i = 0; i < ntiles; ++i) tot += (double)err[(size_t)i];
+        for (int64_t i = 0; i < ntiles; ++i) tot += (double)err[i];
         *mse_out = tot / (double)nel;
     }
     EXL3_HIP(ctx, hipStreamSynchronize(ctx->stream));
