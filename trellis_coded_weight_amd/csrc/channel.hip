@@ -340,6 +340,53 @@ channel_normalize_kernel(const Tin *__restrict__ w, int rows, int cols,
     }
 }
 
+// Lane exchanges of the resident-row form inside a wave without the LDS
+// crossbar: DPP row operations (lane i of each row of 16 reads lane i - n of
+// its row, row_shr:n; rows 1 and 3, or 2 and 3, read lane 15 or 31,
+// row_bcast:15 / :31), lanes without a source keeping `id`, and readlane.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v, double id) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v), i = (uint64_t)__double_as_longlong(id);
+    const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)i, (int)(uint32_t)u, CTRL, ROW_MASK,
+                                               0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(i >> 32), (int)(uint32_t)(u >> 32),
+                                               CTRL, ROW_MASK, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v, int id) {
+    return __builtin_amdgcn_update_dpp(id, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ double lane_f64(double v, int l) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const int hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+// Inclusive scans (sum; minimum) over lanes 0..L-1 of each group of L lanes
+// (L = 8 or 64; for L = 8 only lanes 0..7 are exact, the other groups mixing
+// with their neighbours, which their callers do not read).
+template <int L>
+__device__ __forceinline__ void scan_sum_min(double &v, double &m) {
+    const double inf = (double)INFINITY;
+    v = dpp_f64<kRowShr1, 0xF>(v, 0.0) + v;
+    m = fmin(dpp_f64<kRowShr1, 0xF>(m, inf), m);
+    v = dpp_f64<kRowShr2, 0xF>(v, 0.0) + v;
+    m = fmin(dpp_f64<kRowShr2, 0xF>(m, inf), m);
+    v = dpp_f64<kRowShr4, 0xF>(v, 0.0) + v;
+    m = fmin(dpp_f64<kRowShr4, 0xF>(m, inf), m);
+    if constexpr (L == 64) {
+        v = dpp_f64<kRowShr8, 0xF>(v, 0.0) + v;
+        m = fmin(dpp_f64<kRowShr8, 0xF>(m, inf), m);
+        v = dpp_f64<kRowBcast15, 0xA>(v, 0.0) + v;
+        m = fmin(dpp_f64<kRowBcast15, 0xA>(m, inf), m);
+        v = dpp_f64<kRowBcast31, 0xC>(v, 0.0) + v;
+        m = fmin(dpp_f64<kRowBcast31, 0xC>(m, inf), m);
+    }
+}
+
 // The resident-row form, for bf16 rows of at most NCH chunks of 64 blocks
 // (the rows whose shortcut groups nearly always pass; binary32 rows, whose
 // groups fail, keep the form above).  Wave r of the workgroup owns row r of
@@ -385,17 +432,19 @@ channel_normalize_band_kernel(const Tin *__restrict__ w, int rows, int cols,
         const double s_blk = block_summary<Tin>(u[k], m);
         if (!valid) m = kBig;
         const double s0 = valid ? s_blk : 0.0;
+        // the group's sum and smallest exponent reach its last lane (shifts
+        // within rows of 16, eight lanes per group)
         int mg = m;
         double sg = s0;
-#pragma unroll
-        for (int x = 1; x < kGroup; x <<= 1) {
-            mg = min(mg, __shfl_xor(mg, x));
-            sg = sg + __shfl_xor(sg, x);
-        }
-        if (valid) {
-            raw[r][kb] = u[k];
-            if (b % kGroup == 0) grp[r][kb / kGroup] = make_double2(sg, square_bound(mg));
-        }
+        sg = dpp_f64<kRowShr1, 0xF>(sg, 0.0) + sg;
+        mg = min(dpp_i32<kRowShr1>(mg, kBig), mg);
+        sg = dpp_f64<kRowShr2, 0xF>(sg, 0.0) + sg;
+        mg = min(dpp_i32<kRowShr2>(mg, kBig), mg);
+        sg = dpp_f64<kRowShr4, 0xF>(sg, 0.0) + sg;
+        mg = min(dpp_i32<kRowShr4>(mg, kBig), mg);
+        if (valid) raw[r][kb] = u[k];
+        if (b % kGroup == kGroup - 1 && kb - (kGroup - 1) < nblk)
+            grp[r][kb / kGroup] = make_double2(sg, square_bound(mg));
     }
     // the row's LDS entries are the wave's own: its stores are done before its
     // reads (no other wave is waited for)
@@ -431,14 +480,7 @@ channel_normalize_band_kernel(const Tin *__restrict__ w, int rows, int cols,
                 const bool in = j >= s0 && j < ngr;
                 double v = in ? gq[q].x : 0.0;
                 double m = in ? gq[q].y : (double)INFINITY;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const double vu = __shfl_up(v, d), mu = __shfl_up(m, d);
-                    if (lane >= d) {
-                        v = vu + v;
-                        m = mu < m ? mu : m;
-                    }
-                }
+                scan_sum_min<64>(v, m);
                 const double P = carry + v;
                 const double M = mcarry < m ? mcarry : m;
                 const uint64_t fails = __ballot(in && !(P < M));
@@ -446,13 +488,13 @@ channel_normalize_band_kernel(const Tin *__restrict__ w, int rows, int cols,
                     const int lf = __builtin_ctzll(fails);
                     f = lf + 64 * q;
                     // the state after group f - 1 (or the run's start)
-                    const double Pp = __shfl(P, lf > 0 ? lf - 1 : 0);
-                    const double Mp = __shfl(M, lf > 0 ? lf - 1 : 0);
+                    const double Pp = lane_f64(P, lf > 0 ? lf - 1 : 0);
+                    const double Mp = lane_f64(M, lf > 0 ? lf - 1 : 0);
                     x_f = f > s0 ? (lf > 0 ? Pp : carry) : x;
                     g_f = f > s0 ? (lf > 0 ? Mp : mcarry) : g;
                 }
-                carry = __shfl(P, 63);
-                mcarry = __shfl(M, 63);
+                carry = lane_f64(P, 63);
+                mcarry = lane_f64(M, 63);
             }
             if (f == ngr) {                        // every remaining group passed
                 x = carry;
@@ -476,28 +518,21 @@ channel_normalize_band_kernel(const Tin *__restrict__ w, int rows, int cols,
                 const bool in = li >= i0 && li < ng;
                 double v = in ? S : 0.0;
                 double m = in ? B : (double)INFINITY;
-#pragma unroll
-                for (int d = 1; d < kGroup; d <<= 1) {
-                    const double vu = __shfl_up(v, d, kGroup), mu = __shfl_up(m, d, kGroup);
-                    if (li >= d) {
-                        v = vu + v;
-                        m = mu < m ? mu : m;
-                    }
-                }
+                scan_sum_min<kGroup>(v, m);
                 const double P = x + v;
                 const double M = g < m ? g : m;
                 const uint64_t fails = __ballot(in && !(P < M)) & ((1ull << kGroup) - 1);
                 if (!fails) {                      // the rest of the group passed
-                    x = __shfl(P, ng - 1);
-                    g = __shfl(M, ng - 1);
+                    x = lane_f64(P, ng - 1);
+                    g = lane_f64(M, ng - 1);
                     break;
                 }
                 const int lf = __builtin_ctzll(fails);
                 // the failing block's bound joins g first, as in the column-order
                 // chain; then its squares one at a time
-                const double Pp = __shfl(P, lf > 0 ? lf - 1 : 0);
+                const double Pp = lane_f64(P, lf > 0 ? lf - 1 : 0);
                 x = lf > i0 ? Pp : x;
-                g = __shfl(M, lf);
+                g = lane_f64(M, lf);
                 float vv[EPL];
                 unpack_block<Tin>(raw[r][b0 + lf], vv);
 #pragma unroll
