@@ -307,8 +307,10 @@ int exl3_decode_tiles(exl3_ctx *ctx, const uint16_t *packed, int64_t n, int K, f
  *   w_hat     optional float [rows*cols]: dequantized weights in the
  *             regularized domain, tile-major
  *   tile_sse  optional float [tiles]: per-tile squared error
- * Synchronizes the stream (the scale search reads results back); returns after
- * all work is complete.  Errors: EXL3_EINVAL, EXL3_EUNSUPPORTED, EXL3_ENOMEM,
+ * Synchronizes the stream: the tile energies are read back to pick the sample,
+ * the search's probes and reductions then run on the device without a host
+ * round trip, and its result and the errors are read back; returns after all
+ * work is complete.  Errors: EXL3_EINVAL, EXL3_EUNSUPPORTED, EXL3_ENOMEM,
  * EXL3_ENONFINITE (before any encode), EXL3_EHIP.
  */
 int exl3_quantize_matrix(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int cols,
