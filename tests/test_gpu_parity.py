@@ -161,6 +161,57 @@ def test_regularize_bit_exact(ctx, B, dtype, misaligned):
     assert np.array_equal(_bits(rm.cpu().numpy()), _bits(want))
 
 
+# Sign entries other than +-1 (outside the header's contract, which the
+# whole-matrix entry points enforce): the result is still the definition's,
+# the two products, in every block; lanes whose signs are all +-1 and lanes
+# with other values meet in the same blocks.
+@pytest.mark.parametrize("B,dtype", [(128, torch.bfloat16), (128, torch.float32),
+                                     (64, torch.bfloat16)])
+def test_regularize_non_unit_signs(ctx, B, dtype):
+    R, C = 2 * B, 2 * B
+    rng = np.random.default_rng(100 + B)
+    w = torch.from_numpy((rng.standard_normal((R, C)) * 0.02).astype(np.float32)).to(dtype)
+    w32 = w.to(torch.float32).numpy()
+    su = (2 * rng.integers(0, 2, R) - 1).astype(np.float32)
+    sv = (2 * rng.integers(0, 2, C) - 1).astype(np.float32)
+    su[[3, B + 17]] = [0.5, -3.0]
+    sv[[9, B + 40]] = [1.5, -0.0]
+    want = oracle.to_tiles(oracle.regularize(w32, su, sv, B))
+    out, sums, flag = ctx.regularize(w.to(DEV), torch.from_numpy(su).to(DEV),
+                                     torch.from_numpy(sv).to(DEV), B)
+    assert np.array_equal(_bits(out.cpu().numpy()), _bits(want))
+    assert np.array_equal(_bits(sums.cpu().numpy()), _bits(oracle.tile_sumsq(want)))
+    assert int(flag.item()) == 0
+
+
+# The non-finite flag: set by one NaN or infinity anywhere (bf16 and fp32
+# weights, 16-byte and element-wise loads), left clear by the largest finite
+# bf16 values, whose transforms overflow to infinity.
+@pytest.mark.parametrize("B,dtype,misaligned", [
+    (128, torch.bfloat16, False), (128, torch.float32, False), (64, torch.bfloat16, False),
+    (128, torch.bfloat16, True)])
+def test_regularize_nonfinite_flag(ctx, B, dtype, misaligned):
+    R, C = 2 * B, 3 * B
+    su = torch.ones(R, device=DEV)
+    sv = -torch.ones(C, device=DEV)
+
+    def flag_of(w):
+        wd = w.to(dtype).to(DEV)
+        if misaligned:
+            buf = torch.zeros(R * C + 1, dtype=dtype, device=DEV)
+            buf[1:] = wd.reshape(-1)
+            wd = buf[1:].view(R, C)
+        return int(ctx.regularize(wd, su, sv, B)[2].item())
+
+    for (r, c) in ((0, 0), (R - 1, C - 1), (B + 5, 2 * B + 3)):
+        for bad in (float("inf"), float("-inf"), float("nan")):
+            w = torch.zeros(R, C)
+            w[r, c] = bad
+            assert flag_of(w) == 1, (r, c, bad)
+    big = torch.full((R, C), float(torch.finfo(torch.bfloat16).max))
+    assert flag_of(big) == 0
+
+
 def test_workload1_whole_path(ctx):
     m = workloads.config(1)[0]
     want = oracle.quantize_matrix(m.w, m.su, m.sv, m.K, had_block=m.had_block, gss=None,

@@ -60,42 +60,65 @@ __device__ __forceinline__ float norm_const() {
 // by lane l ^ 32 of the same wave (exchanged with v_permlane32_swap, no LDS).
 //
 //   1. 16-byte loads of the block's rows (coalesced), signs applied, into LDS
-//      (blk_word);
+//      (blk_word).  Where the block's signs are all exactly +-1 (as the header
+//      requires), each product is its value with the sign bit flipped, so the
+//      flips are xors of the raw words (the same result for every finite value
+//      and for infinities); other sign values take the two products.  The
+//      non-finite test reads the raw exponent fields;
 //   2. left transform along columns, x rn(1/sqrt(B)), back to LDS;
 //   3. right transform along rows, x rn(1/sqrt(B)) (row-major output written
 //      from registers);
 //   4. the block in trellis order into a tile-major LDS stage (tile stride
 //      274 words, 17 words per tile row: conflict-free stores);
-//   5. per-tile sequential sum of squares, one lane per tile;
-//   6. tile-major output from the stage, consecutive lanes on consecutive
-//      positions.
+//   5. per-tile sequential sum of squares, one lane per tile, the reads of a
+//      tile row in flight while the previous row is summed;
+//   6. tile-major output from the stage, one wave per tile, consecutive lanes
+//      on consecutive positions.
 constexpr int kStageRow = 17;       // LDS words per 16-element tile row in the stage
 constexpr int kStageTile = 274;     // LDS words per tile in the stage
 
 __device__ __forceinline__ int stage_word(int t) { return (t >> 4) * kStageRow + (t & 15); }
 
 
-// The last butterfly level, across the two halves of the wave: one
-// v_permlane32_swap of the value with itself leaves the top half's value
-// (lanes 0..31) in the first result and the bottom half's (lanes 32..63) in
-// the second, in every lane; the lower half keeps top + bottom, the upper half
-// top - bottom, as fma(+-1, bottom, top): the product is exact, so the single
-// rounding is that of the addition or subtraction.
-__device__ __forceinline__ float last_level(float own, float sgn) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(own), __float_as_uint(own),
+// The last butterfly level, across the two halves of the wave, for two values
+// x, y of every lane (rows or columns r and r + 1 of the lane's half; the pair
+// of x in lane t < 32 is x in lane t + 32).  v_permlane32_swap(x, y) swaps the
+// upper 32 lanes of x with the lower 32 lanes of y, which gives lane t < 32
+// both members (top, bottom) of pair r and lane t + 32 both members of pair
+// r + 1; each lane forms top + bottom and top - bottom (one rounding each), and
+// a swap of those returns the sums to the top lanes and the differences to the
+// bottom lanes, in x (pair r) and y (pair r + 1): 4 instructions per two
+// values.
+__device__ __forceinline__ void last_level2(float &x, float &y) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y),
                                                     false, false);
-    return __builtin_fmaf(sgn, __uint_as_float(r[1]), __uint_as_float(r[0]));
+    const float top = __uint_as_float(p[0]), bot = __uint_as_float(p[1]);
+    const float sum = top + bot, dif = top - bot;
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(dif),
+                                                    false, false);
+    x = __uint_as_float(q[0]);
+    y = __uint_as_float(q[1]);
 }
 
-// LDS word of block element (row, col): rows of B + 1 words, so that the
-// column-wise and the row-wise accesses of the transforms hit 32 distinct
-// banks per half-wave (the first phase's stores, 8 consecutive columns per
-// lane, conflict 4-way; a skew that removes that needs more LDS than two
-// workgroups per compute unit leave).
-template <int B>
-__device__ __forceinline__ int blk_word(int row, int col) { return row * (B + 1) + col; }
-template <int B>
-constexpr int blk_words() { return B * (B + 1); }
+// LDS word of block element (row, col): an odd row pitch P and S words of pad
+// after every 32 columns (S = 2 for bf16 input, 1 for fp32).  The transforms'
+// accesses (32 lanes on 32 consecutive columns of one row, or on one column of
+// 32 consecutive rows) hit 32 distinct banks for any odd P; the first phase's
+// stores (EPC consecutive columns per lane, lanes on consecutive 16-byte
+// chunks) do too with the pad, which moves every fourth (bf16) or eighth
+// (fp32) chunk to the next bank group.
+template <int B, typename Tin>
+struct BlkPad {
+    static constexpr int S = sizeof(Tin) == 2 ? 2 : 1;      // words of pad per 32 columns
+    static constexpr int P0 = B + S * (B / 32 - 1);
+    static constexpr int P = P0 | 1;                         // odd row pitch
+};
+template <int B, typename Tin>
+__device__ __forceinline__ int blk_word(int row, int col) {
+    return row * BlkPad<B, Tin>::P + col + BlkPad<B, Tin>::S * (col >> 5);
+}
+template <int B, typename Tin>
+constexpr int blk_words() { return B * BlkPad<B, Tin>::P; }
 
 template <typename Tin>
 __device__ __forceinline__ void unpack16(const uint4 &u, float (&v)[16 / sizeof(Tin)]);
@@ -125,17 +148,17 @@ regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__
                   const uint8_t *__restrict__ order) {
     constexpr int H = B / 2;          // values per lane in a transform
     constexpr int TB = B / 16;        // tiles per block side
-    constexpr int kWords = blk_words<B>() > TB * TB * kStageTile ? blk_words<B>()
+    constexpr int kWords = blk_words<B, Tin>() > TB * TB * kStageTile ? blk_words<B, Tin>()
                                                                   : TB * TB * kStageTile;
     __shared__ float smem[kWords];
     __shared__ float sgn[2 * B];      // the block's column signs, then its row signs
     __shared__ uint8_t inv[256];      // element -> trellis position (ORDERED)
+    __shared__ bool other_sign[2 * B / 64];   // per wave: a staged sign other than +-1
     const int l = threadIdx.x;
     const int r0 = blockIdx.y * B, c0 = blockIdx.x * B;
     const int TC = cols / 16;
     const float c = norm_const<B>();
     const int idx = (l & 31) + 32 * (l >> 6), half = (l >> 5) & 1;
-    const float sgn_half = half ? -1.0f : 1.0f;
 
     // 1. load, signs (exact), into LDS
     bool bad = false;
@@ -149,22 +172,75 @@ regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__
             const int q = l + 2 * B * i, rr = q / CPR, cb = (q % CPR) * EPC;
             u[i] = *reinterpret_cast<const uint4 *>(w + (size_t)(r0 + rr) * cols + c0 + cb);
         }
-        sgn[l] = l < B ? sv[c0 + l] : su[r0 + l - B];
+        // each lane stages one sign; a wave flag records a sign other than +-1
+        const float sg = l < B ? sv[c0 + l] : su[r0 + l - B];
+        sgn[l] = sg;
+        const bool other = (__float_as_uint(sg) & 0x7FFFFFFFu) != 0x3F800000u;
+        const bool wave_other = __ballot(other) != 0;
+        if ((l & 63) == 0) other_sign[l >> 6] = wave_other;
         if constexpr (ORDERED)
             for (int t = l; t < 256; t += 2 * B) inv[order[t]] = (uint8_t)t;
         __syncthreads();
+        // non-finite: an exponent field of all ones; the largest exponent field of
+        // each half-word (bf16) or word (fp32) is kept
+        constexpr uint32_t kExp = EPC == 8 ? 0x7F807F80u : 0x7F800000u;
+        using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
+        u16x2 emax = {0, 0};
+        uint32_t emax32 = 0;
+        auto track = [&](const uint4 &x) {
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const int q = l + 2 * B * i, rr = q / CPR, cb = (q % CPR) * EPC;
-            float v[EPC];
-            unpack16<Tin>(u[i], v);
-            const float sr = sgn[B + rr];
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t wk = (&x.x)[k] & kExp;
+                if constexpr (EPC == 8)
+                    emax = __builtin_elementwise_max(emax, __builtin_bit_cast(u16x2, wk));
+                else
+                    emax32 = emax32 > wk ? emax32 : wk;
+            }
+        };
+        // the lane's columns are the same for every load.  Where every sign of
+        // the block is exactly +-1, each product is its value with the sign bit
+        // flipped: xors of the raw words; other sign values take the products
+        const int cb = (l % CPR) * EPC;
+        bool pm1 = true;
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                bad |= !isfinite(v[e]);
-                smem[blk_word<B>(rr, cb + e)] = (v[e] * sr) * sgn[cb + e];
+        for (int k = 0; k < 2 * B / 64; ++k) pm1 = pm1 && !other_sign[k];
+        if (pm1) {
+            uint32_t cm[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                cm[k] = EPC == 8 ? ((__float_as_uint(sgn[cb + 2 * k]) >> 16) & 0x8000u) |
+                                       (__float_as_uint(sgn[cb + 2 * k + 1]) & 0x80000000u)
+                                 : __float_as_uint(sgn[cb + k]) & 0x80000000u;
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const int rr = (l + 2 * B * i) / CPR;
+                uint32_t rm = __float_as_uint(sgn[B + rr]) & 0x80000000u;
+                if (EPC == 8) rm |= rm >> 16;
+                track(u[i]);
+                const uint4 x = make_uint4(u[i].x ^ cm[0] ^ rm, u[i].y ^ cm[1] ^ rm,
+                                           u[i].z ^ cm[2] ^ rm, u[i].w ^ cm[3] ^ rm);
+                float v[EPC];
+                unpack16<Tin>(x, v);
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) smem[blk_word<B, Tin>(rr, cb + e)] = v[e];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const int rr = (l + 2 * B * i) / CPR;
+                track(u[i]);
+                float v[EPC];
+                unpack16<Tin>(u[i], v);
+                const float sr = sgn[B + rr];
+#pragma unroll
+                for (int e = 0; e < EPC; ++e)
+                    smem[blk_word<B, Tin>(rr, cb + e)] = (v[e] * sr) * sgn[cb + e];
             }
         }
+        if constexpr (EPC == 8)
+            bad = emax.x == 0x7F80u || emax.y == 0x7F80u;
+        else
+            bad = emax32 == kExp;
     } else {
         if constexpr (ORDERED)
             for (int t = l; t < 256; t += 2 * B) inv[order[t]] = (uint8_t)t;
@@ -172,7 +248,7 @@ regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__
             const int rr = q / B, cc = q % B;
             const float v = load_w(w, (size_t)(r0 + rr) * cols + c0 + cc);
             bad |= !isfinite(v);
-            smem[blk_word<B>(rr, cc)] = (v * su[r0 + rr]) * sv[c0 + cc];
+            smem[blk_word<B, Tin>(rr, cc)] = (v * su[r0 + rr]) * sv[c0 + cc];
         }
     }
     if (bad && nonfinite) *nonfinite = 1;
@@ -181,20 +257,22 @@ regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__
     // 2. left transform: column idx, rows half * H ..
     float a[H];
 #pragma unroll
-    for (int r = 0; r < H; ++r) a[r] = smem[blk_word<B>(half * H + r, idx)];
+    for (int r = 0; r < H; ++r) a[r] = smem[blk_word<B, Tin>(half * H + r, idx)];
     fwht_regs<H>(a);
 #pragma unroll
-    for (int r = 0; r < H; ++r) a[r] = last_level(a[r], sgn_half);
+    for (int r = 0; r < H; r += 2) last_level2(a[r], a[r + 1]);
 #pragma unroll
-    for (int r = 0; r < H; ++r) smem[blk_word<B>(half * H + r, idx)] = a[r] * c;
+    for (int r = 0; r < H; ++r) smem[blk_word<B, Tin>(half * H + r, idx)] = a[r] * c;
     __syncthreads();
 
     // 3. right transform: row idx, columns half * H ..
 #pragma unroll
-    for (int q = 0; q < H; ++q) a[q] = smem[blk_word<B>(idx, half * H + q)];
+    for (int q = 0; q < H; ++q) a[q] = smem[blk_word<B, Tin>(idx, half * H + q)];
     fwht_regs<H>(a);
 #pragma unroll
-    for (int q = 0; q < H; ++q) a[q] = last_level(a[q], sgn_half) * c;
+    for (int q = 0; q < H; q += 2) last_level2(a[q], a[q + 1]);
+#pragma unroll
+    for (int q = 0; q < H; ++q) a[q] = a[q] * c;
     if (layout != 1) {
         float *dst = out + (size_t)(r0 + idx) * cols + c0 + half * H;
 #pragma unroll
@@ -218,46 +296,54 @@ regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__
     __syncthreads();
 
     // 5. per-tile sequential binary32 sum of squares, trellis order: wave 0,
-    // one lane per tile (reads unrolled ahead of the dependent additions)
+    // one lane per tile
     if (tile_sumsq && l < 64) {
         if (l < TB * TB) {
             const float *T = smem + l * kStageTile;
             float acc = 0.0f;
-#pragma unroll 16
-            for (int t = 0; t < 256; ++t) {
-                const float v = T[stage_word(t)];
-                const float sq = v * v;
-                acc = acc + sq;
+            // tile rows double-buffered: the reads of row k + 1 are in flight while
+            // row k is summed
+            float buf[2][16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) buf[0][j] = T[j];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                if (k + 1 < 16)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) buf[(k + 1) & 1][j] = T[(k + 1) * kStageRow + j];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float sq = buf[k & 1][j] * buf[k & 1][j];
+                    acc = acc + sq;
+                }
             }
             tile_sumsq[(size_t)(r0 / 16 + l / TB) * TC + (c0 / 16 + l % TB)] = acc;
         }
         return;
     }
 
-    // 6. tile-major output (the other waves, or all of them without energies):
-    // four consecutive positions per lane and store, eight stores' reads issued
-    // ahead
+    // 6. tile-major output (the other waves, or all of them without energies),
+    // whole tiles per wave: tile lt is one float4 per lane (positions 4 lane ..
+    // 4 lane + 3), the wave's store its 1 KiB; eight tiles' reads are issued
+    // ahead, and the tile bound is wave-uniform
     if (layout == 1) {
-        const int first = tile_sumsq ? 64 : 0;
-        const int nl = 2 * B - first;
-        constexpr int kQuads = B * B / 4;
-        for (int g0 = l - first; g0 < kQuads; g0 += 8 * nl) {
+        const int first = tile_sumsq ? 1 : 0;
+        const int nw = 2 * B / 64 - first, wv = (l >> 6) - first, t = 4 * (l & 63);
+        for (int lt0 = wv; lt0 < TB * TB; lt0 += 8 * nw) {
             float4 v[8];
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
-                const int g = g0 + b * nl;
-                if (g < kQuads) {
-                    const float *T = smem + (g >> 6) * kStageTile;
-                    const int t = 4 * (g & 63);
+                const int lt = lt0 + b * nw;
+                if (lt < TB * TB) {
+                    const float *T = smem + lt * kStageTile;
                     v[b] = make_float4(T[stage_word(t)], T[stage_word(t + 1)],
                                        T[stage_word(t + 2)], T[stage_word(t + 3)]);
                 }
             }
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
-                const int g = g0 + b * nl;
-                if (g < kQuads) {
-                    const int lt = g >> 6, t = 4 * (g & 63);
+                const int lt = lt0 + b * nw;
+                if (lt < TB * TB) {
                     const size_t tau = (size_t)(r0 / 16 + lt / TB) * TC + (c0 / 16 + lt % TB);
                     *reinterpret_cast<float4 *>(out + tau * 256 + t) = v[b];
                 }
