@@ -835,7 +835,7 @@ int exl3_regularize(exl3_ctx *ctx, const void *w, int w_dtype, int rows, int col
     const int id = open_timed(ctx, EXL3_KERNEL_REGULARIZE, (int64_t)ntiles);
     EXL3_HIP(ctx, exl3::launch_regularize(w, w_dtype, rows, cols, had_block, su, sv, w_reg,
                                           out_layout, tile_sumsq, nonfinite, tile_order(ctx),
-                                          ctx->stream));
+                                          ctx->n_cu, ctx->stream));
     close_timed(ctx, id);
     return EXL3_OK;
 }
@@ -1099,7 +1099,7 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
     int reg_id = open_timed(ctx, EXL3_KERNEL_REGULARIZE, ntiles);
     EXL3_HIP(ctx, exl3::launch_regularize(w, w_dtype, rows, cols, had_block, su, sv, ctx->d_wreg,
                                           EXL3_TILE_MAJOR, ctx->d_sumsq, ctx->d_flag,
-                                          tile_order(ctx), ctx->stream));
+                                          tile_order(ctx), ctx->n_cu, ctx->stream));
     close_timed(ctx, reg_id);
     const void *p_sumsq, *p_flag;
     if ((rc = read_back(ctx, ctx->d_sumsq, (size_t)ntiles * sizeof(float), ctx->d_flag,

@@ -168,11 +168,12 @@ hipError_t launch_ldlq_commit(const float *w_tiles, const float *what_span,
                               hipStream_t stream);
 
 // order: the within-tile order (position -> element) of tile-major arrays, or
-// null for the natural order.
+// null for the natural order.  n_cu: compute units of the device (the grid is
+// the workgroups resident at once, each taking blocks in turn).
 hipError_t launch_regularize(const void *w, int w_dtype, int rows, int cols, int had_block,
                              const float *su, const float *sv, float *out, int layout,
                              float *tile_sumsq, int *nonfinite, const uint8_t *order,
-                             hipStream_t stream);
+                             int n_cu, hipStream_t stream);
 
 hipError_t launch_unregularize(const float *in, int in_layout, int rows, int cols, int had_block,
                                const float *su, const float *sv, float *out,

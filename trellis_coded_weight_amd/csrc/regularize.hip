@@ -11,13 +11,13 @@
 // levels h = 1, 2, ..., B/2 (pairs (p, p+h), p mod 2h < h, become (a+b, a-b)),
 // x rn(1/sqrt(B)), the same transform along rows, x rn(1/sqrt(B)).
 //
-// One workgroup of 2B lanes per B x B block (the blocks are independent):
-// coalesced 16-byte loads into LDS, then each column's left transform split
-// over a lane pair, the block turned around in LDS, each row's right transform
-// split the same way, and a tile-major stage in LDS from which each of the
-// block's (B/16)^2 tiles gets its sequential binary32 sum of squares and the
-// output is written (tile-major or row-major).  HBM-bound: 6 bytes per element
-// for bf16 input (2 in, 4 out).
+// Workgroups of 2B lanes, each taking B x B blocks in turn (the blocks are
+// independent): coalesced 16-byte loads into LDS, each column's left transform
+// split over a lane pair, the block turned around in LDS, each row's right
+// transform split the same way, and a tile-major stage in LDS from which each
+// of the block's (B/16)^2 tiles gets its sequential binary32 sum of squares and
+// the output is written (tile-major or row-major).  HBM-bound: 6 bytes per
+// element for bf16 input (2 in, 4 out).
 //
 // Tile-major position t of a tile holds the tile's element order[t]
 // (element 16 r + c), order being the context's within-tile order (the
@@ -52,8 +52,9 @@ __device__ __forceinline__ float norm_const() {
     return B == 64 ? 0.125f : __uint_as_float(0x3DB504F3u);   // rn(1/sqrt(128))
 }
 
-// One workgroup of 2B lanes per B x B block.  Lane l works as half h = (l >> 5)
-// & 1 of index i = (l & 31) + 32 (l >> 6): in the left transform it holds rows
+// A workgroup of 2B lanes works on one B x B block at a time.  Lane l works as
+// half h = (l >> 5) & 1 of index i = (l & 31) + 32 (l >> 6): in the left
+// transform it holds rows
 // h B/2 .. h B/2 + B/2 - 1 of column i, in the right transform columns
 // h B/2 .. of row i.  The levels h < B/2 of a transform run in registers; the
 // last level pairs each value with the same position of the other half, held
@@ -140,6 +141,10 @@ __device__ __forceinline__ void unpack16<float>(const uint4 &u, float (&v)[4]) {
 }
 
 // VEC: the weights start on a 16-byte boundary (else one element per load).
+// Workgroup g takes the blocks g, g + G, g + 2G, ... (G workgroups, as many as
+// are resident at once; blocks in row-major order).  When a lane's 16-byte
+// loads of a block fit in 32 registers, the next block's are issued as soon as
+// the current block is in LDS, and arrive while it is transformed.
 template <int B, typename Tin, bool VEC, bool ORDERED>
 __global__ void __launch_bounds__(2 * B)
 regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__restrict__ su,
@@ -149,207 +154,229 @@ regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__
     constexpr int H = B / 2;          // values per lane in a transform
     constexpr int TB = B / 16;        // tiles per block side
     constexpr int kWords = blk_words<B, Tin>() > TB * TB * kStageTile ? blk_words<B, Tin>()
-                                                                  : TB * TB * kStageTile;
+                                                                       : TB * TB * kStageTile;
+    constexpr int EPC = 16 / sizeof(Tin);       // elements per 16-byte load
+    constexpr int CPR = B / EPC;                // loads per block row
+    constexpr int NL = B * CPR / (2 * B);       // loads per lane
+    constexpr bool kAhead = VEC && NL <= 8;     // the next block's loads issued early
     __shared__ float smem[kWords];
     __shared__ float sgn[2 * B];      // the block's column signs, then its row signs
     __shared__ uint8_t inv[256];      // element -> trellis position (ORDERED)
     __shared__ bool other_sign[2 * B / 64];   // per wave: a staged sign other than +-1
-    const int l = threadIdx.x;
-    const int r0 = blockIdx.y * B, c0 = blockIdx.x * B;
-    const int TC = cols / 16;
+    const int l0 = threadIdx.x;
+    const int TC = cols / 16, nbx = cols / B;
+    const int nblk = nbx * (rows / B);
     const float c = norm_const<B>();
-    const int idx = (l & 31) + 32 * (l >> 6), half = (l >> 5) & 1;
+    if constexpr (ORDERED)
+        for (int t = l0; t < 256; t += 2 * B) inv[order[t]] = (uint8_t)t;
 
-    // 1. load, signs (exact), into LDS
-    bool bad = false;
-    if constexpr (VEC) {
-        constexpr int EPC = 16 / sizeof(Tin);       // elements per 16-byte load
-        constexpr int CPR = B / EPC;                // loads per block row
-        constexpr int NL = B * CPR / (2 * B);       // loads per lane
-        uint4 u[NL];
+    // the lane's 16-byte loads of a block: rows (l + 2B i) / CPR, i < NL, and
+    // the same EPC columns cb .. cb + EPC - 1 for every i
+    uint4 u[NL];
+    auto fetch = [&](int blk) {
+        const int r0 = (blk / nbx) * B, c0 = (blk % nbx) * B, cb = (l0 % CPR) * EPC;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            const int q = l + 2 * B * i, rr = q / CPR, cb = (q % CPR) * EPC;
+            const int rr = (l0 + 2 * B * i) / CPR;
             u[i] = *reinterpret_cast<const uint4 *>(w + (size_t)(r0 + rr) * cols + c0 + cb);
         }
+    };
+    int blk = blockIdx.x;
+    if constexpr (kAhead)
+        if (blk < nblk) fetch(blk);
+
+    // non-finite input: an exponent field of all ones; with 16-byte loads the
+    // largest exponent field of each half-word (bf16) or word (fp32) is kept
+    constexpr uint32_t kExp = EPC == 8 ? 0x7F807F80u : 0x7F800000u;
+    using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
+    u16x2 emax = {0, 0};
+    uint32_t emax32 = 0;
+    auto track = [&](const uint4 &x) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t wk = (&x.x)[k] & kExp;
+            if constexpr (EPC == 8)
+                emax = __builtin_elementwise_max(emax, __builtin_bit_cast(u16x2, wk));
+            else
+                emax32 = emax32 > wk ? emax32 : wk;
+        }
+    };
+    bool bad = false;
+
+    for (; blk < nblk; blk += gridDim.x) {
+        // the lane index, opaque to the compiler once per block, so that the LDS
+        // addresses derived from it are formed inside the loop instead of being
+        // held in registers across it
+        int l = l0;
+        asm volatile("" : "+v"(l));
+        const int idx = (l & 31) + 32 * (l >> 6), half = (l >> 5) & 1;
+        const int cb = (l % CPR) * EPC;
+        const int r0 = (blk / nbx) * B, c0 = (blk % nbx) * B;
+        if constexpr (VEC && !kAhead) fetch(blk);
+
         // each lane stages one sign; a wave flag records a sign other than +-1
         const float sg = l < B ? sv[c0 + l] : su[r0 + l - B];
         sgn[l] = sg;
-        const bool other = (__float_as_uint(sg) & 0x7FFFFFFFu) != 0x3F800000u;
-        const bool wave_other = __ballot(other) != 0;
+        const bool wave_other = __ballot((__float_as_uint(sg) & 0x7FFFFFFFu) != 0x3F800000u) != 0;
         if ((l & 63) == 0) other_sign[l >> 6] = wave_other;
-        if constexpr (ORDERED)
-            for (int t = l; t < 256; t += 2 * B) inv[order[t]] = (uint8_t)t;
-        __syncthreads();
-        // non-finite: an exponent field of all ones; the largest exponent field of
-        // each half-word (bf16) or word (fp32) is kept
-        constexpr uint32_t kExp = EPC == 8 ? 0x7F807F80u : 0x7F800000u;
-        using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
-        u16x2 emax = {0, 0};
-        uint32_t emax32 = 0;
-        auto track = [&](const uint4 &x) {
+        __syncthreads();              // signs in; the previous block's stage is read
+
+        // 1. signs (exact), into LDS
+        if constexpr (VEC) {
+            // where every sign of the block is exactly +-1, each product is its
+            // value with the sign bit flipped: xors of the raw words; other sign
+            // values take the products
+            bool pm1 = true;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t wk = (&x.x)[k] & kExp;
-                if constexpr (EPC == 8)
-                    emax = __builtin_elementwise_max(emax, __builtin_bit_cast(u16x2, wk));
-                else
-                    emax32 = emax32 > wk ? emax32 : wk;
-            }
-        };
-        // the lane's columns are the same for every load.  Where every sign of
-        // the block is exactly +-1, each product is its value with the sign bit
-        // flipped: xors of the raw words; other sign values take the products
-        const int cb = (l % CPR) * EPC;
-        bool pm1 = true;
+            for (int k = 0; k < 2 * B / 64; ++k) pm1 = pm1 && !other_sign[k];
+            if (pm1) {
+                uint32_t cm[4];
 #pragma unroll
-        for (int k = 0; k < 2 * B / 64; ++k) pm1 = pm1 && !other_sign[k];
-        if (pm1) {
-            uint32_t cm[4];
+                for (int k = 0; k < 4; ++k)
+                    cm[k] = EPC == 8 ? ((__float_as_uint(sgn[cb + 2 * k]) >> 16) & 0x8000u) |
+                                           (__float_as_uint(sgn[cb + 2 * k + 1]) & 0x80000000u)
+                                     : __float_as_uint(sgn[cb + k]) & 0x80000000u;
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                cm[k] = EPC == 8 ? ((__float_as_uint(sgn[cb + 2 * k]) >> 16) & 0x8000u) |
-                                       (__float_as_uint(sgn[cb + 2 * k + 1]) & 0x80000000u)
-                                 : __float_as_uint(sgn[cb + k]) & 0x80000000u;
+                for (int i = 0; i < NL; ++i) {
+                    const int rr = (l + 2 * B * i) / CPR;
+                    uint32_t rm = __float_as_uint(sgn[B + rr]) & 0x80000000u;
+                    if (EPC == 8) rm |= rm >> 16;
+                    track(u[i]);
+                    const uint4 x = make_uint4(u[i].x ^ cm[0] ^ rm, u[i].y ^ cm[1] ^ rm,
+                                               u[i].z ^ cm[2] ^ rm, u[i].w ^ cm[3] ^ rm);
+                    float v[EPC];
+                    unpack16<Tin>(x, v);
 #pragma unroll
-            for (int i = 0; i < NL; ++i) {
-                const int rr = (l + 2 * B * i) / CPR;
-                uint32_t rm = __float_as_uint(sgn[B + rr]) & 0x80000000u;
-                if (EPC == 8) rm |= rm >> 16;
-                track(u[i]);
-                const uint4 x = make_uint4(u[i].x ^ cm[0] ^ rm, u[i].y ^ cm[1] ^ rm,
-                                           u[i].z ^ cm[2] ^ rm, u[i].w ^ cm[3] ^ rm);
-                float v[EPC];
-                unpack16<Tin>(x, v);
+                    for (int e = 0; e < EPC; ++e) smem[blk_word<B, Tin>(rr, cb + e)] = v[e];
+                }
+            } else {
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) smem[blk_word<B, Tin>(rr, cb + e)] = v[e];
+                for (int i = 0; i < NL; ++i) {
+                    const int rr = (l + 2 * B * i) / CPR;
+                    track(u[i]);
+                    float v[EPC];
+                    unpack16<Tin>(u[i], v);
+                    const float sr = sgn[B + rr];
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e)
+                        smem[blk_word<B, Tin>(rr, cb + e)] = (v[e] * sr) * sgn[cb + e];
+                }
             }
         } else {
-#pragma unroll
-            for (int i = 0; i < NL; ++i) {
-                const int rr = (l + 2 * B * i) / CPR;
-                track(u[i]);
-                float v[EPC];
-                unpack16<Tin>(u[i], v);
-                const float sr = sgn[B + rr];
-#pragma unroll
-                for (int e = 0; e < EPC; ++e)
-                    smem[blk_word<B, Tin>(rr, cb + e)] = (v[e] * sr) * sgn[cb + e];
+            for (int q = l; q < B * B; q += 2 * B) {
+                const int rr = q / B, cc = q % B;
+                const float v = load_w(w, (size_t)(r0 + rr) * cols + c0 + cc);
+                bad |= !isfinite(v);
+                smem[blk_word<B, Tin>(rr, cc)] = (v * sgn[B + rr]) * sgn[cc];
             }
         }
+        __syncthreads();
+        if constexpr (kAhead)
+            if (blk + (int)gridDim.x < nblk) fetch(blk + gridDim.x);
+
+        // 2. left transform: column idx, rows half * H ..
+        float a[H];
+#pragma unroll
+        for (int r = 0; r < H; ++r) a[r] = smem[blk_word<B, Tin>(half * H + r, idx)];
+        fwht_regs<H>(a);
+#pragma unroll
+        for (int r = 0; r < H; r += 2) last_level2(a[r], a[r + 1]);
+#pragma unroll
+        for (int r = 0; r < H; ++r) smem[blk_word<B, Tin>(half * H + r, idx)] = a[r] * c;
+        __syncthreads();
+
+        // 3. right transform: row idx, columns half * H ..
+#pragma unroll
+        for (int q = 0; q < H; ++q) a[q] = smem[blk_word<B, Tin>(idx, half * H + q)];
+        fwht_regs<H>(a);
+#pragma unroll
+        for (int q = 0; q < H; q += 2) last_level2(a[q], a[q + 1]);
+#pragma unroll
+        for (int q = 0; q < H; ++q) a[q] = a[q] * c;
+        if (layout != 1) {
+            float *dst = out + (size_t)(r0 + idx) * cols + c0 + half * H;
+#pragma unroll
+            for (int q = 0; q < H; q += 4)
+                *reinterpret_cast<float4 *>(dst + q) =
+                    make_float4(a[q], a[q + 1], a[q + 2], a[q + 3]);
+        }
+        if (layout != 1 && !tile_sumsq) continue;
+        __syncthreads();              // the block in LDS is read; the stage reuses it
+
+        // 4. trellis order into the tile-major stage
+        {
+            const int tr = idx >> 4, rin = idx & 15;
+#pragma unroll
+            for (int q = 0; q < H; ++q) {
+                const int cc = half * H + q;
+                const int el = 16 * rin + (cc & 15);
+                const int t = ORDERED ? inv[el] : el;
+                smem[(tr * TB + (cc >> 4)) * kStageTile + stage_word(t)] = a[q];
+            }
+        }
+        __syncthreads();
+
+        if (tile_sumsq && l < 64) {
+            // 5. per-tile sequential binary32 sum of squares, trellis order: wave
+            // 0, one lane per tile, tile rows double-buffered (the reads of row
+            // k + 1 in flight while row k is summed)
+            if (l < TB * TB) {
+                const float *T = smem + l * kStageTile;
+                float acc = 0.0f;
+                float buf[2][16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) buf[0][j] = T[j];
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    if (k + 1 < 16)
+#pragma unroll
+                        for (int j = 0; j < 16; ++j)
+                            buf[(k + 1) & 1][j] = T[(k + 1) * kStageRow + j];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const float sq = buf[k & 1][j] * buf[k & 1][j];
+                        acc = acc + sq;
+                    }
+                }
+                tile_sumsq[(size_t)(r0 / 16 + l / TB) * TC + (c0 / 16 + l % TB)] = acc;
+            }
+        } else if (layout == 1) {
+            // 6. tile-major output (the other waves, or all of them without
+            // energies), whole tiles per wave: tile lt is one float4 per lane
+            // (positions 4 lane .. 4 lane + 3), the wave's store its 1 KiB; eight
+            // tiles' reads are issued ahead, and the tile bound is wave-uniform
+            const int first = tile_sumsq ? 1 : 0;
+            const int nw = 2 * B / 64 - first, wv = (l >> 6) - first, t = 4 * (l & 63);
+            for (int lt0 = wv; lt0 < TB * TB; lt0 += 8 * nw) {
+                float4 v[8];
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    const int lt = lt0 + b * nw;
+                    if (lt < TB * TB) {
+                        const float *T = smem + lt * kStageTile;
+                        v[b] = make_float4(T[stage_word(t)], T[stage_word(t + 1)],
+                                           T[stage_word(t + 2)], T[stage_word(t + 3)]);
+                    }
+                }
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    const int lt = lt0 + b * nw;
+                    if (lt < TB * TB) {
+                        const size_t tau =
+                            (size_t)(r0 / 16 + lt / TB) * TC + (c0 / 16 + lt % TB);
+                        *reinterpret_cast<float4 *>(out + tau * 256 + t) = v[b];
+                    }
+                }
+            }
+        }
+    }
+    if constexpr (VEC) {
         if constexpr (EPC == 8)
             bad = emax.x == 0x7F80u || emax.y == 0x7F80u;
         else
             bad = emax32 == kExp;
-    } else {
-        if constexpr (ORDERED)
-            for (int t = l; t < 256; t += 2 * B) inv[order[t]] = (uint8_t)t;
-        for (int q = l; q < B * B; q += 2 * B) {
-            const int rr = q / B, cc = q % B;
-            const float v = load_w(w, (size_t)(r0 + rr) * cols + c0 + cc);
-            bad |= !isfinite(v);
-            smem[blk_word<B, Tin>(rr, cc)] = (v * su[r0 + rr]) * sv[c0 + cc];
-        }
     }
     if (bad && nonfinite) *nonfinite = 1;
-    __syncthreads();
-
-    // 2. left transform: column idx, rows half * H ..
-    float a[H];
-#pragma unroll
-    for (int r = 0; r < H; ++r) a[r] = smem[blk_word<B, Tin>(half * H + r, idx)];
-    fwht_regs<H>(a);
-#pragma unroll
-    for (int r = 0; r < H; r += 2) last_level2(a[r], a[r + 1]);
-#pragma unroll
-    for (int r = 0; r < H; ++r) smem[blk_word<B, Tin>(half * H + r, idx)] = a[r] * c;
-    __syncthreads();
-
-    // 3. right transform: row idx, columns half * H ..
-#pragma unroll
-    for (int q = 0; q < H; ++q) a[q] = smem[blk_word<B, Tin>(idx, half * H + q)];
-    fwht_regs<H>(a);
-#pragma unroll
-    for (int q = 0; q < H; q += 2) last_level2(a[q], a[q + 1]);
-#pragma unroll
-    for (int q = 0; q < H; ++q) a[q] = a[q] * c;
-    if (layout != 1) {
-        float *dst = out + (size_t)(r0 + idx) * cols + c0 + half * H;
-#pragma unroll
-        for (int q = 0; q < H; q += 4)
-            *reinterpret_cast<float4 *>(dst + q) = make_float4(a[q], a[q + 1], a[q + 2], a[q + 3]);
-    }
-    if (layout != 1 && !tile_sumsq) return;
-    __syncthreads();                  // the block in LDS is read; the stage reuses it
-
-    // 4. trellis order into the tile-major stage
-    {
-        const int tr = idx >> 4, rin = idx & 15;
-#pragma unroll
-        for (int q = 0; q < H; ++q) {
-            const int cc = half * H + q;
-            const int el = 16 * rin + (cc & 15);
-            const int t = ORDERED ? inv[el] : el;
-            smem[(tr * TB + (cc >> 4)) * kStageTile + stage_word(t)] = a[q];
-        }
-    }
-    __syncthreads();
-
-    // 5. per-tile sequential binary32 sum of squares, trellis order: wave 0,
-    // one lane per tile
-    if (tile_sumsq && l < 64) {
-        if (l < TB * TB) {
-            const float *T = smem + l * kStageTile;
-            float acc = 0.0f;
-            // tile rows double-buffered: the reads of row k + 1 are in flight while
-            // row k is summed
-            float buf[2][16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) buf[0][j] = T[j];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                if (k + 1 < 16)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) buf[(k + 1) & 1][j] = T[(k + 1) * kStageRow + j];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const float sq = buf[k & 1][j] * buf[k & 1][j];
-                    acc = acc + sq;
-                }
-            }
-            tile_sumsq[(size_t)(r0 / 16 + l / TB) * TC + (c0 / 16 + l % TB)] = acc;
-        }
-        return;
-    }
-
-    // 6. tile-major output (the other waves, or all of them without energies),
-    // whole tiles per wave: tile lt is one float4 per lane (positions 4 lane ..
-    // 4 lane + 3), the wave's store its 1 KiB; eight tiles' reads are issued
-    // ahead, and the tile bound is wave-uniform
-    if (layout == 1) {
-        const int first = tile_sumsq ? 1 : 0;
-        const int nw = 2 * B / 64 - first, wv = (l >> 6) - first, t = 4 * (l & 63);
-        for (int lt0 = wv; lt0 < TB * TB; lt0 += 8 * nw) {
-            float4 v[8];
-#pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const int lt = lt0 + b * nw;
-                if (lt < TB * TB) {
-                    const float *T = smem + lt * kStageTile;
-                    v[b] = make_float4(T[stage_word(t)], T[stage_word(t + 1)],
-                                       T[stage_word(t + 2)], T[stage_word(t + 3)]);
-                }
-            }
-#pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const int lt = lt0 + b * nw;
-                if (lt < TB * TB) {
-                    const size_t tau = (size_t)(r0 / 16 + lt / TB) * TC + (c0 / 16 + lt % TB);
-                    *reinterpret_cast<float4 *>(out + tau * 256 + t) = v[b];
-                }
-            }
-        }
-    }
 }
 
 // Inverse of the regularization (H is symmetric and orthonormal, so its own
@@ -404,16 +431,30 @@ unregularize_kernel(const float *__restrict__ in, int rows, int cols, int in_lay
     }
 }
 
+// Workgroups of one instantiation resident per compute unit (queried once).
+template <typename Kernel>
+int groups_per_cu(Kernel kernel, int threads) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess)
+        n = 0;
+    return n > 0 ? n : 1;
+}
+
 template <int B, typename Tin>
 hipError_t launch_reg_t(const void *w, int rows, int cols, const float *su, const float *sv,
                         float *out, int layout, float *tile_sumsq, int *nonfinite,
-                        const uint8_t *order, hipStream_t stream) {
-    dim3 grid(cols / B, rows / B);
+                        const uint8_t *order, int n_cu, hipStream_t stream) {
+    const int nblk = (cols / B) * (rows / B);
     const Tin *wt = reinterpret_cast<const Tin *>(w);
     const bool vec = reinterpret_cast<uintptr_t>(w) % 16 == 0;
-#define EXL3_REG_LAUNCH(V, O)                                                                \
-    hipLaunchKernelGGL((regularize_kernel<B, Tin, V, O>), grid, dim3(2 * B), 0, stream, wt,  \
-                       rows, cols, su, sv, out, layout, tile_sumsq, nonfinite, order)
+#define EXL3_REG_LAUNCH(V, O)                                                                  \
+    do {                                                                                       \
+        static const int per_cu = groups_per_cu(regularize_kernel<B, Tin, V, O>, 2 * B);       \
+        const int groups = nblk < per_cu * n_cu ? nblk : per_cu * n_cu;                        \
+        hipLaunchKernelGGL((regularize_kernel<B, Tin, V, O>), dim3((unsigned)groups),          \
+                           dim3(2 * B), 0, stream, wt, rows, cols, su, sv, out, layout,        \
+                           tile_sumsq, nonfinite, order);                                      \
+    } while (0)
     if (vec && order) EXL3_REG_LAUNCH(true, true);
     else if (vec) EXL3_REG_LAUNCH(true, false);
     else if (order) EXL3_REG_LAUNCH(false, true);
@@ -441,19 +482,22 @@ hipError_t launch_unregularize(const float *in, int in_layout, int rows, int col
 
 hipError_t launch_regularize(const void *w, int w_dtype, int rows, int cols, int had_block,
                              const float *su, const float *sv, float *out, int layout,
-                             float *tile_sumsq, int *nonfinite, const uint8_t *order,
+                             float *tile_sumsq, int *nonfinite, const uint8_t *order, int n_cu,
                              hipStream_t stream) {
     if (rows <= 0 || cols <= 0) return hipSuccess;
+    if (n_cu < 1) n_cu = 1;
     if (had_block == 64)
-        return w_dtype == 1 ? launch_reg_t<64, uint16_t>(w, rows, cols, su, sv, out, layout,
-                                                         tile_sumsq, nonfinite, order, stream)
-                            : launch_reg_t<64, float>(w, rows, cols, su, sv, out, layout,
-                                                      tile_sumsq, nonfinite, order, stream);
+        return w_dtype == 1
+                   ? launch_reg_t<64, uint16_t>(w, rows, cols, su, sv, out, layout, tile_sumsq,
+                                                nonfinite, order, n_cu, stream)
+                   : launch_reg_t<64, float>(w, rows, cols, su, sv, out, layout, tile_sumsq,
+                                             nonfinite, order, n_cu, stream);
     if (had_block == 128)
-        return w_dtype == 1 ? launch_reg_t<128, uint16_t>(w, rows, cols, su, sv, out, layout,
-                                                          tile_sumsq, nonfinite, order, stream)
-                            : launch_reg_t<128, float>(w, rows, cols, su, sv, out, layout,
-                                                       tile_sumsq, nonfinite, order, stream);
+        return w_dtype == 1
+                   ? launch_reg_t<128, uint16_t>(w, rows, cols, su, sv, out, layout, tile_sumsq,
+                                                 nonfinite, order, n_cu, stream)
+                   : launch_reg_t<128, float>(w, rows, cols, su, sv, out, layout, tile_sumsq,
+                                              nonfinite, order, n_cu, stream);
     return hipErrorInvalidValue;
 }
 
