@@ -61,6 +61,23 @@ def test_regularize_and_inverse(ctx, B):
     assert np.array_equal(_bits(back.cpu().numpy()), _bits(want_back))
 
 
+# 4096 x 4096: more blocks than workgroups resident at once (1,024 blocks of 128
+# or 4,096 of 64), so each workgroup takes several blocks in turn, with the
+# next block's loads issued early (bf16) or at the top of each block (fp32 at
+# B = 128).
+@pytest.mark.parametrize("B,dtype", [(128, torch.bfloat16), (64, torch.bfloat16),
+                                     (128, torch.float32)])
+def test_regularize_many_blocks_per_workgroup(ctx, B, dtype):
+    m = workloads.gaussian(4096, 4096, 0.02, 31, 32, K=2)
+    w = torch.from_numpy(m.w).to(dtype).to(DEV)
+    su, sv = torch.from_numpy(m.su).to(DEV), torch.from_numpy(m.sv).to(DEV)
+    reg, sums, flag = ctx.regularize(w, su, sv, had_block=B)
+    want = oracle.to_tiles(oracle.regularize(w.cpu().float().numpy(), m.su, m.sv, B), ORDER)
+    assert np.array_equal(_bits(reg.cpu().numpy()), _bits(want))
+    assert np.array_equal(_bits(sums.cpu().numpy()), _bits(oracle.tile_sumsq(want)))
+    assert int(flag.item()) == 0
+
+
 def test_whole_matrix_golden_section(ctx):
     m = workloads.gaussian(128, 256, 0.02, 11, 12, K=2)
     w, su, sv = _dev(m)
