@@ -80,7 +80,6 @@ constexpr int kStageTile = 274;     // LDS words per tile in the stage
 
 __device__ __forceinline__ int stage_word(int t) { return (t >> 4) * kStageRow + (t & 15); }
 
-
 // The last butterfly level, across the two halves of the wave, for two values
 // x, y of every lane (rows or columns r and r + 1 of the lane's half; the pair
 // of x in lane t < 32 is x in lane t + 32).  v_permlane32_swap(x, y) swaps the
@@ -104,10 +103,11 @@ __device__ __forceinline__ void last_level2(float &x, float &y) {
 // LDS word of block element (row, col): an odd row pitch P and S words of pad
 // after every 32 columns (S = 2 for bf16 input, 1 for fp32).  The transforms'
 // accesses (32 lanes on 32 consecutive columns of one row, or on one column of
-// 32 consecutive rows) hit 32 distinct banks for any odd P; the first phase's
-// stores (EPC consecutive columns per lane, lanes on consecutive 16-byte
-// chunks) do too with the pad, which moves every fourth (bf16) or eighth
-// (fp32) chunk to the next bank group.
+// 32 consecutive rows) hit 32 distinct banks for any odd P; at B = 128 the
+// first phase's stores (EPC consecutive columns per lane, lanes on consecutive
+// 16-byte chunks) do too with the pad, which moves every fourth (bf16) or
+// eighth (fp32) chunk to the next bank group (at B = 64, bf16, they meet two
+// to a bank).
 template <int B, typename Tin>
 struct BlkPad {
     static constexpr int S = sizeof(Tin) == 2 ? 2 : 1;      // words of pad per 32 columns
