@@ -470,6 +470,28 @@ def other_workloads(ctx):
     return out
 
 
+def decode_mode(ctx, out, n_tiles):
+    """Decode of the final encode's container (all tiles of the matrix at K = 2):
+    20 launches timed with the library's events on its stream; algorithmic bytes
+    per tile: 64 B of container read, 1 KiB of binary32 values written (the level
+    table, 128 KiB, stays in cache)."""
+    import torch
+    packed = out["packed"].reshape(-1, 32)
+    ctx.decode_tiles(packed, 2, out["scale"])
+    torch.cuda.synchronize()
+    ctx.set_timing(True)
+    for _ in range(20):
+        ctx.decode_tiles(packed, 2, out["scale"])
+    total, launches, _ = ctx.read_timing("decode")
+    ctx.set_timing(False)
+    ms = total / launches
+    nbytes = n_tiles * (64 + 1024)
+    return {"workload": "the final encode's container, %d tiles at K=2" % n_tiles,
+            "decode_ms": round(ms, 4),
+            "decode_gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "decode_hbm_frac": round(nbytes / (ms * 1e-3) / 8e12, 4)}
+
+
 def run_steps(ctx, w, su, sv, K, gss, steps):
     import torch
     out = None
@@ -591,6 +613,7 @@ def main():
     ldlq = None if args.no_ldlq else ldlq_mode(ctx, m, w, su, sv, args.steps)
     grid = None if args.no_grid else grid_mode(ctx, w, su, sv, n_tiles, args.steps)
     chan = None if args.no_grid else channel_mode(ctx, n_tiles, args.steps)
+    dec = decode_mode(ctx, out, n_tiles)
     layer = None if args.no_layer else layer_mode(ctx)
     others = None if args.no_layer else other_workloads(ctx)
 
@@ -634,6 +657,7 @@ def main():
         "ldlq_mode": ldlq,
         "grid_search_mode": grid,
         "channel_norm_mode": chan,
+        "decode_mode": dec,
         "layer_mode": layer,
         "other_workloads": others,
     }

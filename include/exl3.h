@@ -403,7 +403,8 @@ enum {
                                     the main part (their durations overlap) */
     EXL3_KERNEL_FWD_COST = 6,    /* pass 2's cost-only form (scale-search probes,
                                     on the context's stream) */
-    EXL3_KERNEL_CHANNEL = 7      /* out-channel normalization (tile count 0) */
+    EXL3_KERNEL_CHANNEL = 7,     /* out-channel normalization (tile count 0) */
+    EXL3_KERNEL_DECODE = 8       /* exl3_decode_tiles */
 };
 
 /*

@@ -130,6 +130,35 @@ def test_decode_matches_oracle(ctx, K):
     assert np.array_equal(_bits(out.cpu().numpy()), _bits(v[states]))
 
 
+# The container and the output off their natural alignment (the container two
+# bytes past a 4-byte boundary, the output four bytes past a 16-byte one),
+# through the C ABI; 9 tiles, so that the last workgroup is partly empty.
+@pytest.mark.parametrize("K", [1, 2, 3, 8])
+def test_decode_unaligned_pointers(ctx, K):
+    rng = np.random.default_rng(50 + K)
+    n = 9
+    states = np.zeros((n, 256), np.int64)
+    b = rng.integers(0, 1 << K, (n, 256))
+    for t in range(256):
+        s = np.zeros(n, np.int64)
+        for j in range(-(16 // K) - 1, 1):
+            s = ((s << K) | b[:, (t + j) % 256]) & 0xFFFF
+        states[:, t] = s
+    packed = torch.from_numpy(oracle.pack_states(states, K).view(np.int16).reshape(-1))
+    pbuf = torch.zeros(packed.numel() + 1, dtype=torch.int16, device=DEV)
+    pbuf[1:] = packed.to(DEV)
+    obuf = torch.full((n * 256 + 1,), -1.0, device=DEV)
+    assert pbuf[1:].data_ptr() % 4 == 2 and obuf[1:].data_ptr() % 16 == 4
+    torch.cuda.synchronize()
+    rc = ctx.lib.exl3_decode_tiles(ctx.handle, pbuf[1:].data_ptr(), n, K, 0.5,
+                                   obuf[1:].data_ptr())
+    assert rc == 0
+    torch.cuda.synchronize()
+    v = oracle.scaled_levels(oracle.mul1_levels_fp16(), 0.5)
+    assert np.array_equal(_bits(obuf[1:].cpu().numpy()), _bits(v[states].reshape(-1)))
+    assert obuf[0].item() == -1.0
+
+
 # misaligned: the weights start one element past a 16-byte boundary (the
 # kernel then loads one element at a time)
 @pytest.mark.parametrize("B,dtype,misaligned", [

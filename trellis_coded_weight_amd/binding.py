@@ -38,7 +38,7 @@ EXPORTED = [
 ]
 CODEBOOK_KINDS = {"mul1": 0, "mcg": 1, "3inst": 2}
 KERNEL_KINDS = {"fwd1": 0, "fwd2": 1, "tb1": 2, "tb2": 3, "regularize": 4, "fwd_side": 5,
-                "fwd_cost": 6, "channel": 7}
+                "fwd_cost": 6, "channel": 7, "decode": 8}
 
 
 class Exl3Error(RuntimeError):

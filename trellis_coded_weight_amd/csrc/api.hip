@@ -996,7 +996,10 @@ int exl3_decode_tiles(exl3_ctx *ctx, const uint16_t *packed, int64_t n, int K, f
         (rc = check_span(ctx, out, nt * 256 * sizeof(float), "out")) != EXL3_OK)
         return rc;
     if ((rc = set_device(ctx)) != EXL3_OK) return rc;
-    EXL3_HIP(ctx, exl3::launch_decode(packed, n, K, scale, ctx->d_levels, out, ctx->stream));
+    const int id = open_timed(ctx, EXL3_KERNEL_DECODE, n);
+    EXL3_HIP(ctx, exl3::launch_decode(packed, n, K, scale, ctx->d_levels, out, ctx->n_cu,
+                                      ctx->stream));
+    close_timed(ctx, id);
     return EXL3_OK;
 }
 

@@ -183,8 +183,10 @@ hipError_t launch_channel_normalize(const void *w, int w_dtype, int rows, int co
                                     const float *su, double floor_value, float *w_norm,
                                     float *su_folded, double *row_rms, hipStream_t stream);
 
+// levels: the device level table (16-byte aligned); n_cu: compute units of
+// the device (one workgroup each at most, decoding tiles in turn).
 hipError_t launch_decode(const uint16_t *packed, int64_t n, int K, float scale,
-                         const uint16_t *levels, float *out, hipStream_t stream);
+                         const uint16_t *levels, float *out, int n_cu, hipStream_t stream);
 
 hipError_t launch_to_f16(const float *src, const int32_t *idx, int64_t n, float scale,
                          uint16_t *dst, hipStream_t stream);

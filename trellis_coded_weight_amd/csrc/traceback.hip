@@ -291,24 +291,59 @@ traceback2_wave_kernel(const typename Geo<K>::bp_t *__restrict__ bp, int64_t n,
     }
 }
 
-__global__ void __launch_bounds__(256)
-decode_kernel(const uint16_t *__restrict__ packed, int K, float scale,
-              const uint16_t *__restrict__ levels, float *__restrict__ out) {
-    __shared__ uint16_t words[16 * 8];
-    const int64_t tile = blockIdx.x;
-    const int t = threadIdx.x;
-    const int nw = 16 * K;
-    if (t < nw) words[t] = packed[(size_t)tile * nw + (t ^ 1)];   // undo the pair swap
+// Decode: one workgroup of 16 waves per compute unit (as many as the grid
+// holds), which copies the level table (65,536 binary16 values, 128 KiB) into
+// LDS once and then decodes tiles in turn, one wave per tile and four
+// consecutive states per lane; the level lookups, random over the table, are
+// LDS reads.  The container stores each pair of 16-bit words swapped, so words
+// 2i + 1 and 2i read as one little-endian 32-bit value are stream bits 32i ..
+// 32i + 31 with bit 32i as its most significant bit (chunk i).  S_t, the 16
+// stream bits ending at bit (t + 1)K - 1 (circularly), is then the top half of
+// a funnel shift of two consecutive chunks.  The chunks are assembled from
+// 16-bit loads (no alignment needed); the output is one float4 per lane, a
+// wave's 1 KiB tile in one store, where it is 16-byte aligned.
+constexpr int kDecodeWaves = 16;
+
+__global__ void __launch_bounds__(64 * kDecodeWaves)
+decode_kernel(const uint16_t *__restrict__ packed, int64_t n, int K, float scale,
+              const uint16_t *__restrict__ levels, float *__restrict__ out, bool out_vec) {
+    __shared__ uint4 lut[8192];                        // the level table
+    __shared__ uint32_t chunk[kDecodeWaves][64];       // one tile's stream per wave
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint4 *src = reinterpret_cast<const uint4 *>(levels);
+    for (int i = threadIdx.x; i < 8192; i += 64 * kDecodeWaves) lut[i] = src[i];
     __syncthreads();
-    const int nbits = kSteps * K;
-    uint32_t s = 0;
-    const int end = (t + 1) * K;                  // exclusive end of S_t's window
-    for (int j = end - 16; j < end; ++j) {
-        int jj = j < 0 ? j + nbits : j;
-        uint32_t bit = (words[jj >> 4] >> (15 - (jj & 15))) & 1u;
-        s = (s << 1) | bit;
+    const uint16_t *lv = reinterpret_cast<const uint16_t *>(lut);
+    const int nc = 8 * K;                              // 32-bit chunks per tile (K <= 8)
+    const int nbits = 256 * K;
+    const int64_t stride = (int64_t)gridDim.x * kDecodeWaves;
+    for (int64_t tile = (int64_t)blockIdx.x * kDecodeWaves + wv; tile < n; tile += stride) {
+        if (lane < nc) {
+            const uint16_t *pw = packed + (size_t)tile * (16 * K) + 2 * lane;
+            chunk[wv][lane] = ((uint32_t)pw[1] << 16) | pw[0];
+        }
+        // the wave's own stores, read back by other lanes of the same wave
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        float v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            int p = (4 * lane + k + 1) * K - 16;       // first bit of S_t's window
+            if (p < 0) p += nbits;
+            const int c = p >> 5;
+            const uint32_t hi = chunk[wv][c], lo = chunk[wv][c + 1 == nc ? 0 : c + 1];
+            const uint32_t st = __funnelshift_l(lo, hi, (unsigned)(p & 31)) >> 16;
+            v[k] = scale * half_bits_to_float(lv[st]);
+        }
+        float *o = out + (size_t)tile * kSteps + 4 * lane;
+        if (out_vec) {
+            *reinterpret_cast<float4 *>(o) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = v[k];
+        }
+        // the chunk reads of this tile are done before the next tile's stores
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
-    out[(size_t)tile * kSteps + t] = scale * half_bits_to_float(levels[s]);
 }
 
 __global__ void __launch_bounds__(256)
@@ -387,11 +422,16 @@ hipError_t launch_traceback(int K, int pass, bool f16, const void *bp, int64_t n
 }
 
 hipError_t launch_decode(const uint16_t *packed, int64_t n, int K, float scale,
-                         const uint16_t *levels, float *out, hipStream_t stream) {
+                         const uint16_t *levels, float *out, int n_cu, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     if (K < 1 || K > 8) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(decode_kernel, dim3((unsigned)n), dim3(kSteps), 0, stream, packed, K, scale,
-                       levels, out);
+    // the level table is read as 16-byte words
+    if (reinterpret_cast<uintptr_t>(levels) % 16 != 0) return hipErrorInvalidValue;
+    const int64_t need = (n + kDecodeWaves - 1) / kDecodeWaves;
+    const int64_t groups = need < n_cu ? need : (n_cu > 0 ? n_cu : 1);
+    const bool out_vec = reinterpret_cast<uintptr_t>(out) % 16 == 0;
+    hipLaunchKernelGGL(decode_kernel, dim3((unsigned)groups), dim3(64 * kDecodeWaves), 0, stream,
+                       packed, n, K, scale, levels, out, out_vec);
     return hipGetLastError();
 }
 
