@@ -75,6 +75,11 @@ struct exl3_ctx {
     size_t sumsq_cap = 0;
     float *d_sse = nullptr;
     size_t sse_cap = 0;
+    // grid search: the tile indices and per-tile scales of a batch of points
+    int32_t *d_bidx = nullptr;
+    size_t bidx_cap = 0;
+    float *d_bscale = nullptr;
+    size_t bscale_cap = 0;
     int *d_flag = nullptr;
     GssDev *d_gss = nullptr;
     // pinned host staging for the read-backs (sign checks, tile energies, the
@@ -367,7 +372,7 @@ int ensure_aux(exl3_ctx *ctx) {
 // chain runs on the second stream, so its pass 1 shares a round with the main
 // part's pass 2 instead of leaving the chip idle for a round of its own.
 int probe_split(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, int K, float scale,
-                const float *scale_dev, float *cost_out) {
+                const float *scale_dev, float *cost_out, bool scale_per_tile) {
     const int64_t rem = n % ctx->n_cu, a = n - rem;
     const size_t per_tile = exl3::bp_bytes_per_tile(K);
     char *bp = static_cast<char *>(ctx->d_bp);
@@ -384,9 +389,11 @@ int probe_split(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, in
     for (const Part &p : parts) {
         int id = open_timed(ctx, p.s == ctx->stream ? EXL3_KERNEL_FWD1 : EXL3_KERNEL_FWD_SIDE,
                             p.count, p.s);
+        const float *sd = scale_dev && scale_per_tile ? scale_dev + p.first : scale_dev;
         EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 1, x, idx + p.first, 0, p.count, ctx->d_levels,
-                                               scale, scale_dev, nullptr, bp + p.first * per_tile,
-                                               ctx->d_end + p.first, nullptr, p.s));
+                                               scale, sd, nullptr, bp + p.first * per_tile,
+                                               ctx->d_end + p.first, nullptr, p.s,
+                                               scale_per_tile));
         close_timed(ctx, id);
     }
     for (const Part &p : parts) {
@@ -398,10 +405,11 @@ int probe_split(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, in
         close_timed(ctx, id);
         id = open_timed(ctx, p.s == ctx->stream ? EXL3_KERNEL_FWD_COST : EXL3_KERNEL_FWD_SIDE,
                         p.count, p.s);
+        const float *sd = scale_dev && scale_per_tile ? scale_dev + p.first : scale_dev;
         EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 3, x, idx + p.first, 0, p.count, ctx->d_levels,
-                                               scale, scale_dev, ctx->d_X + p.first,
+                                               scale, sd, ctx->d_X + p.first,
                                                bp + p.first * per_tile, nullptr,
-                                               cost_out + p.first, p.s));
+                                               cost_out + p.first, p.s, scale_per_tile));
         close_timed(ctx, id);
     }
     EXL3_HIP(ctx, hipEventRecord(ctx->ev_join, ctx->aux));
@@ -461,7 +469,8 @@ gss_step_kernel(GssDev *__restrict__ st, const float *__restrict__ costs, int64_
 // scale_dev, the forward passes read the scale from device memory.
 int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, int K,
                  float scale, uint16_t *packed, uint16_t *states, float *sse, float *w_hat,
-                 float *cost_only, const float *scale_dev = nullptr) {
+                 float *cost_only, const float *scale_dev = nullptr,
+                 bool scale_per_tile = false) {
     if (n == 0) return EXL3_OK;
     // the traceback dequantizes at the host's scale: a device scale is for
     // path costs only
@@ -471,14 +480,15 @@ int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, i
     if ((rc = admit_batch(ctx, n, K, &batch)) != EXL3_OK) return rc;
     if (cost_only && idx && batch == n && n > ctx->n_cu && n % ctx->n_cu != 0 &&
         n % ctx->n_cu <= ctx->n_cu / 8)
-        return probe_split(ctx, x, idx, n, K, scale, scale_dev, cost_only);
+        return probe_split(ctx, x, idx, n, K, scale, scale_dev, cost_only, scale_per_tile);
     for (int64_t i0 = 0; i0 < n; i0 += batch) {
         const int64_t nb = std::min<int64_t>(batch, n - i0);
         const int32_t *idx_b = idx ? idx + i0 : nullptr;
+        const float *sd = scale_dev && scale_per_tile ? scale_dev + i0 : scale_dev;
         int id = open_timed(ctx, EXL3_KERNEL_FWD1, nb);
-        EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 1, x, idx_b, i0, nb, ctx->d_levels, scale,
-                                               scale_dev, nullptr, ctx->d_bp, ctx->d_end, nullptr,
-                                               ctx->stream));
+        EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, 1, x, idx_b, i0, nb, ctx->d_levels, scale, sd,
+                                               nullptr, ctx->d_bp, ctx->d_end, nullptr,
+                                               ctx->stream, scale_per_tile));
         close_timed(ctx, id);
         id = open_timed(ctx, EXL3_KERNEL_TB1, nb);
         EXL3_HIP(ctx, exl3::launch_traceback(K, 1, false, ctx->d_bp, nb, ctx->d_end, ctx->d_X, nullptr,
@@ -487,10 +497,10 @@ int encode_chain(exl3_ctx *ctx, const float *x, const int32_t *idx, int64_t n, i
         close_timed(ctx, id);
         id = open_timed(ctx, cost_only ? EXL3_KERNEL_FWD_COST : EXL3_KERNEL_FWD2, nb);
         EXL3_HIP(ctx, exl3::launch_viterbi_fwd(K, cost_only ? 3 : 2, x, idx_b, i0, nb,
-                                               ctx->d_levels, scale, scale_dev,
+                                               ctx->d_levels, scale, sd,
                                                ctx->d_X, ctx->d_bp, nullptr,
                                                cost_only ? cost_only + i0 : ctx->d_cost,
-                                               ctx->stream));
+                                               ctx->stream, scale_per_tile));
         close_timed(ctx, id);
         if (!cost_only) {
             id = open_timed(ctx, EXL3_KERNEL_TB2, nb);
@@ -664,7 +674,8 @@ void exl3_ctx_destroy(exl3_ctx *ctx) {
                     ctx->d_cost,        ctx->d_idx,         ctx->d_wreg,        ctx->d_sumsq,
                     ctx->d_sse,         ctx->d_flag,        ctx->d_err_tiles,   ctx->d_span_target,
                     ctx->d_span_what,   ctx->d_span_packed, ctx->d_gs,          ctx->d_x16,
-                    ctx->d_pk,          ctx->d_order,       ctx->d_gss};
+                    ctx->d_pk,          ctx->d_order,       ctx->d_gss,         ctx->d_bidx,
+                    ctx->d_bscale};
     for (void *p : bufs)
         if (p) (void)hipFree(p);
     delete ctx;
@@ -1014,23 +1025,21 @@ namespace {
 // an interior fine minimum and its neighbours; at least `floor`.
 template <typename FS, typename FF>
 double grid_search(const exl3_grid &grid, FS f_sub, FF f_full) {
+    // f_sub, f_full: the objectives of a list of points (one batch each)
     const long n_c = std::lround((grid.coarse_hi - grid.coarse_lo) / grid.coarse_step);
-    double g_c = grid.coarse_lo, best = 0.0;
-    for (long k = 0; k <= n_c; ++k) {
-        const double g = grid.coarse_lo + (double)k * grid.coarse_step;
-        const double v = f_sub(g);
-        if (k == 0 || v < best) {
-            best = v;
-            g_c = g;
+    std::vector<double> gc;
+    for (long k = 0; k <= n_c; ++k) gc.push_back(grid.coarse_lo + (double)k * grid.coarse_step);
+    const std::vector<double> vc = f_sub(gc);
+    double g_c = gc[0], best = vc[0];
+    for (size_t k = 1; k < gc.size(); ++k)
+        if (vc[k] < best) {
+            best = vc[k];
+            g_c = gc[k];
         }
-    }
     const long M = std::lround(grid.fine_radius / grid.fine_step);
-    std::vector<double> gs, fs;
-    for (long m = -M; m <= M; ++m) {
-        const double g = g_c + (double)m * grid.fine_step;
-        gs.push_back(g);
-        fs.push_back(f_full(g));
-    }
+    std::vector<double> gs;
+    for (long m = -M; m <= M; ++m) gs.push_back(g_c + (double)m * grid.fine_step);
+    const std::vector<double> fs = f_full(gs);
     size_t ib = 0;
     for (size_t i = 1; i < fs.size(); ++i)
         if (fs[i] < fs[ib]) ib = i;
@@ -1163,22 +1172,18 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
             }
             // binary64 sum, in ascending tile order, of the path costs of the
             // tiles idx[off .. off+cnt) at scale (float)s
-            auto objective_on = [&](double s, int64_t off, int64_t cnt) -> double {
+            // binary16 mode: the binary64 sum, in ascending tile order, of the
+            // sample's path costs at scale (float)s (the search on fp16(w / s);
+            // the traceback scores the dequantized tiles in binary32)
+            auto objective_f16 = [&](double s) -> double {
                 if (err != EXL3_OK) return 0.0;
-                int r;
-                if (f16) {
-                    // binary16 search on fp16(w / s); the traceback scores the
-                    // dequantized tiles in binary32 (off is 0: no subsample)
-                    hipError_t e = exl3::launch_to_f16(ctx->d_gs, nullptr, cnt, (float)s,
-                                                       ctx->d_x16, ctx->stream);
-                    r = e == hipSuccess
+                const int64_t cnt = ns;
+                hipError_t e = exl3::launch_to_f16(ctx->d_gs, nullptr, cnt, (float)s, ctx->d_x16,
+                                                   ctx->stream);
+                int r = e == hipSuccess
                             ? encode_chain_f16(ctx, ctx->d_x16, cnt, K, ctx->d_pk, nullptr,
                                                nullptr, ctx->d_gs, (float)s, ctx->d_sse)
                             : fail(ctx, EXL3_EHIP, "binary16 inputs: %s", hipGetErrorString(e));
-                } else {
-                    r = encode_chain(ctx, ctx->d_wreg, ctx->d_idx + off, cnt, K, (float)s,
-                                     nullptr, nullptr, nullptr, nullptr, ctx->d_sse);
-                }
                 if (r == EXL3_OK) {
                     hipError_t e = hipMemcpyAsync(costs.data(), ctx->d_sse,
                                                   (size_t)cnt * sizeof(float),
@@ -1196,10 +1201,69 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
                 for (int64_t i = 0; i < cnt; ++i) f += (double)costs[(size_t)i];
                 return f;
             };
+            // grid search (binary32): the objective of each scale in ss, the
+            // binary64 sum in ascending tile order of the path costs of the tiles
+            // idx_all[off .. off + cnt) at (float)s.  Every point's tiles go in
+            // one batch, each tile with its point's scale (a tile's cost does not
+            // depend on what else is in the batch), with one read-back.
+            auto objectives_on = [&](const std::vector<double> &ss, int64_t off,
+                                     int64_t cnt) -> std::vector<double> {
+                std::vector<double> f(ss.size(), 0.0);
+                if (err != EXL3_OK) return f;
+                const size_t np = ss.size(), nt = np * (size_t)cnt;
+                std::vector<int32_t> bidx(nt);
+                std::vector<float> bscale(nt);
+                for (size_t q = 0; q < np; ++q)
+                    for (int64_t i = 0; i < cnt; ++i) {
+                        bidx[q * (size_t)cnt + (size_t)i] = idx_all[(size_t)(off + i)];
+                        bscale[q * (size_t)cnt + (size_t)i] = (float)ss[q];
+                    }
+                int r;
+                if ((r = ensure(ctx, ctx->d_bidx, ctx->bidx_cap, nt)) != EXL3_OK ||
+                    (r = ensure(ctx, ctx->d_bscale, ctx->bscale_cap, nt)) != EXL3_OK ||
+                    (r = ensure(ctx, ctx->d_sse, ctx->sse_cap, nt)) != EXL3_OK) {
+                    err = r;
+                    return f;
+                }
+                hipError_t e = hipMemcpyAsync(ctx->d_bidx, bidx.data(), nt * sizeof(int32_t),
+                                              hipMemcpyHostToDevice, ctx->stream);
+                if (e == hipSuccess)
+                    e = hipMemcpyAsync(ctx->d_bscale, bscale.data(), nt * sizeof(float),
+                                       hipMemcpyHostToDevice, ctx->stream);
+                if (e != hipSuccess) {
+                    err = fail(ctx, EXL3_EHIP, "scale-search batch: %s", hipGetErrorString(e));
+                    return f;
+                }
+                r = encode_chain(ctx, ctx->d_wreg, ctx->d_bidx, (int64_t)nt, K, 0.0f, nullptr,
+                                 nullptr, nullptr, nullptr, ctx->d_sse, ctx->d_bscale, true);
+                const void *pc = nullptr;
+                if (r == EXL3_OK)
+                    r = read_back(ctx, ctx->d_sse, nt * sizeof(float), nullptr, 0, &pc);
+                if (r != EXL3_OK) {
+                    err = r;
+                    return f;
+                }
+                const float *c = static_cast<const float *>(pc);
+                for (size_t q = 0; q < np; ++q) {
+                    double sum = 0.0;
+                    for (int64_t i = 0; i < cnt; ++i)
+                        sum += (double)c[q * (size_t)cnt + (size_t)i];
+                    f[q] = sum;
+                }
+                return f;
+            };
             if (grid) {
+                auto scaled = [&](const std::vector<double> &ms) {
+                    std::vector<double> ss;
+                    for (double m : ms) ss.push_back(m * rms);
+                    return ss;
+                };
                 const double mult = grid_search(
-                    *grid, [&](double m) { return objective_on(m * rms, ns, ns_sub); },
-                    [&](double m) { return objective_on(m * rms, 0, ns); });
+                    *grid,
+                    [&](const std::vector<double> &ms) {
+                        return objectives_on(scaled(ms), ns, ns_sub);
+                    },
+                    [&](const std::vector<double> &ms) { return objectives_on(scaled(ms), 0, ns); });
                 if (err != EXL3_OK) return err;
                 *scale_chosen = (float)(mult * rms);
                 return EXL3_OK;
@@ -1231,11 +1295,10 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
                 *scale_chosen = *static_cast<const float *>(p_scale);
                 return EXL3_OK;
             }
-            auto objective = [&](double s) { return objective_on(s, 0, ns); };
             // The result is the midpoint of the last bracket, which the last
             // reduction sets before its new point is scored: that score can
             // never be read, so it is not computed (iters + 1 probes in all).
-            double fp = objective(p), fq = objective(q);
+            double fp = objective_f16(p), fq = objective_f16(q);
             for (int it = 0; it < gss->iters && err == EXL3_OK; ++it) {
                 const bool last = it + 1 == gss->iters;
                 if (fp < fq) {
@@ -1243,13 +1306,13 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
                     q = p;
                     fq = fp;
                     p = b - (b - a) * g;
-                    if (!last) fp = objective(p);
+                    if (!last) fp = objective_f16(p);
                 } else {
                     a = p;
                     p = q;
                     fp = fq;
                     q = a + (b - a) * g;
-                    if (!last) fq = objective(q);
+                    if (!last) fq = objective_f16(q);
                 }
             }
             if (err != EXL3_OK) return err;

@@ -139,11 +139,13 @@ inline size_t bp_bytes_per_tile(int K) {
 // pass: 1 (rotated, free start, backpointers 127..254, end state), 2 (start
 // pinned to X, backpointers 0..254, path cost) or 3 (as 2, path cost only).
 // scale_dev: when not null, the levels are scaled by the binary32 value it
-// points to (read when the launch runs) instead of `scale`.
+// points to (read when the launch runs) instead of `scale`; with
+// scale_per_tile, tile b of the launch takes scale_dev[b].
 hipError_t launch_viterbi_fwd(int K, int pass, const float *x, const int32_t *tile_idx,
                               int64_t tile0, int64_t n, const uint16_t *levels, float scale,
                               const float *scale_dev, const uint16_t *X_in, void *bp,
-                              uint16_t *end_state, float *cost_out, hipStream_t stream);
+                              uint16_t *end_state, float *cost_out, hipStream_t stream,
+                              bool scale_per_tile = false);
 
 hipError_t launch_viterbi_fwd_f16(int K, int pass, const uint16_t *x, int64_t tile0, int64_t n,
                                   const uint16_t *levels, const uint16_t *X_in, void *bp,

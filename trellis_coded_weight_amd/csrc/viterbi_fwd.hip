@@ -542,7 +542,7 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
                    int64_t tile0, const uint16_t *__restrict__ levels, float scale,
                    const float *__restrict__ scale_dev, const uint16_t *__restrict__ X_in,
                    typename Geo<K>::bp_t *__restrict__ bp, uint16_t *__restrict__ end_state,
-                   float *__restrict__ cost_out) {
+                   float *__restrict__ cost_out, bool scale_per_tile) {
     using G = Geo<K>;
     using bp_t = typename G::bp_t;
     constexpr bool SKEW = skewed<K, PASS>();
@@ -587,8 +587,9 @@ viterbi_fwd_kernel(const float *__restrict__ x, const int32_t *__restrict__ tile
     lane_butterflies<K>(g, m, b0);
 
     // levels of the lane's 64 states, scaled once per pass (the scale from
-    // device memory when given: a search that chooses it on the device)
-    if (scale_dev) scale = *scale_dev;
+    // device memory when given: a search that chooses it on the device, or one
+    // scale per tile for a batch of a search's points)
+    if (scale_dev) scale = scale_dev[scale_per_tile ? b : 0];
     Levels<K> lv;
 #pragma unroll
     for (int i = 0; i < G::GPL; ++i)
@@ -845,11 +846,12 @@ template <int K, int PASS>
 hipError_t launch_fwd_t(const float *x, const int32_t *tile_idx, int64_t tile0, int64_t n,
                         const uint16_t *levels, float scale, const float *scale_dev,
                         const uint16_t *X_in, void *bp, uint16_t *end_state, float *cost_out,
-                        hipStream_t stream) {
+                        hipStream_t stream, bool scale_per_tile) {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL((viterbi_fwd_kernel<K, PASS>), dim3((unsigned)n), dim3(kLanes), 0, stream,
                        x, tile_idx, tile0, levels, scale, scale_dev, X_in,
-                       reinterpret_cast<typename Geo<K>::bp_t *>(bp), end_state, cost_out);
+                       reinterpret_cast<typename Geo<K>::bp_t *>(bp), end_state, cost_out,
+                       scale_per_tile);
     return hipGetLastError();
 }
 
@@ -858,18 +860,19 @@ hipError_t launch_fwd_t(const float *x, const int32_t *tile_idx, int64_t tile0, 
 hipError_t launch_viterbi_fwd(int K, int pass, const float *x, const int32_t *tile_idx,
                               int64_t tile0, int64_t n, const uint16_t *levels, float scale,
                               const float *scale_dev, const uint16_t *X_in, void *bp,
-                              uint16_t *end_state, float *cost_out, hipStream_t stream) {
+                              uint16_t *end_state, float *cost_out, hipStream_t stream,
+                              bool scale_per_tile) {
 #define EXL3_FWD_CASE(KK)                                                                    \
     case KK:                                                                                 \
         return pass == 1   ? launch_fwd_t<KK, 1>(x, tile_idx, tile0, n, levels, scale,       \
                                                   scale_dev, X_in, bp, end_state, cost_out,  \
-                                                  stream)                                    \
+                                                  stream, scale_per_tile)                    \
                : pass == 2 ? launch_fwd_t<KK, 2>(x, tile_idx, tile0, n, levels, scale,       \
                                                   scale_dev, X_in, bp, end_state, cost_out,  \
-                                                  stream)                                    \
+                                                  stream, scale_per_tile)                    \
                            : launch_fwd_t<KK, 3>(x, tile_idx, tile0, n, levels, scale,       \
                                                   scale_dev, X_in, bp, end_state, cost_out,  \
-                                                  stream);
+                                                  stream, scale_per_tile);
     switch (K) {
         EXL3_FWD_CASE(1)
         EXL3_FWD_CASE(2)
