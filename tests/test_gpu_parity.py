@@ -317,6 +317,31 @@ def test_small_matrix_with_grid_search(ctx, K):
     assert got["mse"] == want["mse"]
 
 
+# The grid search encodes each phase's points as one batch with a scale per
+# tile; a scratch bound of seven tiles splits those batches into launches whose
+# boundaries fall inside points (each launch then reads its own slice of the
+# per-tile scales).
+def test_grid_search_with_split_batches():
+    import trellis_coded_weight_amd as T
+    K = 2
+    m = workloads.gaussian(256, 384, 0.02, 61, 62, K=K)
+    want = oracle.quantize_matrix(m.w, m.su, m.sv, K, had_block=128, gss=None,
+                                  grid=oracle.GRID_DEFAULT)
+    with T.Context(0, scratch_bytes=T.scratch_per_tile(K) * 7) as small:
+        small.set_timing(True)
+        got = small.quantize_matrix_grid(torch.from_numpy(m.w).to(torch.bfloat16).to(DEV), K,
+                                         torch.from_numpy(m.su).to(DEV),
+                                         torch.from_numpy(m.sv).to(DEV), grid=T.GRID_PAGES,
+                                         want_tile_sse=True)
+        _, launches, _ = small.read_timing("fwd1")
+        small.set_timing(False)
+    assert launches > 40
+    assert np.float32(got["scale"]) == want["scale"]
+    assert np.array_equal(_u16(got["packed"]).reshape(-1, 16 * K), want["packed"])
+    assert np.array_equal(_bits(got["tile_sse"].cpu().numpy()), _bits(want["sse"]))
+    assert got["mse"] == want["mse"]
+
+
 def test_grid_rejects_malformed_grid(ctx):
     import trellis_coded_weight_amd as T
     m = workloads.gaussian(128, 128, 0.02, 1, 2, K=2)
