@@ -33,7 +33,7 @@ def _bits(a):
     return np.asarray(a, np.float32).view(np.uint32)
 
 
-@pytest.mark.parametrize("B,tile_major", [(64, True), (128, False), (128, True)])
+@pytest.mark.parametrize("B,tile_major", [(64, True), (64, False), (128, False), (128, True)])
 def test_unregularize_bit_exact(ctx, B, tile_major):
     rng = np.random.default_rng(B + tile_major)
     R, C = 2 * B, 3 * B
@@ -46,6 +46,32 @@ def test_unregularize_bit_exact(ctx, B, tile_major):
                            torch.from_numpy(su).to(DEV), torch.from_numpy(sv).to(DEV),
                            had_block=B, tile_major=tile_major)
     assert np.array_equal(_bits(got.cpu().numpy()), _bits(want))
+
+
+# Input and output four bytes past a 16-byte boundary (one element per access),
+# through the C ABI.
+@pytest.mark.parametrize("tile_major", [True, False])
+def test_unregularize_unaligned(ctx, tile_major):
+    import trellis_coded_weight_amd as T
+    B, R, C = 128, 256, 384
+    rng = np.random.default_rng(90 + tile_major)
+    w_reg = rng.standard_normal((R, C)).astype(np.float32)
+    su = (rng.standard_normal(R) * 0.1).astype(np.float32)
+    sv = (2 * rng.integers(0, 2, C) - 1).astype(np.float32)
+    want = oracle.unregularize(w_reg, su, sv, B)
+    src = np.ascontiguousarray(oracle.to_tiles(w_reg) if tile_major else w_reg).reshape(-1)
+    ibuf = torch.zeros(R * C + 1, device=DEV)
+    ibuf[1:] = torch.from_numpy(src).to(DEV)
+    obuf = torch.full((R * C + 1,), -1.0, device=DEV)
+    sud, svd = torch.from_numpy(su).to(DEV), torch.from_numpy(sv).to(DEV)
+    torch.cuda.synchronize()
+    rc = ctx.lib.exl3_unregularize(ctx.handle, ibuf[1:].data_ptr(),
+                                   T.EXL3_TILE_MAJOR if tile_major else T.EXL3_ROW_MAJOR, R, C, B,
+                                   sud.data_ptr(), svd.data_ptr(), obuf[1:].data_ptr())
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(obuf[1:].cpu().numpy()), _bits(want.reshape(-1)))
+    assert obuf[0].item() == -1.0
 
 
 def test_normalize_quantize_reconstruct(ctx):

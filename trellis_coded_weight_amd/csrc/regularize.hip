@@ -383,51 +383,111 @@ regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__
 // inverse): W = diag(su) H_l W_reg H_r diag(sv), evaluated as left transform,
 // x rn(1/sqrt(B)), right transform, x rn(1/sqrt(B)), then x su[row], x sv[col]
 // (su, sv may be the folded channel scales, not only +-1).  Input tile-major
-// or row-major, output row-major.
-template <int B>
-__global__ void __launch_bounds__(B)
+// or row-major, output row-major.  One workgroup of 2B lanes per block, laid
+// out as in the forward kernel: the block in LDS (16-byte loads of tiles or
+// rows), each column's transform over a lane pair (the last level by lane
+// swaps), each row's the same way, the scaled block back into LDS, and the
+// row-major output with consecutive lanes on consecutive 16-byte pieces.
+// VEC: input and output start on 16-byte boundaries (else one element per
+// access).
+template <int B, bool VEC>
+__global__ void __launch_bounds__(2 * B)
 unregularize_kernel(const float *__restrict__ in, int rows, int cols, int in_layout,
                     const float *__restrict__ su, const float *__restrict__ sv,
                     float *__restrict__ out, const uint8_t *__restrict__ order) {
-    __shared__ float blk[B][B + 1];
-    const int j = threadIdx.x;
-    const int r0 = blockIdx.y * B, c0 = blockIdx.x * B;
-    const float c = norm_const<B>();
-    const int TC = cols / 16;
+    constexpr int H = B / 2;
     constexpr int TB = B / 16;
-    for (int idx = j; idx < B * B; idx += B) {
-        int rr, cc;
-        size_t src;
-        if (in_layout == 1) {
-            const int lt = idx >> 8, t = idx & 255, tr = lt / TB, tc = lt % TB;
-            const int el = order ? order[t] : t;
-            rr = tr * 16 + (el >> 4);
-            cc = tc * 16 + (el & 15);
-            src = ((size_t)(r0 / 16 + tr) * TC + (c0 / 16 + tc)) * 256 + t;
-        } else {
-            rr = idx / B;
-            cc = idx % B;
-            src = (size_t)(r0 + rr) * cols + c0 + cc;
+    __shared__ float smem[blk_words<B, float>()];
+    __shared__ float srow[B], scol[B];
+    __shared__ uint8_t ord[256];      // the within-tile order (tile-major input with one)
+    const int l = threadIdx.x;
+    const int r0 = blockIdx.y * B, c0 = blockIdx.x * B;
+    const int TC = cols / 16;
+    const float c = norm_const<B>();
+    const int idx = (l & 31) + 32 * (l >> 6), half = (l >> 5) & 1;
+    if (l < B) scol[l] = sv[c0 + l];
+    else srow[l - B] = su[r0 + l - B];
+    const bool ordered = in_layout == 1 && order;
+    if (ordered) {
+        for (int t = l; t < 256; t += 2 * B) ord[t] = order[t];
+        __syncthreads();
+    }
+
+    // 1. the block into LDS
+    if (in_layout == 1) {
+        // tile lt = (tr, tc) of the block: positions 4 q .. 4 q + 3 per access
+        for (int g = l; g < B * B / 4; g += 2 * B) {
+            const int lt = g >> 6, q = g & 63, tr = lt / TB, tc = lt % TB;
+            const size_t tau = (size_t)(r0 / 16 + tr) * TC + (c0 / 16 + tc);
+            float v[4];
+            if constexpr (VEC) {
+                const float4 x = *reinterpret_cast<const float4 *>(in + tau * 256 + 4 * q);
+                v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = in[tau * 256 + 4 * q + e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * q + e, el = ordered ? ord[t] : t;
+                smem[blk_word<B, float>(16 * tr + (el >> 4), 16 * tc + (el & 15))] = v[e];
+            }
         }
-        blk[rr][cc] = in[src];
+    } else {
+        for (int g = l; g < B * B / 4; g += 2 * B) {
+            const int row = g / (B / 4), cq = 4 * (g % (B / 4));
+            const float *src = in + (size_t)(r0 + row) * cols + c0 + cq;
+            float v[4];
+            if constexpr (VEC) {
+                const float4 x = *reinterpret_cast<const float4 *>(src);
+                v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = src[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) smem[blk_word<B, float>(row, cq + e)] = v[e];
+        }
     }
     __syncthreads();
-    float a[B];
+
+    // 2. left transform: column idx, rows half * H ..
+    float a[H];
 #pragma unroll
-    for (int r = 0; r < B; ++r) a[r] = blk[r][j];
-    fwht_regs<B>(a);
+    for (int r = 0; r < H; ++r) a[r] = smem[blk_word<B, float>(half * H + r, idx)];
+    fwht_regs<H>(a);
 #pragma unroll
-    for (int r = 0; r < B; ++r) blk[r][j] = a[r] * c;
+    for (int r = 0; r < H; r += 2) last_level2(a[r], a[r + 1]);
+#pragma unroll
+    for (int r = 0; r < H; ++r) smem[blk_word<B, float>(half * H + r, idx)] = a[r] * c;
     __syncthreads();
+
+    // 3. right transform: row idx, columns half * H .., then the row and
+    // column factors, back into LDS
 #pragma unroll
-    for (int q = 0; q < B; ++q) a[q] = blk[j][q];
-    fwht_regs<B>(a);
+    for (int q = 0; q < H; ++q) a[q] = smem[blk_word<B, float>(idx, half * H + q)];
+    fwht_regs<H>(a);
 #pragma unroll
-    for (int q = 0; q < B; ++q) blk[j][q] = a[q] * c;
+    for (int q = 0; q < H; q += 2) last_level2(a[q], a[q + 1]);
+    const float fr = srow[idx];
+#pragma unroll
+    for (int q = 0; q < H; ++q)
+        smem[blk_word<B, float>(idx, half * H + q)] = ((a[q] * c) * fr) * scol[half * H + q];
     __syncthreads();
-    for (int idx = j; idx < B * B; idx += B) {
-        const int rr = idx / B, cc = idx % B;
-        out[(size_t)(r0 + rr) * cols + c0 + cc] = (blk[rr][cc] * su[r0 + rr]) * sv[c0 + cc];
+
+    // 4. row-major output
+    for (int g = l; g < B * B / 4; g += 2 * B) {
+        const int row = g / (B / 4), cq = 4 * (g % (B / 4));
+        float *dst = out + (size_t)(r0 + row) * cols + c0 + cq;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = smem[blk_word<B, float>(row, cq + e)];
+        if constexpr (VEC) {
+            *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[e] = v[e];
+        }
     }
 }
 
@@ -471,12 +531,19 @@ hipError_t launch_unregularize(const float *in, int in_layout, int rows, int col
     if (rows <= 0 || cols <= 0) return hipSuccess;
     if (had_block != 64 && had_block != 128) return hipErrorInvalidValue;
     dim3 grid(cols / had_block, rows / had_block);
-    if (had_block == 64)
-        hipLaunchKernelGGL(unregularize_kernel<64>, grid, dim3(64), 0, stream, in, rows, cols,
-                           in_layout, su, sv, out, order);
-    else
-        hipLaunchKernelGGL(unregularize_kernel<128>, grid, dim3(128), 0, stream, in, rows, cols,
-                           in_layout, su, sv, out, order);
+    const bool vec = reinterpret_cast<uintptr_t>(in) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(out) % 16 == 0;
+#define EXL3_UNREG_LAUNCH(BB, V)                                                                \
+    hipLaunchKernelGGL((unregularize_kernel<BB, V>), grid, dim3(2 * BB), 0, stream, in, rows,  \
+                       cols, in_layout, su, sv, out, order)
+    if (had_block == 64) {
+        if (vec) EXL3_UNREG_LAUNCH(64, true);
+        else EXL3_UNREG_LAUNCH(64, false);
+    } else {
+        if (vec) EXL3_UNREG_LAUNCH(128, true);
+        else EXL3_UNREG_LAUNCH(128, false);
+    }
+#undef EXL3_UNREG_LAUNCH
     return hipGetLastError();
 }
 
