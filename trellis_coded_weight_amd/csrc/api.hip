@@ -1170,8 +1170,6 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
                 EXL3_HIP(ctx, exl3::launch_gather_tiles(ctx->d_wreg, ctx->d_idx, ns, ctx->d_gs,
                                                         ctx->stream));
             }
-            // binary64 sum, in ascending tile order, of the path costs of the
-            // tiles idx[off .. off+cnt) at scale (float)s
             // binary16 mode: the binary64 sum, in ascending tile order, of the
             // sample's path costs at scale (float)s (the search on fp16(w / s);
             // the traceback scores the dequantized tiles in binary32)
@@ -1232,15 +1230,18 @@ int regularize_and_choose_scale(exl3_ctx *ctx, const void *w, int w_dtype, int r
                                        hipMemcpyHostToDevice, ctx->stream);
                 if (e != hipSuccess) {
                     err = fail(ctx, EXL3_EHIP, "scale-search batch: %s", hipGetErrorString(e));
+                    (void)hipStreamSynchronize(ctx->stream);   // bidx, bscale read by then
                     return f;
                 }
                 r = encode_chain(ctx, ctx->d_wreg, ctx->d_bidx, (int64_t)nt, K, 0.0f, nullptr,
                                  nullptr, nullptr, nullptr, ctx->d_sse, ctx->d_bscale, true);
                 const void *pc = nullptr;
+                // (read_back synchronizes the stream: the uploads are done by then)
                 if (r == EXL3_OK)
                     r = read_back(ctx, ctx->d_sse, nt * sizeof(float), nullptr, 0, &pc);
                 if (r != EXL3_OK) {
                     err = r;
+                    (void)hipStreamSynchronize(ctx->stream);   // bidx, bscale read by then
                     return f;
                 }
                 const float *c = static_cast<const float *>(pc);
