@@ -130,6 +130,19 @@ def test_decode_matches_oracle(ctx, K):
     assert np.array_equal(_bits(out.cpu().numpy()), _bits(v[states]))
 
 
+# Arbitrary container words (every word pattern is a container) for 5,000 tiles:
+# more than the resident workgroups decode in one round, so workgroups take
+# several tiles per wave in turn.
+@pytest.mark.parametrize("K", [1, 3, 4])
+def test_decode_many_tiles(ctx, K):
+    rng = np.random.default_rng(70 + K)
+    n = 5000
+    words = rng.integers(0, 1 << 16, (n, 16 * K)).astype(np.uint16)
+    want = oracle.scaled_levels(oracle.mul1_levels_fp16(), 0.3)[oracle.unpack_states(words, K)]
+    out = ctx.decode_tiles(torch.from_numpy(words.view(np.int16)).to(DEV), K, 0.3)
+    assert np.array_equal(_bits(out.cpu().numpy()), _bits(want))
+
+
 # The container and the output off their natural alignment (the container two
 # bytes past a 4-byte boundary, the output four bytes past a 16-byte one),
 # through the C ABI; 9 tiles, so that the last workgroup is partly empty.
