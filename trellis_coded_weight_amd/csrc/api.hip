@@ -524,6 +524,55 @@ int encode_chain_f16(exl3_ctx *ctx, const uint16_t *x, int64_t n, int K, uint16_
     int rc;
     if ((rc = admit_batch(ctx, n, K, &batch)) != EXL3_OK) return rc;
     uint16_t *cost_tmp = reinterpret_cast<uint16_t *>(ctx->d_cost);
+    // A batch a few tiles past a whole round of the compute units (one tile each
+    // at K = 1..3; the scale search's sample): the remainder runs on a second
+    // stream beside the main part, three tile-pass times instead of four (as
+    // in probe_split)
+    if (K <= 3 && batch == n && n > ctx->n_cu && n % ctx->n_cu != 0 &&
+        n % ctx->n_cu <= ctx->n_cu / 8) {
+        const int64_t rem = n % ctx->n_cu, a = n - rem;
+        const size_t per_tile = exl3::bp_bytes_per_tile(K);
+        char *bp = static_cast<char *>(ctx->d_bp);
+        if ((rc = ensure_aux(ctx)) != EXL3_OK) return rc;
+        EXL3_HIP(ctx, hipEventRecord(ctx->ev_fork, ctx->stream));
+        EXL3_HIP(ctx, hipStreamWaitEvent(ctx->aux, ctx->ev_fork, 0));
+        struct Part {
+            hipStream_t s;
+            int64_t first, count;
+        } parts[2] = {{ctx->stream, 0, a}, {ctx->aux, a, rem}};
+        for (const Part &p : parts) {
+            int id = open_timed(ctx, p.s == ctx->stream ? EXL3_KERNEL_FWD1 : EXL3_KERNEL_FWD_SIDE,
+                                p.count, p.s);
+            EXL3_HIP(ctx, exl3::launch_viterbi_fwd_f16(K, 1, x, p.first, p.count, ctx->d_levels,
+                                                       nullptr, bp + p.first * per_tile,
+                                                       ctx->d_end + p.first, nullptr, p.s));
+            close_timed(ctx, id);
+        }
+        for (const Part &p : parts) {
+            int id = open_timed(ctx, EXL3_KERNEL_TB1, p.count, p.s);
+            EXL3_HIP(ctx, exl3::launch_traceback(K, 1, true, bp + p.first * per_tile, p.count,
+                                                 ctx->d_end + p.first, ctx->d_X + p.first,
+                                                 nullptr, nullptr, 0, nullptr, 0.0f, nullptr,
+                                                 nullptr, nullptr, nullptr, p.s));
+            close_timed(ctx, id);
+            id = open_timed(ctx, p.s == ctx->stream ? EXL3_KERNEL_FWD2 : EXL3_KERNEL_FWD_SIDE,
+                            p.count, p.s);
+            EXL3_HIP(ctx, exl3::launch_viterbi_fwd_f16(K, 2, x, p.first, p.count, ctx->d_levels,
+                                                       ctx->d_X + p.first,
+                                                       bp + p.first * per_tile, nullptr,
+                                                       (cost ? cost : cost_tmp) + p.first, p.s));
+            close_timed(ctx, id);
+            id = open_timed(ctx, EXL3_KERNEL_TB2, p.count, p.s);
+            EXL3_HIP(ctx, exl3::launch_traceback(K, 2, true, bp + p.first * per_tile, p.count,
+                                                 ctx->d_X + p.first, nullptr, x32, nullptr,
+                                                 p.first, ctx->d_levels, scale, packed, states,
+                                                 sse, w_hat, p.s));
+            close_timed(ctx, id);
+        }
+        EXL3_HIP(ctx, hipEventRecord(ctx->ev_join, ctx->aux));
+        EXL3_HIP(ctx, hipStreamWaitEvent(ctx->stream, ctx->ev_join, 0));
+        return EXL3_OK;
+    }
     for (int64_t i0 = 0; i0 < n; i0 += batch) {
         const int64_t nb = std::min<int64_t>(batch, n - i0);
         int id = open_timed(ctx, EXL3_KERNEL_FWD1, nb);
