@@ -130,6 +130,18 @@ __host__ __device__ inline void bp_locate_h(uint32_t e, uint32_t &lane, uint32_t
     }
 }
 
+// A 16-byte store (p 16-byte aligned) that does not allocate in the caches:
+// for output streams written once, and read, if at all, by a later launch
+// from HBM anyway (no cache holds a whole matrix).  Only where a wave's store
+// instruction writes whole lines (consecutive lanes on consecutive 16-byte
+// pieces): pieces at a stride then reach memory unmerged, several times
+// slower than plain stores.
+__device__ __forceinline__ void store_stream(float *p, float a, float b, float c, float d) {
+    using f4v = float __attribute__((ext_vector_type(4)));
+    const f4v v = {a, b, c, d};
+    __builtin_nontemporal_store(v, reinterpret_cast<f4v *>(p));
+}
+
 // Bytes of backpointer scratch per tile in flight.
 inline size_t bp_bytes_per_tile(int K) {
     return (size_t)kSlots * kLanes * (K == 4 ? 2 : 4);

@@ -364,7 +364,7 @@ regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__
                     if (lt < TB * TB) {
                         const size_t tau =
                             (size_t)(r0 / 16 + lt / TB) * TC + (c0 / 16 + lt % TB);
-                        *reinterpret_cast<float4 *>(out + tau * 256 + t) = v[b];
+                        store_stream(out + tau * 256 + t, v[b].x, v[b].y, v[b].z, v[b].w);
                     }
                 }
             }
@@ -483,7 +483,7 @@ unregularize_kernel(const float *__restrict__ in, int rows, int cols, int in_lay
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = smem[blk_word<B, float>(row, cq + e)];
         if constexpr (VEC) {
-            *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            store_stream(dst, v[0], v[1], v[2], v[3]);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) dst[e] = v[e];

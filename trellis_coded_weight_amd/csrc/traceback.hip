@@ -336,7 +336,7 @@ decode_kernel(const uint16_t *__restrict__ packed, int64_t n, int K, float scale
         }
         float *o = out + (size_t)tile * kSteps + 4 * lane;
         if (out_vec) {
-            *reinterpret_cast<float4 *>(o) = make_float4(v[0], v[1], v[2], v[3]);
+            store_stream(o, v[0], v[1], v[2], v[3]);
         } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] = v[k];
