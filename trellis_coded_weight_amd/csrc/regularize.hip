@@ -294,11 +294,20 @@ regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__
 #pragma unroll
         for (int q = 0; q < H; ++q) a[q] = a[q] * c;
         if (layout != 1) {
-            float *dst = out + (size_t)(r0 + idx) * cols + c0 + half * H;
+            // row-major output through LDS: each lane puts back the words it
+            // alone read above (no barrier needed before), then consecutive
+            // lanes store consecutive 16-byte pieces of a row, so that a wave's
+            // store covers whole lines and can stream past the caches
 #pragma unroll
-            for (int q = 0; q < H; q += 4)
-                *reinterpret_cast<float4 *>(dst + q) =
-                    make_float4(a[q], a[q + 1], a[q + 2], a[q + 3]);
+            for (int q = 0; q < H; ++q) smem[blk_word<B, Tin>(idx, half * H + q)] = a[q];
+            __syncthreads();
+            for (int g = l; g < B * B / 4; g += 2 * B) {
+                const int row = g / (B / 4), cq = 4 * (g % (B / 4));
+                store_stream(out + (size_t)(r0 + row) * cols + c0 + cq,
+                             smem[blk_word<B, Tin>(row, cq)], smem[blk_word<B, Tin>(row, cq + 1)],
+                             smem[blk_word<B, Tin>(row, cq + 2)],
+                             smem[blk_word<B, Tin>(row, cq + 3)]);
+            }
         }
         if (layout != 1 && !tile_sumsq) continue;
         __syncthreads();              // the block in LDS is read; the stage reuses it
