@@ -173,8 +173,10 @@ regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__
     // the lane's 16-byte loads of a block: rows (l + 2B i) / CPR, i < NL, and
     // the same EPC columns cb .. cb + EPC - 1 for every i
     uint4 u[NL];
+    float sgv = 0.0f;                 // the lane's sign of the fetched block, loaded with it
     auto fetch = [&](int blk) {
         const int r0 = (blk / nbx) * B, c0 = (blk % nbx) * B, cb = (l0 % CPR) * EPC;
+        sgv = l0 < B ? sv[c0 + l0] : su[r0 + l0 - B];
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int rr = (l0 + 2 * B * i) / CPR;
@@ -215,7 +217,9 @@ regularize_kernel(const Tin *__restrict__ w, int rows, int cols, const float *__
         if constexpr (VEC && !kAhead) fetch(blk);
 
         // each lane stages one sign; a wave flag records a sign other than +-1
-        const float sg = l < B ? sv[c0 + l] : su[r0 + l - B];
+        float sg;
+        if constexpr (VEC) sg = sgv;
+        else sg = l < B ? sv[c0 + l] : su[r0 + l - B];
         sgn[l] = sg;
         const bool wave_other = __ballot((__float_as_uint(sg) & 0x7FFFFFFFu) != 0x3F800000u) != 0;
         if ((l & 63) == 0) other_sign[l >> 6] = wave_other;
