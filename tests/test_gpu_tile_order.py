@@ -63,17 +63,23 @@ def test_regularize_and_inverse(ctx, B):
 
 # 4096 x 4096: more blocks than workgroups resident at once (1,024 blocks of 128
 # or 4,096 of 64), so each workgroup takes several blocks in turn, with the
-# next block's loads issued early (bf16) or at the top of each block (fp32 at
-# B = 128).
-@pytest.mark.parametrize("B,dtype", [(128, torch.bfloat16), (64, torch.bfloat16),
-                                     (128, torch.float32)])
-def test_regularize_many_blocks_per_workgroup(ctx, B, dtype):
+# next block's loads (and its signs) issued early (bf16) or at the top of each
+# block (fp32 at B = 128).  The row-major output (natural element order, the
+# energies still in the tiles' order) goes back through LDS before its row
+# stores.
+@pytest.mark.parametrize("B,dtype,tile_major", [(128, torch.bfloat16, True),
+                                                (64, torch.bfloat16, True),
+                                                (128, torch.float32, True),
+                                                (128, torch.bfloat16, False),
+                                                (64, torch.float32, False)])
+def test_regularize_many_blocks_per_workgroup(ctx, B, dtype, tile_major):
     m = workloads.gaussian(4096, 4096, 0.02, 31, 32, K=2)
     w = torch.from_numpy(m.w).to(dtype).to(DEV)
     su, sv = torch.from_numpy(m.su).to(DEV), torch.from_numpy(m.sv).to(DEV)
-    reg, sums, flag = ctx.regularize(w, su, sv, had_block=B)
-    want = oracle.to_tiles(oracle.regularize(w.cpu().float().numpy(), m.su, m.sv, B), ORDER)
-    assert np.array_equal(_bits(reg.cpu().numpy()), _bits(want))
+    reg, sums, flag = ctx.regularize(w, su, sv, had_block=B, tile_major=tile_major)
+    rm = oracle.regularize(w.cpu().float().numpy(), m.su, m.sv, B)
+    want = oracle.to_tiles(rm, ORDER)
+    assert np.array_equal(_bits(reg.cpu().numpy()), _bits(want if tile_major else rm))
     assert np.array_equal(_bits(sums.cpu().numpy()), _bits(oracle.tile_sumsq(want)))
     assert int(flag.item()) == 0
 
